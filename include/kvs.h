@@ -1,0 +1,263 @@
+/*
+ * kvs.h -- C ABI of libkvs: attention-guided KV eviction and in-place compaction
+ * of a paged bf16 KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * One eviction round is five calls, enqueued in order on one HIP stream:
+ *
+ *   kvs_score        attention each cached entry receives from a set of observer
+ *                    queries, recovered from the decode kernel's log-sum-exp and
+ *                    summed over observers and the GQA group
+ *   kvs_lrfu_update  the attention-mass cut ("action-critical" hits) and the LRFU
+ *                    update of each entry's combined recency-frequency value (CRF)
+ *   kvs_select       the per-(layer, KV head) keep set of exactly min(B, n) entries
+ *   kvs_plan         the conflict-free slot plan: kept rows outside the tail paired
+ *                    with evicted slots inside it; the freed pages (host side)
+ *   kvs_compact      one in-place pass that moves K row, V row and CRF per pair
+ *
+ * Sources, cited by page title and section:
+ *   "ActKV Dissected: 99% of an Agent's KV Cache Is Scratch Work, and the Budget
+ *   Follows Hesitation" (zhichai.net):  Summary; Component 1 (action-attention-
+ *   guided eviction); Component 2 (budget follows hesitation); Component 3
+ *   (systems engineering); Lineage.
+ *   "BeaconKV Compresses KV Cache for Long-Reasoning Models with Beacon Queries"
+ *   (cctest.ai): Key ideas (beacon plus recent queries as the observer set).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless their name ends in _h (host memory).
+ *   - The caller owns and allocates all memory.  No call allocates, frees,
+ *     synchronizes, or copies between host and device; every call first
+ *     validates its arguments on the host and, on error, enqueues nothing and
+ *     returns a non-zero kvs_status (kvs_last_error() then describes it).
+ *   - Host mirrors (_h) must hold the same values as their device arrays; they
+ *     size the launches and are range-checked so that no kernel reads outside a
+ *     pool.  Device contents that disagree with their mirrors are undefined
+ *     behaviour.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls on different
+ *     streams are independent as long as their outputs are disjoint.
+ *   - Layout constants: head_dim = 128 and page_size = 16 only (else
+ *     KVS_ERR_UNSUPPORTED).
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvs_status {
+  KVS_OK = 0,
+  KVS_ERR_NULL = 1,         /* a required pointer is NULL */
+  KVS_ERR_SHAPE = 2,        /* sizes inconsistent or out of range (page id, lengths, budget...) */
+  KVS_ERR_UNSUPPORTED = 3,  /* head_dim != 128, page_size != 16, or a limit exceeded */
+  KVS_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  KVS_ERR_HIP = 5           /* a HIP runtime error (launch failure) */
+} kvs_status;
+
+/*
+ * Paged KV cache (ActKV, Component 3: the cache is held in fixed-size blocks of
+ * a paged-attention engine).  One (layer, page, KV head) block of K or V is 16
+ * rows x 128 bf16 = 4 KiB, contiguous:
+ *   k, v : bf16 [num_layers][num_pages][num_kv_heads][16][128]
+ *   crf  : fp32 [num_layers][num_pages][num_kv_heads][16]
+ * crf is the per-slot LRFU state (ActKV, Component 1); it lives in a paged side
+ * pool with the same page ids as K/V so that kvs_compact moves it with its row.
+ */
+typedef struct kvs_cache {
+  void *k;
+  void *v;
+  float *crf;
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* must be 128 */
+  int32_t page_size;     /* must be 16 */
+  int64_t num_pages;
+} kvs_cache;
+
+/*
+ * A batch of sequences.  Sequence i owns logical pages 0..npages_i-1 mapped to
+ * physical pages block_table[i][*]; its live entries are slots j = 0..len[i]-1
+ * at logical positions start[i] + j (start in 0..15: the first live row inside
+ * logical page 0).  npages_i = ceil((start[i] + len[i]) / 16) <= max_pages.
+ * Per-entry arrays (scores, hit, keep) are [num_layers][num_kv_heads][E] with
+ * E = entry_off[num_seqs]; sequence i's entries sit at entry_off[i] + j, and
+ * entry_off[i+1] - entry_off[i] must equal len[i].
+ * A *stream* is one (sequence, layer, KV head): its own scores, hits, CRF, keep
+ * set and moves.
+ */
+typedef struct kvs_seqs {
+  int32_t num_seqs;
+  int32_t max_pages;
+  const int32_t *block_table;    /* [num_seqs][max_pages] */
+  const int32_t *block_table_h;
+  const int32_t *start;          /* [num_seqs] */
+  const int32_t *start_h;
+  const int32_t *len;            /* [num_seqs] */
+  const int32_t *len_h;
+  const int64_t *entry_off;      /* [num_seqs + 1] */
+  const int64_t *entry_off_h;
+} kvs_seqs;
+
+/*
+ * Observer queries and their log-sum-exp (ActKV, Component 3: the LSE is a
+ * byproduct of paged attention; BeaconKV, Key ideas: beacon queries alongside
+ * recent queries -- both are simply observers here, weighted equally).
+ *   q   : bf16 [num_layers][num_q_heads][obs_total][128]
+ *   lse : fp32 [num_layers][num_q_heads][obs_total], natural log, over the same
+ *         live entries and the same scale as kvs_score uses
+ * Sequence i's observers are obs_off[i] .. obs_off[i+1]-1.  Query head h reads
+ * KV head h / (num_q_heads / num_kv_heads).
+ */
+typedef struct kvs_observers {
+  const void *q;
+  const float *lse;
+  const int64_t *obs_off;        /* [num_seqs + 1] */
+  const int64_t *obs_off_h;
+  int32_t num_q_heads;
+  int64_t obs_total;
+} kvs_observers;
+
+/* Human-readable name of a status code (static storage). */
+const char *kvs_status_string(kvs_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *kvs_last_error(void);
+
+/*
+ * Bytes of device workspace kvs_score needs for this batch: two small work-item
+ * tables of num_seqs + 1 int32, plus, when some sequence has more than 256
+ * observer rows (observers x GQA group), fp32 partial sums per group of 256 rows
+ * for every entry.  Returns 0 (and sets kvs_last_error()) on invalid arguments;
+ * a batch without entries needs 0.
+ */
+size_t kvs_score_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs,
+                                const kvs_observers *obs);
+
+/*
+ * kvs_score -- ActKV, Component 3 (attention recovered per block by subtracting
+ * the LSE from the query's logits: no gather, no recomputation) and Component 1
+ * (each entry's attention tallied over all action tokens).  For every stream
+ * (i, l, g) and live slot j:
+ *     s_j = sum over observers o of sequence i and query heads h of group g of
+ *           exp(scale * <q[l][h][o], k_j> - lse[l][h][o])
+ * bf16 inputs, fp32 accumulation.  Writes scores (fp32 [L][Hkv][E]); entries of
+ * a sequence with no observers get 0.  Sequences with 16 or more observers use
+ * the MFMA kernel, the others a VALU dot-product kernel.
+ * workspace: device, >= kvs_score_workspace_size bytes, 256-byte aligned; its
+ * contents are scratch (overwritten).
+ */
+kvs_status kvs_score(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *obs,
+                     float scale, float *scores, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * kvs_lrfu_update -- ActKV, Component 1.  Per stream:
+ *   1. mass cut: m_j = floor(s_j * 2^32) (integers), M = sum m_j,
+ *      T = ceil(mass_num * M / mass_den); hits are the shortest prefix of the
+ *      order (s desc, slot asc) whose mass reaches T (no hits if T == 0).
+ *      mass_num/mass_den = 9/10 is the pages' "top 90%".
+ *   2. LRFU: CRF_j <- fma(decay[i], CRF_j, hit_j) in fp32, with CRF_j taken as 0
+ *      for j >= n_prev[i] (entries appended since the last round).
+ *      decay[i] = fp32(2^(-lambda * dt_i)); kvs_lrfu_decay() computes it.
+ * scores must be finite and >= 0 (as kvs_score produces).  crf is updated in
+ * place through the block table.  hit (nullable): uint8 [L][Hkv][E], 1 = hit.
+ * decay: fp32 [num_seqs] (device); n_prev: int32 [num_seqs] (device).
+ * Requires 0 < mass_den, mass_num <= mass_den.
+ */
+kvs_status kvs_lrfu_update(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
+                           uint32_t mass_num, uint32_t mass_den, const float *decay,
+                           const int32_t *n_prev, uint8_t *hit, void *stream);
+
+/* fp32(2^(-lambda * dt)) computed in double on the host (LRFU weight of dt steps). */
+float kvs_lrfu_decay(double lambda, int32_t dt);
+
+/*
+ * kvs_select -- ActKV, Summary/Results (an entry budget per head).  Per stream,
+ * keep exactly K = min(budget[i], len[i]) entries: the first K of the order
+ * (CRF desc, s desc, slot asc), comparing fp32 values (all >= 0).
+ * keep: uint8 [L][Hkv][E] (1 = keep).  budget: int32 [num_seqs] device, with its
+ * host mirror budget_h (values >= 0).
+ */
+kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
+                      const int32_t *budget, const int32_t *budget_h, uint8_t *keep,
+                      void *stream);
+
+/*
+ * Per-stream capacity of the move-pair buffer for this batch and budget:
+ *   P = max over sequences of min(len_i - K_i, K_i),  K_i = min(budget_h[i], len_i).
+ * pairs must hold int32 [num_layers][num_kv_heads][num_seqs][P][2] and pair_count
+ * int32 [num_layers][num_kv_heads][num_seqs].  Returns -1 (and sets
+ * kvs_last_error()) on invalid arguments.
+ */
+int64_t kvs_pair_capacity(const kvs_seqs *seqs, const int32_t *budget_h);
+
+/*
+ * kvs_plan -- ActKV, Component 3 (survivors skew to the tail, so the tail is the
+ * target region; survivors outside it are paired one-to-one with holes inside
+ * it).  Per stream, with K = min(budget_i, len_i) and D = len_i - K:
+ *   sources      = kept slots j < D, ascending
+ *   destinations = evicted slots j >= D, ascending
+ * pair t = (source_t, destination_t) is written to
+ *   pairs[(((l * Hkv + g) * num_seqs + i) * P + t) * 2 + {0, 1}],  P = kvs_pair_capacity,
+ * and pair_count[(l * Hkv + g) * num_seqs + i] receives the number of pairs.
+ * keep (uint8 [L][Hkv][E]) must hold exactly K ones per stream, as kvs_select
+ * writes; with another count the pairs written stay within the capacity but the
+ * plan is meaningless.  budget: int32 [num_seqs] device, budget_h its host mirror.
+ * Host outputs (each nullable), computed from host data only, no wait:
+ *   shift_h[i]     = (start_i + D) / 16   logical pages freed at the front
+ *   new_start_h[i] = (start_i + D) % 16
+ *   new_len_h[i]   = K
+ *   freed_h        = block_table_h[i][0 .. shift_i-1] for each i in order
+ *                    (ActKV, Component 3: freed blocks go back to the scheduler);
+ *                    capacity freed_capacity entries, count in *freed_count_h.
+ * After kvs_compact has run, the live entries of sequence i are logical
+ * positions start_i + D .. start_i + len_i - 1: the caller drops the first
+ * shift_i block-table entries and sets start = new_start, len = new_len.  Freed
+ * pages may be reused only by work enqueued after kvs_compact on the same
+ * stream (it still reads them).
+ */
+kvs_status kvs_plan(const kvs_seqs *seqs, int32_t num_layers, int32_t num_kv_heads,
+                    const uint8_t *keep, const int32_t *budget, const int32_t *budget_h,
+                    int32_t *pairs, int32_t *pair_count, int32_t *shift_h, int32_t *new_start_h,
+                    int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                    int64_t *freed_count_h, void *stream);
+
+/*
+ * The host outputs of kvs_plan alone (same definitions, same argument rules), for
+ * callers that plan page reuse before enqueuing any device work.  Touches no
+ * device memory.
+ */
+kvs_status kvs_plan_host(const kvs_seqs *seqs, const int32_t *budget_h, int32_t *shift_h,
+                         int32_t *new_start_h, int32_t *new_len_h, int32_t *freed_h,
+                         int64_t freed_capacity, int64_t *freed_count_h);
+
+/*
+ * kvs_compact -- ActKV, Component 3 (copied in one parallel pass; no extra KV
+ * buffer).  For every pair of every stream, copies the K row (256 B), the V row
+ * (256 B) and the CRF value of the source slot onto the destination slot, in
+ * place, addressed through the pre-compaction layout in seqs.  Sources and
+ * destinations of a plan from kvs_plan are disjoint, so the pairs are applied
+ * in any order.  budget_h must be the array given to kvs_plan (it fixes P).
+ */
+kvs_status kvs_compact(const kvs_cache *cache, const kvs_seqs *seqs, const int32_t *budget_h,
+                       const int32_t *pairs, const int32_t *pair_count, void *stream);
+
+/*
+ * Host-side budget ratchet (ActKV, Component 2 and Lineage): for each sequence
+ * whose flag_h is non-zero, budget_h[i] <- max(budget_h[i],
+ * min(cap, floor(budget_h[i] * num / den))).  The pages' ratchet is num/den = 7/4,
+ * cap = 30000, starting from 512; the budget never shrinks.
+ */
+kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs,
+                              int32_t num, int32_t den, int32_t cap);
+
+/* Library version string. */
+const char *kvs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

@@ -1,0 +1,265 @@
+"""ctypes binding of libkvs (include/kvs.h).  Argument marshalling only: every
+step runs in the HIP kernels of libkvs.so, and there is no fallback -- if the
+library is missing, loading raises.
+
+Device arrays are torch tensors on a ROCm device (only their data_ptr() is
+used); host mirrors are numpy arrays; the stream is torch's current stream
+unless one is given.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("KVS_LIB", os.path.join(HERE, "libkvs.so"))
+
+KVS_OK = 0
+STATUS = {0: "KVS_OK", 1: "KVS_ERR_NULL", 2: "KVS_ERR_SHAPE", 3: "KVS_ERR_UNSUPPORTED",
+          4: "KVS_ERR_WORKSPACE", 5: "KVS_ERR_HIP"}
+
+EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_workspace_size",
+           "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_pair_capacity",
+           "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_budget_ratchet")
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class Cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("crf", C.c_void_p),
+                ("num_layers", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("num_pages", C.c_int64)]
+
+
+class Seqs(C.Structure):
+    _fields_ = [("num_seqs", C.c_int32), ("max_pages", C.c_int32),
+                ("block_table", C.c_void_p), ("block_table_h", C.c_void_p),
+                ("start", C.c_void_p), ("start_h", C.c_void_p),
+                ("len", C.c_void_p), ("len_h", C.c_void_p),
+                ("entry_off", C.c_void_p), ("entry_off_h", C.c_void_p)]
+
+
+class Observers(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("lse", C.c_void_p), ("obs_off", C.c_void_p),
+                ("obs_off_h", C.c_void_p), ("num_q_heads", C.c_int32), ("obs_total", C.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libkvs.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkvs.so not found at {LIB_PATH}; build it with "
+                               "`python -m kv_cache_eviction_lse_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        L.kvs_status_string.restype = C.c_char_p
+        L.kvs_status_string.argtypes = [C.c_int]
+        L.kvs_last_error.restype = C.c_char_p
+        L.kvs_last_error.argtypes = []
+        L.kvs_version.restype = C.c_char_p
+        L.kvs_score_workspace_size.restype = C.c_size_t
+        L.kvs_score_workspace_size.argtypes = [P, P, P]
+        L.kvs_score.restype = C.c_int
+        L.kvs_score.argtypes = [P, P, P, C.c_float, P, P, C.c_size_t, P]
+        L.kvs_lrfu_update.restype = C.c_int
+        L.kvs_lrfu_update.argtypes = [P, P, P, C.c_uint32, C.c_uint32, P, P, P, P]
+        L.kvs_lrfu_decay.restype = C.c_float
+        L.kvs_lrfu_decay.argtypes = [C.c_double, C.c_int32]
+        L.kvs_select.restype = C.c_int
+        L.kvs_select.argtypes = [P, P, P, P, P, P, P]
+        L.kvs_pair_capacity.restype = C.c_int64
+        L.kvs_pair_capacity.argtypes = [P, P]
+        L.kvs_plan.restype = C.c_int
+        L.kvs_plan.argtypes = [P, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, C.c_int64, P, P]
+        L.kvs_plan_host.restype = C.c_int
+        L.kvs_plan_host.argtypes = [P, P, P, P, P, P, C.c_int64, P]
+        L.kvs_compact.restype = C.c_int
+        L.kvs_compact.argtypes = [P, P, P, P, P, P]
+        L.kvs_budget_ratchet.restype = C.c_int
+        L.kvs_budget_ratchet.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != KVS_OK:
+        raise KvsError(status, lib().kvs_last_error().decode())
+
+
+def _ptr(x) -> int | None:
+    """data pointer of a torch tensor or numpy array (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        assert x.flags["C_CONTIGUOUS"]
+        return x.ctypes.data
+    assert x.is_contiguous()
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# structures
+# ---------------------------------------------------------------------------
+
+
+class PagedCache:
+    """Caller-owned pools: k, v bf16 [L][P][Hkv][16][128], crf fp32 [L][P][Hkv][16]."""
+
+    def __init__(self, k, v, crf):
+        L, P, Hkv, page, D = k.shape
+        assert v.shape == k.shape and tuple(crf.shape) == (L, P, Hkv, page)
+        self.k, self.v, self.crf = k, v, crf
+        self.c = Cache(_ptr(k), _ptr(v), _ptr(crf), L, Hkv, D, page, P)
+
+    @property
+    def ref(self):
+        return C.byref(self.c)
+
+
+class SeqBatch:
+    """Device arrays plus their host mirrors (numpy) for a batch of sequences."""
+
+    def __init__(self, block_table: np.ndarray, start: np.ndarray, length: np.ndarray,
+                 device="cuda"):
+        import torch
+        self.block_table_h = np.ascontiguousarray(block_table, np.int32)
+        self.start_h = np.ascontiguousarray(start, np.int32)
+        self.len_h = np.ascontiguousarray(length, np.int32)
+        S = self.len_h.shape[0]
+        self.entry_off_h = np.zeros(S + 1, np.int64)
+        self.entry_off_h[1:] = np.cumsum(self.len_h.astype(np.int64))
+        self.block_table = torch.from_numpy(self.block_table_h).to(device)
+        self.start = torch.from_numpy(self.start_h).to(device)
+        self.len = torch.from_numpy(self.len_h).to(device)
+        self.entry_off = torch.from_numpy(self.entry_off_h).to(device)
+        mp = self.block_table_h.shape[1] if self.block_table_h.ndim == 2 else 0
+        self.s = Seqs(S, mp, _ptr(self.block_table), _ptr(self.block_table_h),
+                      _ptr(self.start), _ptr(self.start_h), _ptr(self.len), _ptr(self.len_h),
+                      _ptr(self.entry_off), _ptr(self.entry_off_h))
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.len_h.shape[0])
+
+    @property
+    def entries(self) -> int:
+        return int(self.entry_off_h[-1])
+
+    @property
+    def ref(self):
+        return C.byref(self.s)
+
+
+class ObserverSet:
+    """Observer queries bf16 [L][Hq][O_tot][128], their LSE fp32 [L][Hq][O_tot], offsets."""
+
+    def __init__(self, q, lse, obs_off_h: np.ndarray, device="cuda"):
+        import torch
+        self.q, self.lse = q, lse
+        self.obs_off_h = np.ascontiguousarray(obs_off_h, np.int64)
+        self.obs_off = torch.from_numpy(self.obs_off_h).to(device)
+        self.o = Observers(_ptr(q), _ptr(lse), _ptr(self.obs_off), _ptr(self.obs_off_h),
+                           int(q.shape[1]), int(q.shape[2]))
+
+    @property
+    def ref(self):
+        return C.byref(self.o)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+
+def kvs_score_workspace_size(cache: PagedCache, seqs: SeqBatch, obs: ObserverSet) -> int:
+    return int(lib().kvs_score_workspace_size(cache.ref, seqs.ref, obs.ref))
+
+
+def kvs_score(cache: PagedCache, seqs: SeqBatch, obs: ObserverSet, scale: float, scores,
+              workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvs_score(cache.ref, seqs.ref, obs.ref, C.c_float(scale), _ptr(scores),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvs_lrfu_update(cache: PagedCache, seqs: SeqBatch, scores, mass_num: int, mass_den: int,
+                    decay, n_prev, hit=None, stream=None) -> None:
+    _check(lib().kvs_lrfu_update(cache.ref, seqs.ref, _ptr(scores), mass_num, mass_den,
+                                 _ptr(decay), _ptr(n_prev), _ptr(hit), _stream(stream)))
+
+
+def kvs_lrfu_decay(lam: float, dt: int) -> np.float32:
+    return np.float32(lib().kvs_lrfu_decay(float(lam), int(dt)))
+
+
+def kvs_select(cache: PagedCache, seqs: SeqBatch, scores, budget, budget_h: np.ndarray, keep,
+               stream=None) -> None:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    _check(lib().kvs_select(cache.ref, seqs.ref, _ptr(scores), _ptr(budget), _ptr(budget_h),
+                            _ptr(keep), _stream(stream)))
+
+
+def kvs_pair_capacity(seqs: SeqBatch, budget_h: np.ndarray) -> int:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    P = int(lib().kvs_pair_capacity(seqs.ref, _ptr(budget_h)))
+    if P < 0:
+        raise KvsError(2, lib().kvs_last_error().decode())
+    return P
+
+
+class PlanHost:
+    def __init__(self, shift, new_start, new_len, freed):
+        self.shift, self.new_start, self.new_len, self.freed = shift, new_start, new_len, freed
+
+
+def kvs_plan(seqs: SeqBatch, num_layers: int, num_kv_heads: int, keep, budget,
+             budget_h: np.ndarray, pairs, pair_count, stream=None) -> PlanHost:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    S = seqs.num_seqs
+    shift = np.zeros(S, np.int32)
+    new_start = np.zeros(S, np.int32)
+    new_len = np.zeros(S, np.int32)
+    cap = int(seqs.block_table_h.size)
+    freed = np.zeros(max(cap, 1), np.int32)
+    nfreed = np.zeros(1, np.int64)
+    _check(lib().kvs_plan(seqs.ref, num_layers, num_kv_heads, _ptr(keep), _ptr(budget),
+                          _ptr(budget_h), _ptr(pairs), _ptr(pair_count), _ptr(shift),
+                          _ptr(new_start), _ptr(new_len), _ptr(freed), cap, _ptr(nfreed),
+                          _stream(stream)))
+    return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
+
+
+def kvs_compact(cache: PagedCache, seqs: SeqBatch, budget_h: np.ndarray, pairs, pair_count,
+                stream=None) -> None:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    _check(lib().kvs_compact(cache.ref, seqs.ref, _ptr(budget_h), _ptr(pairs), _ptr(pair_count),
+                             _stream(stream)))
+
+
+def kvs_budget_ratchet(budget_h: np.ndarray, flags: np.ndarray, num: int = 7, den: int = 4,
+                       cap: int = 30000) -> np.ndarray:
+    b = np.ascontiguousarray(budget_h, np.int32).copy()
+    f = np.ascontiguousarray(flags, np.uint8)
+    _check(lib().kvs_budget_ratchet(_ptr(b), _ptr(f), b.shape[0], num, den, cap))
+    return b
+
+
+def kvs_version() -> str:
+    return lib().kvs_version().decode()

@@ -1,0 +1,317 @@
+// libkvs C ABI: host-side validation, launch planning and the host-only outputs.
+// Every entry point checks its arguments before any HIP call; on error it enqueues
+// nothing and returns a status (detail in kvs_last_error()).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kvs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvs_status fail(kvs_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvs_status ok() {
+  g_err[0] = 0;
+  return KVS_OK;
+}
+
+kvs_status check_cache(const kvs_cache *c, bool need_kv, bool need_crf) {
+  if (!c) return fail(KVS_ERR_NULL, "cache is NULL");
+  if (c->head_dim != kvs::kHeadDim) return fail(KVS_ERR_UNSUPPORTED, "head_dim %d != 128", c->head_dim);
+  if (c->page_size != kvs::kPage) return fail(KVS_ERR_UNSUPPORTED, "page_size %d != 16", c->page_size);
+  if (c->num_layers <= 0 || c->num_kv_heads <= 0 || c->num_pages <= 0)
+    return fail(KVS_ERR_SHAPE, "num_layers, num_kv_heads and num_pages must be > 0");
+  if (c->num_pages > (int64_t(1) << 31))
+    return fail(KVS_ERR_UNSUPPORTED, "num_pages %lld exceeds 2^31", (long long)c->num_pages);
+  if (need_kv && (!c->k || !c->v)) return fail(KVS_ERR_NULL, "cache k/v is NULL");
+  if (need_crf && !c->crf) return fail(KVS_ERR_NULL, "cache crf is NULL");
+  return KVS_OK;
+}
+
+// Checks the batch against the pool; optionally that no physical page is used twice
+// (required by the calls that write the pools in place).
+kvs_status check_seqs(const kvs_seqs *s, int64_t num_pages, bool unique_pages) {
+  if (!s) return fail(KVS_ERR_NULL, "seqs is NULL");
+  if (s->num_seqs < 0 || s->max_pages < 0) return fail(KVS_ERR_SHAPE, "num_seqs/max_pages < 0");
+  if (s->num_seqs == 0) return KVS_OK;
+  if (!s->block_table || !s->block_table_h || !s->start || !s->start_h || !s->len || !s->len_h ||
+      !s->entry_off || !s->entry_off_h)
+    return fail(KVS_ERR_NULL, "a seqs array is NULL");
+  if (s->entry_off_h[0] < 0) return fail(KVS_ERR_SHAPE, "entry_off[0] < 0");
+  std::vector<uint8_t> used;
+  if (unique_pages) used.assign((size_t)num_pages, 0);
+  for (int32_t i = 0; i < s->num_seqs; ++i) {
+    const int32_t st = s->start_h[i], n = s->len_h[i];
+    if (st < 0 || st >= kvs::kPage) return fail(KVS_ERR_SHAPE, "start[%d] = %d not in [0, 16)", i, st);
+    if (n < 0 || n > kvs::kMaxLen) return fail(KVS_ERR_SHAPE, "len[%d] = %d out of range", i, n);
+    if (s->entry_off_h[i + 1] - s->entry_off_h[i] != n)
+      return fail(KVS_ERR_SHAPE, "entry_off[%d+1] - entry_off[%d] != len[%d]", i, i, i);
+    const int64_t npg = n == 0 ? 0 : (st + (int64_t)n + kvs::kPage - 1) / kvs::kPage;
+    if (npg > s->max_pages) return fail(KVS_ERR_SHAPE, "sequence %d needs %lld pages > max_pages", i, (long long)npg);
+    const int32_t *row = s->block_table_h + (int64_t)i * s->max_pages;
+    for (int64_t p = 0; p < npg; ++p) {
+      const int32_t pg = row[p];
+      if (pg < 0 || pg >= num_pages)
+        return fail(KVS_ERR_SHAPE, "block_table[%d][%lld] = %d outside the pool", i, (long long)p, pg);
+      if (unique_pages) {
+        if (used[pg]) return fail(KVS_ERR_SHAPE, "page %d is used twice (in-place update needs distinct pages)", pg);
+        used[pg] = 1;
+      }
+    }
+  }
+  return KVS_OK;
+}
+
+kvs::Batch make_batch(const kvs_cache *c, const kvs_seqs *s) {
+  kvs::Batch b{};
+  b.bt = s->block_table;
+  b.start = s->start;
+  b.len = s->len;
+  b.entry_off = s->entry_off;
+  b.num_pages = c->num_pages;
+  b.E = s->num_seqs ? s->entry_off_h[s->num_seqs] : 0;
+  b.S = s->num_seqs;
+  b.max_pages = s->max_pages;
+  b.L = c->num_layers;
+  b.Hkv = c->num_kv_heads;
+  return b;
+}
+
+int32_t max_len_of(const kvs_seqs *s) {
+  int32_t m = 0;
+  for (int32_t i = 0; i < s->num_seqs; ++i) m = s->len_h[i] > m ? s->len_h[i] : m;
+  return m;
+}
+
+kvs_status check_obs(const kvs_observers *o, const kvs_seqs *s, int32_t Hkv) {
+  if (!o) return fail(KVS_ERR_NULL, "observers is NULL");
+  if (o->num_q_heads <= 0 || o->num_q_heads % Hkv != 0)
+    return fail(KVS_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", o->num_q_heads, Hkv);
+  if (o->num_q_heads / Hkv > 64) return fail(KVS_ERR_UNSUPPORTED, "GQA group larger than 64");
+  if (o->obs_total < 0) return fail(KVS_ERR_SHAPE, "obs_total < 0");
+  if (s->num_seqs == 0) return KVS_OK;
+  if (!o->obs_off || !o->obs_off_h) return fail(KVS_ERR_NULL, "obs_off is NULL");
+  if (o->obs_off_h[0] < 0) return fail(KVS_ERR_SHAPE, "obs_off[0] < 0");
+  for (int32_t i = 0; i < s->num_seqs; ++i) {
+    const int64_t O = o->obs_off_h[i + 1] - o->obs_off_h[i];
+    if (O < 0) return fail(KVS_ERR_SHAPE, "obs_off not monotone at %d", i);
+    if (O > 65536) return fail(KVS_ERR_UNSUPPORTED, "sequence %d has %lld observers (max 65536)", i, (long long)O);
+  }
+  if (o->obs_off_h[s->num_seqs] > o->obs_total) return fail(KVS_ERR_SHAPE, "obs_off exceeds obs_total");
+  if (o->obs_off_h[s->num_seqs] > o->obs_off_h[0] && (!o->q || !o->lse))
+    return fail(KVS_ERR_NULL, "q/lse is NULL");
+  return KVS_OK;
+}
+
+int64_t pair_cap_of(const kvs_seqs *s, const int32_t *budget_h) {
+  int64_t P = 0;
+  for (int32_t i = 0; i < s->num_seqs; ++i) {
+    const int32_t n = s->len_h[i];
+    const int32_t b = budget_h[i];
+    const int32_t K = b < n ? b : n;
+    const int64_t c = (n - K) < K ? (n - K) : K;
+    P = c > P ? c : P;
+  }
+  return P;
+}
+
+kvs_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(KVS_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvs_status_string(kvs_status s) {
+  switch (s) {
+    case KVS_OK: return "KVS_OK";
+    case KVS_ERR_NULL: return "KVS_ERR_NULL";
+    case KVS_ERR_SHAPE: return "KVS_ERR_SHAPE";
+    case KVS_ERR_UNSUPPORTED: return "KVS_ERR_UNSUPPORTED";
+    case KVS_ERR_WORKSPACE: return "KVS_ERR_WORKSPACE";
+    case KVS_ERR_HIP: return "KVS_ERR_HIP";
+  }
+  return "KVS_ERR_UNKNOWN";
+}
+
+const char *kvs_last_error(void) { return g_err; }
+
+const char *kvs_version(void) { return "kvs 0.1.0 (gfx950)"; }
+
+size_t kvs_score_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *obs) {
+  if (check_cache(cache, false, false) != KVS_OK) return 0;
+  if (check_seqs(seqs, cache->num_pages, false) != KVS_OK) return 0;
+  if (check_obs(obs, seqs, cache->num_kv_heads) != KVS_OK) return 0;
+  if (seqs->num_seqs == 0) return 0;
+  const kvs::Batch b = make_batch(cache, seqs);
+  ok();
+  if (b.E == 0) return 0;
+  return kvs::score_workspace_bytes(b, obs->num_q_heads, obs->obs_off_h, seqs->len_h, seqs->start_h);
+}
+
+kvs_status kvs_score(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *obs, float scale,
+                     float *scores, void *workspace, size_t workspace_bytes, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, false)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, false)) != KVS_OK) return st;
+  if ((st = check_obs(obs, seqs, cache->num_kv_heads)) != KVS_OK) return st;
+  if (!std::isfinite(scale)) return fail(KVS_ERR_SHAPE, "scale is not finite");
+  if (seqs->num_seqs == 0) return ok();
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  if (!scores) return fail(KVS_ERR_NULL, "scores is NULL");
+  const size_t need = kvs::score_workspace_bytes(b, obs->num_q_heads, obs->obs_off_h, seqs->len_h, seqs->start_h);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  return hip_status(kvs::launch_score(*cache, b, *obs, scale, scores, workspace, workspace_bytes,
+                                      obs->obs_off_h, seqs->len_h, seqs->start_h, (hipStream_t)stream));
+}
+
+float kvs_lrfu_decay(double lambda, int32_t dt) { return (float)std::exp2(-lambda * (double)dt); }
+
+kvs_status kvs_lrfu_update(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, uint32_t mass_num,
+                           uint32_t mass_den, const float *decay, const int32_t *n_prev, uint8_t *hit,
+                           void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, false, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if (mass_den == 0 || mass_num > mass_den)
+    return fail(KVS_ERR_SHAPE, "mass fraction %u/%u must satisfy 0 <= num <= den, den > 0", mass_num, mass_den);
+  if (seqs->num_seqs == 0) return ok();
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  if (!scores || !decay || !n_prev) return fail(KVS_ERR_NULL, "scores/decay/n_prev is NULL");
+  return hip_status(kvs::launch_lrfu(*cache, b, scores, mass_num, mass_den, decay, n_prev, hit,
+                                     max_len_of(seqs), (hipStream_t)stream));
+}
+
+kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, const int32_t *budget,
+                      const int32_t *budget_h, uint8_t *keep, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, false, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, false)) != KVS_OK) return st;
+  if (seqs->num_seqs == 0) return ok();
+  if (!budget || !budget_h) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  if (!scores || !keep) return fail(KVS_ERR_NULL, "scores/keep is NULL");
+  return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len_of(seqs), (hipStream_t)stream));
+}
+
+int64_t kvs_pair_capacity(const kvs_seqs *seqs, const int32_t *budget_h) {
+  if (!seqs) { fail(KVS_ERR_NULL, "seqs is NULL"); return -1; }
+  if (seqs->num_seqs < 0) { fail(KVS_ERR_SHAPE, "num_seqs < 0"); return -1; }
+  if (seqs->num_seqs == 0) { ok(); return 0; }
+  if (!seqs->len_h || !budget_h) { fail(KVS_ERR_NULL, "len_h/budget_h is NULL"); return -1; }
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0 || seqs->len_h[i] < 0) { fail(KVS_ERR_SHAPE, "negative budget or length"); return -1; }
+  ok();
+  return pair_cap_of(seqs, budget_h);
+}
+
+kvs_status kvs_plan_host(const kvs_seqs *seqs, const int32_t *budget_h, int32_t *shift_h, int32_t *new_start_h,
+                         int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity, int64_t *freed_count_h) {
+  kvs_status st;
+  if ((st = check_seqs(seqs, (int64_t(1) << 31), false)) != KVS_OK) return st;
+  if (seqs->num_seqs > 0 && !budget_h) return fail(KVS_ERR_NULL, "budget_h is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  int64_t nfreed = 0;
+  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
+    const int32_t n = seqs->len_h[i];
+    const int32_t K = budget_h[i] < n ? budget_h[i] : n;
+    nfreed += (seqs->start_h[i] + n - K) / kvs::kPage;
+  }
+  if (freed_h && nfreed > freed_capacity)
+    return fail(KVS_ERR_SHAPE, "freed capacity %lld < %lld freed pages", (long long)freed_capacity, (long long)nfreed);
+  int64_t w = 0;
+  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
+    const int32_t n = seqs->len_h[i];
+    const int32_t K = budget_h[i] < n ? budget_h[i] : n;
+    const int32_t D = n - K;
+    const int32_t shift = (seqs->start_h[i] + D) / kvs::kPage;
+    if (shift_h) shift_h[i] = shift;
+    if (new_start_h) new_start_h[i] = (seqs->start_h[i] + D) % kvs::kPage;
+    if (new_len_h) new_len_h[i] = K;
+    if (freed_h)
+      for (int32_t p = 0; p < shift; ++p) freed_h[w++] = seqs->block_table_h[(int64_t)i * seqs->max_pages + p];
+  }
+  if (freed_count_h) *freed_count_h = nfreed;
+  return ok();
+}
+
+kvs_status kvs_plan(const kvs_seqs *seqs, int32_t num_layers, int32_t num_kv_heads, const uint8_t *keep,
+                    const int32_t *budget, const int32_t *budget_h, int32_t *pairs, int32_t *pair_count,
+                    int32_t *shift_h, int32_t *new_start_h, int32_t *new_len_h, int32_t *freed_h,
+                    int64_t freed_capacity, int64_t *freed_count_h, void *stream) {
+  if (!seqs) return fail(KVS_ERR_NULL, "seqs is NULL");
+  if (num_layers <= 0 || num_kv_heads <= 0) return fail(KVS_ERR_SHAPE, "num_layers/num_kv_heads must be > 0");
+  kvs_status st;
+  // page ids are not touched by the plan: check the structure only (pool size unknown here)
+  if ((st = check_seqs(seqs, (int64_t(1) << 31), false)) != KVS_OK) return st;
+  if (seqs->num_seqs > 0 && (!budget || !budget_h)) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const int64_t P = seqs->num_seqs ? pair_cap_of(seqs, budget_h) : 0;
+  if (seqs->num_seqs > 0 && (!keep || !pair_count || (P > 0 && !pairs)))
+    return fail(KVS_ERR_NULL, "keep/pairs/pair_count is NULL");
+  if ((st = kvs_plan_host(seqs, budget_h, shift_h, new_start_h, new_len_h, freed_h, freed_capacity,
+                          freed_count_h)) != KVS_OK)
+    return st;
+  if (seqs->num_seqs == 0) return ok();
+  kvs_cache dummy{};
+  dummy.num_layers = num_layers;
+  dummy.num_kv_heads = num_kv_heads;
+  dummy.num_pages = 1;
+  const kvs::Batch b = make_batch(&dummy, seqs);
+  return hip_status(kvs::launch_plan(b, keep, budget, pairs, pair_count, P, (hipStream_t)stream));
+}
+
+kvs_status kvs_compact(const kvs_cache *cache, const kvs_seqs *seqs, const int32_t *budget_h, const int32_t *pairs,
+                       const int32_t *pair_count, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if (seqs->num_seqs == 0) return ok();
+  if (!budget_h) return fail(KVS_ERR_NULL, "budget_h is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const int64_t P = pair_cap_of(seqs, budget_h);
+  if (P == 0) return ok();
+  if (!pairs || !pair_count) return fail(KVS_ERR_NULL, "pairs/pair_count is NULL");
+  const kvs::Batch b = make_batch(cache, seqs);
+  return hip_status(kvs::launch_compact(*cache, b, pairs, pair_count, P, (hipStream_t)stream));
+}
+
+kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs, int32_t num, int32_t den,
+                              int32_t cap) {
+  if (num_seqs < 0) return fail(KVS_ERR_SHAPE, "num_seqs < 0");
+  if (num_seqs == 0) return ok();
+  if (!budget_h || !flag_h) return fail(KVS_ERR_NULL, "budget_h/flag_h is NULL");
+  if (den <= 0 || num < den || cap < 0) return fail(KVS_ERR_SHAPE, "ratchet needs num >= den > 0 and cap >= 0");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (!flag_h[i]) continue;
+    const int64_t b = budget_h[i];
+    int64_t grown = b * num / den;
+    if (grown > cap) grown = cap;
+    budget_h[i] = (int32_t)(grown > b ? grown : b);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal declarations shared by the libkvs translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+
+namespace kvs {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kPageElems = kPage * kHeadDim;          // bf16 elements in one (layer, page, head) block
+constexpr int64_t kMaxLen = int64_t(1) << 24;         // live entries per sequence
+constexpr int kMfmaMinObservers = 16;                 // MFMA scorer when observers >= 16
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Flattened batch description passed by value to every kernel.
+struct Batch {
+  const int32_t *bt;         // [S][max_pages]
+  const int32_t *start;      // [S]
+  const int32_t *len;        // [S]
+  const int64_t *entry_off;  // [S+1]
+  int64_t num_pages;
+  int64_t E;                 // entries per (layer, head) row of per-entry arrays
+  int32_t S;
+  int32_t max_pages;
+  int32_t L;
+  int32_t Hkv;
+};
+
+// ---- launchers (defined in the .hip files, called by api.hip after validation) ----
+hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale,
+                        float *scores, void *ws, size_t ws_bytes, const int64_t *obs_off_h,
+                        const int32_t *len_h, const int32_t *start_h, hipStream_t st);
+size_t score_workspace_bytes(const Batch &b, int32_t Hq, const int64_t *obs_off_h,
+                             const int32_t *len_h, const int32_t *start_h);
+
+hipError_t launch_lrfu(const kvs_cache &c, const Batch &b, const float *scores, uint32_t num,
+                       uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
+                       int32_t max_len, hipStream_t st);
+
+hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores,
+                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st);
+
+hipError_t launch_plan(const Batch &b, const uint8_t *keep, const int32_t *budget, int32_t *pairs,
+                       int32_t *pair_count, int64_t pair_cap, hipStream_t st);
+
+hipError_t launch_compact(const kvs_cache &c, const Batch &b, const int32_t *pairs,
+                          const int32_t *pair_count, int64_t pair_cap, hipStream_t st);
+
+}  // namespace kvs

@@ -1,0 +1,78 @@
+// kvs_plan (device part): conflict-free slot plan, one workgroup per stream.
+//
+// ActKV Dissected, Component 3: survivors skew toward the tail, so the tail is the
+// target region; survivors outside it are paired one-to-one with holes inside it.
+// With K kept and D = n - K, sources are the kept slots below D and destinations
+// the evicted slots at or above D, both ascending; pair t = (source t, dest t).
+// Ranks come from ballot scans in slot order.  Writes are bounded by the stream's
+// capacity min(D, K) so that a keep mask with the wrong count cannot overrun.
+#include "kvs_device.h"
+
+namespace kvs {
+namespace {
+
+struct PlanArgs {
+  const uint8_t *keep;
+  const int32_t *budget;
+  int32_t *pairs;
+  int32_t *pair_count;
+  Batch b;
+  int64_t P;   // pair capacity per stream
+};
+
+__device__ __forceinline__ int32_t kept_of(int32_t len, int32_t bud) {
+  return bud < len ? (bud > 0 ? bud : 0) : len;
+}
+
+__global__ __launch_bounds__(kStreamThreads) void plan_kernel(PlanArgs a) {
+  __shared__ uint32_t sc1[kStreamWaves], sc2[kStreamWaves];
+
+  const int32_t i = blockIdx.y;
+  const int32_t lg = blockIdx.x;
+  const int32_t n = a.b.len[i];
+  const int32_t K = kept_of(n, a.budget[i]);
+  const int32_t D = n - K;
+  const int32_t cap = min(D, K);
+  int32_t *pp = a.pairs + (((int64_t)lg * a.b.S + i) * a.P) * 2;
+  const uint8_t *kp = a.keep + (int64_t)lg * a.b.E + a.b.entry_off[i];
+  uint32_t cs = 0, cd = 0;
+  if (cap > 0 && cap <= a.P) {
+    for (int32_t base = 0; base < n; base += blockDim.x) {
+      const int32_t j = base + threadIdx.x;
+      const bool valid = j < n;
+      const bool k = valid && kp[j] != 0;
+      const bool fs = valid && j < D && k;
+      const bool fd = valid && j >= D && !k;
+      uint32_t ts, td;
+      const uint32_t rs = block_flag_rank(fs, ts, sc1);
+      const uint32_t rd = block_flag_rank(fd, td, sc2);
+      if (fs && cs + rs < (uint32_t)cap) pp[(int64_t)(cs + rs) * 2] = j;
+      if (fd && cd + rd < (uint32_t)cap) pp[(int64_t)(cd + rd) * 2 + 1] = j;
+      cs += ts;
+      cd += td;
+    }
+  }
+  if (threadIdx.x == 0) {
+    uint32_t c = cs < cd ? cs : cd;
+    if (c > (uint32_t)cap) c = (uint32_t)(cap > 0 ? cap : 0);
+    a.pair_count[(int64_t)lg * a.b.S + i] = (int32_t)c;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Batch &b, const uint8_t *keep, const int32_t *budget, int32_t *pairs,
+                       int32_t *pair_count, int64_t pair_cap, hipStream_t st) {
+  PlanArgs a{};
+  a.keep = keep;
+  a.budget = budget;
+  a.pairs = pairs;
+  a.pair_count = pair_count;
+  a.b = b;
+  a.P = pair_cap;
+  dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
+  plan_kernel<<<grid, kStreamThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

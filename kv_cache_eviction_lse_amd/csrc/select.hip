@@ -1,0 +1,141 @@
+// kvs_select: per-(layer, KV head) top-B keep set, one workgroup per stream.
+//
+// ActKV Dissected, Summary / Results: eviction keeps an entry budget.  Exactly
+// K = min(B, n) entries are kept per stream: the first K of the order
+// (CRF desc, s desc, slot asc) on fp32 bit patterns.  Selection runs in up to three
+// levels, each only over the entries still tied:
+//   1. radix-select the K-th largest CRF value c* (CRF cached in LDS when it fits);
+//   2. among CRF == c*, radix-select s* so that the remaining count is met;
+//   3. among (c*, s*) ties, take the lowest slots (ballot scan in slot order).
+// A level is skipped when every tied entry is kept.
+#include "select_common.h"
+
+namespace kvs {
+namespace {
+
+struct SelectArgs {
+  const float *scores;
+  const float *crf;
+  const int32_t *budget;
+  uint8_t *keep;
+  Batch b;
+  int32_t cache_cap;
+};
+
+__global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t c_cache[];
+  __shared__ SelShared sh;
+  __shared__ uint32_t flag_scratch[kStreamWaves];
+
+  const int32_t i = blockIdx.y;
+  const int32_t lg = blockIdx.x;
+  const int32_t n = a.b.len[i];
+  if (n <= 0) return;
+  const int32_t l = lg / a.b.Hkv;
+  const int32_t g = lg - l * a.b.Hkv;
+  const int64_t e0 = a.b.entry_off[i];
+  const int32_t start = a.b.start[i];
+  const int32_t *bt_row = a.b.bt + (int64_t)i * a.b.max_pages;
+  const uint32_t *sp = (const uint32_t *)(a.scores + (int64_t)lg * a.b.E + e0);
+  uint8_t *kp = a.keep + (int64_t)lg * a.b.E + e0;
+  const int32_t bud = a.budget[i];
+  const int32_t K = bud < n ? (bud > 0 ? bud : 0) : n;
+  if (K == 0 || K == n) {
+    const uint8_t v = K == n ? 1 : 0;
+    for (int32_t j = threadIdx.x; j < n; j += blockDim.x) kp[j] = v;
+    return;
+  }
+  const bool cached = n <= a.cache_cap;
+  float *crf = (float *)a.crf;
+  uint32_t band = ~0u, bor = 0u;
+  for (int32_t j = threadIdx.x; j < n; j += blockDim.x) {
+    const uint32_t bits = __float_as_uint(*crf_slot(crf, bt_row, start, j, l, g, a.b.num_pages, a.b.Hkv));
+    if (cached) c_cache[j] = bits;
+    band &= bits;
+    bor |= bits;
+  }
+  block_and_or(band, bor, (uint32_t *)sh.scratch);
+  auto crf_of = [&](int32_t j) -> uint32_t {
+    return cached ? c_cache[j]
+                  : __float_as_uint(*crf_slot(crf, bt_row, start, j, l, g, a.b.num_pages, a.b.Hkv));
+  };
+  auto one = [](uint32_t) -> uint64_t { return 1; };
+  auto all = [](int32_t) { return true; };
+
+  // level 1: CRF
+  const SelResult r1 = radix_select32(n, crf_of, all, one, (uint64_t)K, band, bor, sh);
+  const uint32_t cstar = r1.key;
+  const uint64_t need = K - r1.above;                 // entries to keep among CRF == c*
+  const bool lvl2 = need < r1.at;
+  uint32_t sstar = 0;
+  uint64_t need2 = 0, at2 = 0;
+  if (lvl2) {
+    // level 2: s among the CRF ties
+    uint32_t sa = ~0u, so = 0u;
+    for (int32_t j = threadIdx.x; j < n; j += blockDim.x) {
+      if (crf_of(j) == cstar) {
+        const uint32_t s = sp[j];
+        sa &= s;
+        so |= s;
+      }
+    }
+    block_and_or(sa, so, (uint32_t *)sh.scratch);
+    auto s_of = [&](int32_t j) -> uint32_t { return sp[j]; };
+    auto in_tie = [&](int32_t j) { return crf_of(j) == cstar; };
+    const SelResult r2 = radix_select32(n, s_of, in_tie, one, need, sa, so, sh);
+    sstar = r2.key;
+    need2 = need - r2.above;
+    at2 = r2.at;
+  }
+  const bool lvl3 = lvl2 && need2 < at2;
+
+  uint64_t carry = 0;
+  for (int32_t base = 0; base < n; base += blockDim.x) {
+    const int32_t j = base + threadIdx.x;
+    const bool valid = j < n;
+    const uint32_t c = valid ? crf_of(j) : 0u;
+    bool k;
+    if (!lvl2) {
+      k = valid && c >= cstar;
+    } else {
+      const uint32_t s = valid && c == cstar ? sp[j] : 0u;
+      if (lvl3) {
+        const bool tie = valid && c == cstar && s == sstar;
+        uint32_t tot;
+        const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
+        k = valid && (c > cstar || (c == cstar && (s > sstar || (tie && carry + rk < need2))));
+        carry += tot;
+      } else {
+        k = valid && (c > cstar || (c == cstar && s >= sstar));
+      }
+    }
+    if (valid) kp[j] = k ? 1 : 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores,
+                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st) {
+  static bool attr_set = false;
+  const int32_t cap = 39 * 1024;
+  const size_t dyn = (size_t)(max_len <= cap ? max_len : 0) * sizeof(uint32_t);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap * 4);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  SelectArgs a{};
+  a.scores = scores;
+  a.crf = c.crf;
+  a.budget = budget;
+  a.keep = keep;
+  a.b = b;
+  a.cache_cap = max_len <= cap ? max_len : 0;
+  dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
+  select_kernel<<<grid, kStreamThreads, dyn, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

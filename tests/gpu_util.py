@@ -1,0 +1,160 @@
+"""Shared helpers of the GPU parity tests: upload host-generated inputs, run the
+five C-ABI calls one at a time (reading every intermediate back), and compare
+each stage with the oracle on identical inputs."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+PAGE = 16
+
+
+def _dev():
+    import torch
+    return torch.device("cuda", 0)
+
+
+def upload(lay, inp):
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    dev = _dev()
+    k = torch.from_numpy(inp.k_pool.view(np.int16)).to(dev)
+    v = torch.from_numpy(inp.v_pool.view(np.int16)).to(dev)
+    crf = torch.from_numpy(inp.crf_pool.copy()).to(dev)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev)
+    lse = torch.from_numpy(inp.lse.copy()).to(dev)
+    cache = K.PagedCache(k, v, crf)
+    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
+    obs = K.ObserverSet(q, lse, lay.obs_off, device=dev)
+    return cache, seqs, obs
+
+
+def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None):
+    """Run the round stage by stage on the GPU; return every intermediate on the host."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    dev = _dev()
+    cache, seqs, obs = upload(lay, inp)
+    bufs = K.RoundBuffers(cache, seqs, obs, np.asarray(budget, np.int32), keep_hits=True)
+    decay = torch.from_numpy(np.asarray(decay_h, np.float32)).to(dev)
+    n_prev = torch.from_numpy(np.asarray(lay.n_prev, np.int32)).to(dev)
+    scale = 1.0 / np.sqrt(128.0) if scale is None else scale
+    out = {}
+    K.kvs_score(cache, seqs, obs, scale, bufs.scores, bufs.workspace)
+    torch.cuda.synchronize()
+    out["s"] = bufs.scores.cpu().numpy()
+    out["crf0"] = cache.crf.cpu().numpy()
+    K.kvs_lrfu_update(cache, seqs, bufs.scores, mass[0], mass[1], decay, n_prev, bufs.hit)
+    torch.cuda.synchronize()
+    out["hit"] = bufs.hit.cpu().numpy().astype(bool)
+    out["crf1"] = cache.crf.cpu().numpy()
+    K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
+    torch.cuda.synchronize()
+    out["keep"] = bufs.keep.cpu().numpy().astype(bool)
+    plan = K.kvs_plan(seqs, cache.c.num_layers, cache.c.num_kv_heads, bufs.keep, bufs.budget,
+                      bufs.budget_h, bufs.pairs, bufs.pair_count)
+    torch.cuda.synchronize()
+    out["plan"] = plan
+    out["pairs"] = bufs.pairs.cpu().numpy()
+    out["pair_count"] = bufs.pair_count.cpu().numpy()
+    out["P"] = bufs.P
+    out["k0"] = cache.k.cpu().numpy().view(np.uint16)
+    out["v0"] = cache.v.cpu().numpy().view(np.uint16)
+    K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    torch.cuda.synchronize()
+    out["k1"] = cache.k.cpu().numpy().view(np.uint16)
+    out["v1"] = cache.v.cpu().numpy().view(np.uint16)
+    out["crf2"] = cache.crf.cpu().numpy()
+    return out
+
+
+def streams_of(lay, L, Hkv):
+    return [(i, l, g) for i in range(len(lay.length)) for l in range(L) for g in range(Hkv)
+            if lay.length[i] > 0]
+
+
+def check_stages(lay, inp, out, Hq, budget, decay_h, mass=(9, 10), score_rtol=1e-3, scale=None):
+    """Component parity: scores within tolerance; every later stage exact on the GPU's
+    own inputs.  Returns the largest relative score error."""
+    L, P, Hkv = inp.k_pool.shape[:3]
+    scale = 1.0 / np.sqrt(128.0) if scale is None else scale
+    ora_s = O.score(inp.k_pool, inp.q, inp.lse, lay.obs_off, lay.block_table, lay.start,
+                    lay.length, Hq, scale, streams=streams_of(lay, L, Hkv))
+    worst = 0.0
+    exp_k, exp_v, exp_c = out["k0"].copy(), out["v0"].copy(), out["crf1"].copy()
+    for (i, l, g), s_ora in ora_s.items():
+        e0, e1 = int(lay.entry_off[i]), int(lay.entry_off[i + 1])
+        n = e1 - e0
+        s_gpu = out["s"][l, g, e0:e1]
+        if n:
+            denom = np.maximum(np.abs(s_ora.astype(np.float64)), 1e-30)
+            err = np.abs(s_gpu.astype(np.float64) - s_ora.astype(np.float64)) / denom
+            nz = s_ora > 0
+            if nz.any():
+                worst = max(worst, float(err[nz].max()))
+                assert err[nz].max() <= score_rtol, (i, l, g, float(err[nz].max()))
+            assert np.all(s_gpu[~nz] == 0) if (~nz).any() else True
+        # cut + LRFU on the GPU's own scores
+        hit = O.mass_cut(s_gpu, *mass)
+        np.testing.assert_array_equal(out["hit"][l, g, e0:e1], hit, err_msg=f"hit {(i, l, g)}")
+        page, row = O.slot_location(lay.block_table[i], lay.start[i], np.arange(n))
+        prior = out["crf0"][l, page, g, row]
+        crf_new = O.lrfu_update(prior, hit, np.float32(decay_h[i]), int(lay.n_prev[i]))
+        got = out["crf1"][l, page, g, row]
+        np.testing.assert_array_equal(got.view(np.uint32), crf_new.view(np.uint32),
+                                      err_msg=f"crf {(i, l, g)}")
+        # top-B on the GPU's CRF and scores
+        keep = O.select_top_b(got, s_gpu, int(budget[i]))
+        np.testing.assert_array_equal(out["keep"][l, g, e0:e1], keep, err_msg=f"keep {(i, l, g)}")
+        # plan on the GPU's keep mask
+        src, dst = O.plan_stream(out["keep"][l, g, e0:e1])
+        cnt = int(out["pair_count"][l, g, i])
+        assert cnt == len(src), ((i, l, g), cnt, len(src))
+        if cnt:
+            gp = out["pairs"][l, g, i, :cnt]
+            np.testing.assert_array_equal(gp[:, 0], src)
+            np.testing.assert_array_equal(gp[:, 1], dst)
+        O.compact_stream(exp_k, exp_v, exp_c, l, g, lay.block_table[i], lay.start[i], src, dst)
+    # host outputs of the plan
+    for i in range(len(lay.length)):
+        n = int(lay.length[i])
+        K_ = min(int(budget[i]), n)
+        sh, ns, nl, fr = O.plan_sequence(n, K_, int(lay.start[i]), lay.block_table[i])
+        assert (out["plan"].shift[i], out["plan"].new_start[i], out["plan"].new_len[i]) == (sh, ns, nl)
+    fr_all = np.concatenate([O.plan_sequence(int(lay.length[i]), min(int(budget[i]), int(lay.length[i])),
+                                             int(lay.start[i]), lay.block_table[i])[3]
+                             for i in range(len(lay.length))] or [np.zeros(0, np.int32)])
+    np.testing.assert_array_equal(out["plan"].freed, fr_all)
+    # compaction: every byte of every pool
+    np.testing.assert_array_equal(out["k1"], exp_k)
+    np.testing.assert_array_equal(out["v1"], exp_v)
+    np.testing.assert_array_equal(out["crf2"].view(np.uint32), exp_c.view(np.uint32))
+    return worst
+
+
+def pinned_keep_check(s_ora, crf_ora, keep_ora, hit_ora, s_gpu, crf_gpu, keep_gpu, tol=1e-3):
+    """End-to-end keep parity wherever the oracle's margins exceed the score tolerance.
+
+    tau = smallest oracle score among the hits (cut threshold); b = the oracle's last
+    kept entry in (CRF desc, s desc, slot asc) order.  Entry j is pinned when its hit
+    bit is unambiguous (|s_j - tau| > tol*tau) and its rank against b is decided by
+    CRF by more than tol, or by s by more than tol at bit-equal CRF.
+    Returns (number pinned, number of pinned mismatches)."""
+    n = len(s_ora)
+    assert keep_gpu.sum() == keep_ora.sum()
+    if n == 0 or keep_ora.sum() in (0, n):
+        return n, int((keep_gpu != keep_ora).sum())
+    s64 = s_ora.astype(np.float64)
+    tau = s64[hit_ora].min() if hit_ora.any() else None
+    order = np.lexsort((np.arange(n), -s64, -crf_ora.astype(np.float64)))
+    b = order[int(keep_ora.sum()) - 1]
+    cb, sb = float(crf_ora[b]), s64[b]
+    c64 = crf_ora.astype(np.float64)
+    unamb = np.ones(n, bool) if tau is None else np.abs(s64 - tau) > tol * tau
+    by_crf = np.abs(c64 - cb) > tol * cb if cb > 0 else c64 > 0
+    same_crf = (crf_ora.view(np.uint32) == np.float32(cb).view(np.uint32)) & \
+               (crf_gpu.view(np.uint32) == crf_ora.view(np.uint32))
+    by_s = same_crf & (np.abs(s64 - sb) > tol * sb)
+    pinned = unamb & (by_crf | by_s)
+    return int(pinned.sum()), int((keep_gpu[pinned] != keep_ora[pinned]).sum())

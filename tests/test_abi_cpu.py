@@ -1,0 +1,178 @@
+"""CPU-only checks of the C ABI: the library loads without a GPU, exports every
+function include/kvs.h declares, and its host-side validation rejects bad
+arguments before any HIP call.  Host-only entry points (decay, ratchet, pair
+capacity, plan host outputs) are checked against the oracle here too."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from kv_cache_eviction_lse_amd import _lib as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000   # a non-NULL pointer value that no test dereferences
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "kvs.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    L = K.lib()
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(K.EXPORTS) <= set(names)
+
+
+def test_status_strings():
+    L = K.lib()
+    for code, name in K.STATUS.items():
+        assert L.kvs_status_string(code).decode() == name
+
+
+def _cache(L=1, Hkv=1, P=8, head_dim=128, page=16, k=FAKE, v=FAKE, crf=FAKE):
+    return K.Cache(k, v, crf, L, Hkv, head_dim, page, P)
+
+
+class HostSeqs:
+    def __init__(self, bt, start, length, max_pages=None):
+        self.bt = np.ascontiguousarray(bt, np.int32)
+        self.start = np.ascontiguousarray(start, np.int32)
+        self.len = np.ascontiguousarray(length, np.int32)
+        self.off = np.zeros(len(self.len) + 1, np.int64)
+        self.off[1:] = np.cumsum(self.len)
+        mp = self.bt.shape[1] if max_pages is None else max_pages
+        self.s = K.Seqs(len(self.len), mp, FAKE, self.bt.ctypes.data, FAKE, self.start.ctypes.data,
+                        FAKE, self.len.ctypes.data, FAKE, self.off.ctypes.data)
+
+
+def _obs(S, Hq=4, O_=4):
+    off = np.arange(S + 1, dtype=np.int64) * O_
+    o = K.Observers(FAKE, FAKE, FAKE, off.ctypes.data, Hq, int(off[-1]))
+    return o, off
+
+
+def status(code):
+    return K.STATUS[code]
+
+
+def test_score_validation():
+    L = K.lib()
+    seqs = HostSeqs([[0, 1, 2]], [0], [40])
+    obs, off = _obs(1)
+    c = _cache()
+    ws = FAKE
+
+    def call(cache=c, s=seqs.s, o=obs, scale=0.1, scores=FAKE, wsb=1 << 20):
+        return status(L.kvs_score(C.byref(cache), C.byref(s), C.byref(o), C.c_float(scale),
+                                  scores, ws, wsb, None))
+
+    assert call(cache=_cache(head_dim=64)) == "KVS_ERR_UNSUPPORTED"
+    assert call(cache=_cache(page=32)) == "KVS_ERR_UNSUPPORTED"
+    assert call(cache=_cache(k=0)) == "KVS_ERR_NULL"
+    assert call(scores=None) == "KVS_ERR_NULL"
+    assert call(scale=float("nan")) == "KVS_ERR_SHAPE"
+    assert call(wsb=8) == "KVS_ERR_WORKSPACE"
+    obs_bad, _ = _obs(1, Hq=6)   # not a multiple of Hkv = 4? (Hkv = 1 here, use Hkv=4 cache)
+    assert call(cache=_cache(Hkv=4), o=obs_bad) == "KVS_ERR_SHAPE"
+    bad = HostSeqs([[0, 1, 9]], [0], [40])          # page 9 outside an 8-page pool
+    assert call(s=bad.s) == "KVS_ERR_SHAPE"
+    bad = HostSeqs([[0, 1, 2]], [16], [20])         # start out of range
+    assert call(s=bad.s) == "KVS_ERR_SHAPE"
+    bad = HostSeqs([[0, 1]], [0], [40])             # needs 3 pages, table has 2
+    assert call(s=bad.s) == "KVS_ERR_SHAPE"
+    assert "outside" in K.lib().kvs_last_error().decode() or "pages" in K.lib().kvs_last_error().decode()
+
+
+def test_inplace_calls_reject_shared_pages():
+    L = K.lib()
+    seqs = HostSeqs([[0, 1], [1, 2]], [0, 0], [20, 20])     # page 1 in both sequences
+    c = _cache()
+    r = L.kvs_lrfu_update(C.byref(c), C.byref(seqs.s), FAKE, 9, 10, FAKE, FAKE, None, None)
+    assert status(r) == "KVS_ERR_SHAPE"
+    bud = np.array([4, 4], np.int32)
+    r = L.kvs_compact(C.byref(c), C.byref(seqs.s), bud.ctypes.data, FAKE, FAKE, None)
+    assert status(r) == "KVS_ERR_SHAPE"
+
+
+def test_lrfu_select_validation():
+    L = K.lib()
+    seqs = HostSeqs([[0, 1]], [3], [20])
+    c = _cache()
+    assert status(L.kvs_lrfu_update(C.byref(c), C.byref(seqs.s), FAKE, 11, 10, FAKE, FAKE, None, None)) == "KVS_ERR_SHAPE"
+    assert status(L.kvs_lrfu_update(C.byref(c), C.byref(seqs.s), FAKE, 9, 0, FAKE, FAKE, None, None)) == "KVS_ERR_SHAPE"
+    assert status(L.kvs_lrfu_update(C.byref(_cache(crf=0)), C.byref(seqs.s), FAKE, 9, 10, FAKE, FAKE, None, None)) == "KVS_ERR_NULL"
+    bud = np.array([-1], np.int32)
+    assert status(L.kvs_select(C.byref(c), C.byref(seqs.s), FAKE, FAKE, bud.ctypes.data, FAKE, None)) == "KVS_ERR_SHAPE"
+
+
+def test_lrfu_decay_matches_oracle():
+    for lam in (0.5, 0.0, 0.25, 1.0):
+        for dt in range(0, 130):
+            assert K.kvs_lrfu_decay(lam, dt) == O.lrfu_decay(lam, dt), (lam, dt)
+
+
+def test_budget_ratchet_matches_oracle_and_golden(golden_dir):
+    vals = [int(x) for x in open(os.path.join(golden_dir, "ratchet_sequence.txt"))
+            if x.strip() and not x.startswith("#")]
+    b = np.array([512], np.int32)
+    seq = [512]
+    for _ in range(len(vals) - 1):
+        b = K.kvs_budget_ratchet(b, np.array([1], np.uint8))
+        seq.append(int(b[0]))
+    assert seq == vals
+    rng = np.random.default_rng(0)
+    b = rng.integers(0, 40000, 200).astype(np.int32)
+    f = (rng.random(200) < 0.5).astype(np.uint8)
+    got = K.kvs_budget_ratchet(b, f)
+    exp = [O.ratchet(int(x), bool(y)) for x, y in zip(b, f)]
+    assert got.tolist() == exp
+
+
+def test_pair_capacity_and_plan_host_match_oracle():
+    L = K.lib()
+    rng = np.random.default_rng(3)
+    S = 7
+    length = rng.integers(0, 200, S).astype(np.int32)
+    length[2] = 0
+    start = rng.integers(0, 16, S).astype(np.int32)
+    budget = rng.integers(0, 120, S).astype(np.int32)
+    budget[4] = 500
+    mp = int(((start + length + 15) // 16).max())
+    bt = np.arange(S * mp, dtype=np.int32).reshape(S, mp)
+    seqs = HostSeqs(bt, start, length)
+    P = L.kvs_pair_capacity(C.byref(seqs.s), budget.ctypes.data)
+    Ks = np.minimum(budget, length)
+    assert P == int(np.max(np.minimum(length - Ks, Ks)))
+    shift = np.zeros(S, np.int32); ns = np.zeros(S, np.int32); nl = np.zeros(S, np.int32)
+    freed = np.zeros(bt.size, np.int32); nf = np.zeros(1, np.int64)
+    r = L.kvs_plan_host(C.byref(seqs.s), budget.ctypes.data, shift.ctypes.data, ns.ctypes.data,
+                        nl.ctypes.data, freed.ctypes.data, bt.size, nf.ctypes.data)
+    assert status(r) == "KVS_OK"
+    w = 0
+    for i in range(S):
+        sh, st, ln, fr = O.plan_sequence(int(length[i]), int(Ks[i]), int(start[i]), bt[i])
+        assert (shift[i], ns[i], nl[i]) == (sh, st, ln)
+        np.testing.assert_array_equal(freed[w:w + sh], fr)
+        w += sh
+    assert nf[0] == w
+    # a freed list that does not fit is an error, not an overrun
+    r = L.kvs_plan_host(C.byref(seqs.s), budget.ctypes.data, None, None, None, freed.ctypes.data,
+                        max(w - 1, 0), nf.ctypes.data)
+    assert status(r) == ("KVS_ERR_SHAPE" if w > 0 else "KVS_OK")
+
+
+def test_empty_batch_is_a_no_op():
+    L = K.lib()
+    s = K.Seqs(0, 0, None, None, None, None, None, None, None, None)
+    c = _cache()
+    o = K.Observers(None, None, None, None, 4, 0)
+    assert status(L.kvs_score(C.byref(c), C.byref(s), C.byref(o), C.c_float(0.1), None, None, 0, None)) == "KVS_OK"
+    assert L.kvs_score_workspace_size(C.byref(c), C.byref(s), C.byref(o)) == 0
