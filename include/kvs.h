@@ -126,11 +126,11 @@ const char *kvs_status_string(kvs_status status);
 const char *kvs_last_error(void);
 
 /*
- * Bytes of device workspace kvs_score needs for this batch: two small work-item
- * tables of num_seqs + 1 int32, plus, when some sequence has more than 256
- * observer rows (observers x GQA group), fp32 partial sums per group of 256 rows
- * for every entry.  Returns 0 (and sets kvs_last_error()) on invalid arguments;
- * a batch without entries needs 0.
+ * Bytes of device workspace kvs_score needs for this batch: fp32 partial sums
+ * per group of 256 observer rows for every entry when some sequence has more
+ * than 256 rows (observers x GQA group), plus two small work-item tables when the
+ * batch has more than 255 sequences.  0 otherwise.  Returns 0 (and sets
+ * kvs_last_error()) on invalid arguments.
  */
 size_t kvs_score_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs,
                                 const kvs_observers *obs);

@@ -24,14 +24,16 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStepPages = 8;                       // one pipeline step: 8 pages, 128 keys
+constexpr int kStepPages = 4;                       // one pipeline step: 4 pages = 64 keys = 16 KiB
 constexpr int kStepKeys = kStepPages * kPage;
-constexpr int kStepBytes = kStepPages * kPageElems * 2;   // 32 KiB
+constexpr int kStepBytes = kStepPages * kPageElems * 2;
+constexpr int kRing = 4;                            // LDS ring depth: 3 steps in flight per workgroup
 constexpr int kTileKeys = 32;                       // one MFMA N tile (2 pages)
-constexpr int kStepTiles = kStepKeys / kTileKeys;   // 4
-constexpr int kRowsPerWave = 64;                    // 2 MFMA M tiles
-constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+constexpr int kStepTiles = kStepKeys / kTileKeys;   // 2
+constexpr int kRowsPerGroup = 256;                  // observer rows handled by one work item
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSmallSeqs = 255;                     // item offsets travel in the kernel arguments
+constexpr int kMaxChunkSteps = 128;                 // chunk length limit (block-table slice in LDS)
 
 struct ScoreArgs {
   const uint16_t *k;          // bf16 K pool
@@ -50,6 +52,8 @@ struct ScoreArgs {
   int32_t chunk_steps;
   int32_t partials;           // 1: write [rg][L][Hkv][E] partial sums
   float alpha;                // scale * log2(e)
+  int32_t use_small;          // 1: item offsets are in small_off (batches of <= 255 sequences)
+  int32_t small_off[kSmallSeqs + 1];
 };
 
 struct Item {
@@ -68,10 +72,11 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
   if (id >= a.total_items) return false;
   const int32_t lg = (int32_t)(id / a.items_per_lg);
   const int32_t rem = (int32_t)(id - (int64_t)lg * a.items_per_lg);
+  const int32_t *off = a.use_small ? a.small_off : a.item_off;
   int lo = 0, hi = a.b.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.item_off[mid] <= rem) lo = mid; else hi = mid;
+    if (off[mid] <= rem) lo = mid; else hi = mid;
   }
   it.i = lo;
   it.l = lg / a.b.Hkv;
@@ -84,7 +89,7 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
   it.npages = (it.start + it.n + kPage - 1) / kPage;
   it.nsteps = (it.npages + kStepPages - 1) / kStepPages;
   const int32_t nchunks = (it.nsteps + a.chunk_steps - 1) / a.chunk_steps;
-  const int32_t local = rem - a.item_off[lo];
+  const int32_t local = rem - off[lo];
   it.rg = local / nchunks;
   it.chunk = local - it.rg * nchunks;
   // host and device item counts agree by construction; refuse anything else
@@ -93,30 +98,40 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
   return true;
 }
 
-// Issue this wave's share (pages p0, p0+1) of one 8-page step into an LDS buffer.
-// Lane t of instruction r fills LDS chunk t%16 of page row 4r + t/16 with global
-// chunk (t%16) ^ row, so that a later read of chunk c of row n lands on c ^ (n%16).
-__device__ __forceinline__ void issue_step(const ScoreArgs &a, const Item &it, int step, uint8_t *buf,
-                                           int wave, int lane) {
-  const int32_t *bt = a.b.bt + (int64_t)it.i * a.b.max_pages;
+// Issue this wave's page (page w of the 4-page step) into an LDS ring slot.  Lane t
+// of instruction r fills LDS chunk t%16 of page row 4r + t/16 with global chunk
+// (t%16) ^ row, so that a later read of chunk c of row n lands on c ^ (n%16).  Page
+// ids come from the chunk's block-table slice staged in LDS, so no global load sits
+// between two page loads.  Returns the number of load instructions issued (0 or 4).
+__device__ __forceinline__ int issue_step(const ScoreArgs &a, const Item &it, int step, uint8_t *buf,
+                                          const int32_t *bt_lds, int32_t page0, int wave, int lane) {
+  const int lp = step * kStepPages + wave;
+  if (lp >= it.npages) return 0;
+  const int64_t phys = __builtin_amdgcn_readfirstlane(bt_lds[lp - page0]);
+  const uint16_t *page = a.k + (((int64_t)it.l * a.b.num_pages + phys) * a.b.Hkv + it.g) * kPageElems;
   const int row_in_instr = lane >> 4;
   const int chunk = lane & 15;
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    const int page_in_step = wave * 2 + pp;
-    const int lp = step * kStepPages + page_in_step;
-    if (lp < it.npages) {
-      const int64_t phys = bt[lp];
-      const uint16_t *page = a.k + (((int64_t)it.l * a.b.num_pages + phys) * a.b.Hkv + it.g) * kPageElems;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * r + row_in_instr;
-        const uint16_t *src = page + row * kHeadDim + ((chunk ^ row) << 3);
-        uint8_t *dst = buf + page_in_step * (kPageElems * 2) + r * 1024;
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
-      }
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * r + row_in_instr;
+    const uint16_t *src = page + row * kHeadDim + ((chunk ^ row) << 3);
+    uint8_t *dst = buf + wave * (kPageElems * 2) + r * 1024;
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
   }
+  return 4;
+}
+
+// Ring barrier: wait until this wave's loads of the current step have landed,
+// leaving `later` loads (of later steps) in flight, and its LDS writes are done;
+// then a plain s_barrier.  (A __syncthreads() would also drain every outstanding
+// vector memory operation, i.e. the whole prefetch ring, at each step.)  Vector
+// loads complete in issue order; stores in between only make the wait longer.
+__device__ __forceinline__ void ring_barrier(int later) {
+  if (later >= 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  else if (later >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void store_key(const ScoreArgs &a, const Item &it, int tile, int n,
@@ -130,9 +145,147 @@ __device__ __forceinline__ void store_key(const ScoreArgs &a, const Item &it, in
   }
 }
 
+// B operands of one 32-key tile: lane (n, h) gets dims 16s + 8h .. +8 of key n.
+__device__ __forceinline__ void read_tile(const uint8_t *buf, int tt, int col, int half, bf16x8 kb[8]) {
+  const uint8_t *tb = buf + tt * (kTileKeys * kHeadDim * 2) + col * (kHeadDim * 2);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kb[s] = *(const bf16x8 *)(tb + (((2 * s + half) ^ (col & 15)) << 4));
+}
+
+__device__ __forceinline__ floatx16 qk_tile(const bf16x8 qa[8], const bf16x8 kb[8]) {
+  floatx16 acc = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb[s], acc, 0, 0, 0);
+  return acc;
+}
+
+// sum over the 16 rows a lane holds of exp2(acc * alpha - lse*log2e)
+__device__ __forceinline__ float exp_rows(const floatx16 &acc, float alpha, const float nl[16]) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; k += 4) {
+    s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k], alpha, nl[k]));
+    s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k + 1], alpha, nl[k + 1]));
+    s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k + 2], alpha, nl[k + 2]));
+    s3 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k + 3], alpha, nl[k + 3]));
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Main loop.  NPH = number of tile phases per step (1: every wave takes both tiles of
+// a step with its own rows; 2: waves of phase p take tile p).  With NPH = 1 the two
+// tiles are software-pipelined (MFMA of tile 1 in flight during the exp of tile 0).
+template <int NPH>
+__device__ __forceinline__ void score_steps(const ScoreArgs &a, const Item &it, uint8_t (*ring)[kStepBytes],
+                                            float (*part)[kStepTiles][kWaves][kTileKeys],
+                                            const int32_t *bt_lds, int32_t page0, int wave, int lane,
+                                            int wpr, int phase, int wrow, bool active, bool on0,
+                                            bool on1, const bf16x8 (*qa)[8], const float (*nl)[16]) {
+  constexpr int TPW = kStepTiles / NPH;   // tiles per wave per step
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int32_t s_begin = it.chunk * a.chunk_steps;
+  const int32_t s_end = min(s_begin + a.chunk_steps, it.nsteps);
+  const int32_t ntiles = (it.start + it.n + kTileKeys - 1) / kTileKeys;
+
+  // loads this wave issues for step j (its page of the step, if the page exists)
+  auto nloads = [&](int32_t j) -> int { return (j < s_end && j * kStepPages + wave < it.npages) ? 4 : 0; };
+  // prologue: kRing - 1 steps in flight
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u)
+    if (s_begin + u < s_end) issue_step(a, it, s_begin + u, ring[u], bt_lds, page0, wave, lane);
+
+  for (int32_t step = s_begin; step < s_end; ++step) {
+    const int k = step - s_begin;
+    const int cur = k & (kRing - 1);
+    ring_barrier(nloads(step + 1) + nloads(step + 2));
+    // combine the previous step's per-wave partials (row sets split over waves)
+    if (wpr > 1 && k > 0 && wrow == 0 && active && lane < 32) {
+      const int pb = (k - 1) & 1;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tt = phase + u * NPH;
+        const int tile = (step - 1) * kStepTiles + tt;
+        float v = 0.f;
+        for (int w = 0; w < wpr; ++w) v += part[pb][tt][w][lane];
+        if (tile < ntiles) store_key(a, it, tile, lane, v);
+      }
+    }
+    // refill the slot freed by the previous step
+    if (step + kRing - 1 < s_end)
+      issue_step(a, it, step + kRing - 1, ring[(k + kRing - 1) & (kRing - 1)], bt_lds, page0, wave, lane);
+    if (!active) continue;
+    const uint8_t *buf = ring[cur];
+    const int tile0 = step * kStepTiles;
+    float sums[TPW];
+    if (on1) {
+      bf16x8 kb[8];
+      read_tile(buf, phase, col, half, kb);
+      floatx16 a0 = qk_tile(qa[0], kb);
+      floatx16 a1 = qk_tile(qa[1], kb);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        floatx16 b0, b1;
+        if (u + 1 < TPW) {
+          read_tile(buf, phase + (u + 1) * NPH, col, half, kb);
+          b0 = qk_tile(qa[0], kb);
+          b1 = qk_tile(qa[1], kb);
+        }
+        sums[u] = exp_rows(a0, a.alpha, nl[0]) + exp_rows(a1, a.alpha, nl[1]);
+        if (u + 1 < TPW) { a0 = b0; a1 = b1; }
+      }
+    } else if (on0) {
+      bf16x8 kb[8];
+      read_tile(buf, phase, col, half, kb);
+      floatx16 a0 = qk_tile(qa[0], kb);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        floatx16 b0;
+        if (u + 1 < TPW) {
+          read_tile(buf, phase + (u + 1) * NPH, col, half, kb);
+          b0 = qk_tile(qa[0], kb);
+        }
+        sums[u] = exp_rows(a0, a.alpha, nl[0]);
+        if (u + 1 < TPW) a0 = b0;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) sums[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = phase + u * NPH;
+      const float v = sums[u] + __shfl_xor(sums[u], 32);
+      if (lane < 32) {
+        if (wpr == 1) {
+          if (tile0 + tt < ntiles) store_key(a, it, tile0 + tt, col, v);
+        } else {
+          part[k & 1][tt][wrow][lane] = v;
+        }
+      }
+    }
+  }
+  if (wpr > 1) {
+    __syncthreads();
+    const int k = s_end - 1 - s_begin;
+    const int step = s_end - 1;
+    if (wrow == 0 && active && lane < 32) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tt = phase + u * NPH;
+        const int tile = step * kStepTiles + tt;
+        float v = 0.f;
+        for (int w = 0; w < wpr; ++w) v += part[k & 1][tt][w][lane];
+        if (tile < ntiles) store_key(a, it, tile, lane, v);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kStepBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
   __shared__ float part[2][kStepTiles][kWaves][kTileKeys];
+  __shared__ int32_t bt_lds[kMaxChunkSteps * kStepPages];
 
   Item it;
   if (!decode_item(a, it)) return;
@@ -141,135 +294,70 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
+  // Row sets: more than 128 rows -> 64-row sets (2 M tiles per wave), 3-4 waves per
+  // set, each wave takes both tiles of a step; 65..128 rows -> two 64-row sets, one
+  // tile each; up to 64 rows -> 32-row sets (1 M tile), one tile each.
   const int32_t R = it.O * a.G;
   const int32_t r0 = it.rg * kRowsPerGroup;
   const int32_t rows_here = min(kRowsPerGroup, R - r0);
-  const int wpr = (rows_here + kRowsPerWave - 1) / kRowsPerWave;        // waves per row set
-  const int nph = wpr == 1 ? 4 : (wpr == 2 ? 2 : 1);                    // tile phases
-  const int phase = wave / wpr;
-  const int wrow = wave - phase * wpr;
-  const bool active = phase < nph;
-  const int32_t wr0 = r0 + wrow * kRowsPerWave;
-  const bool mt_on0 = active && wr0 < R;
-  const bool mt_on1 = active && wr0 + 32 < R;
+  const int rw = rows_here > 64 ? 64 : 32;                              // rows per wave
+  const int wpr = (rows_here + rw - 1) / rw;                            // waves per row set
+  const int nph = wpr > 2 ? 1 : 2;                                      // tile phases
+  const int phase = wave / (nph == 1 ? 4 : 2);
+  const int wrow = nph == 1 ? wave : (wave & 1);
+  const bool active = wrow < wpr;
+  const int32_t wr0 = r0 + wrow * rw;
+  const bool on0 = active && wr0 < R;
+  const bool on1 = active && rw == 64 && wr0 + 32 < R;
 
   // Observer rows of this wave as MFMA A operands: lane (m, h) holds row m,
-  // dims 16s + 8h .. +8 for k-step s.  LSE (times log2 e) in the accumulator
-  // layout: register k of M tile t holds row 32t + 8(k/4) + 4h + k%4.
+  // dims 16s + 8h .. +8 for k-step s.  Loads are unconditional (invalid rows read
+  // row 0 of the stream and are zeroed) so that they all issue back to back.
   bf16x8 qa[2][8];
-  float nl[2][16];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int32_t r = wr0 + 32 * t + col;
-    const bool ok = active && r < R;
-    const uint16_t *qp = a.q;
-    if (ok) {
-      const int32_t h = it.g * a.G + r / it.O;
-      const int32_t o = r % it.O;
-      qp = a.q + (((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o) * kHeadDim + 8 * half;
-    }
+    const bool ok = active && r < R && (t == 0 || rw == 64);
+    const int32_t rc = ok ? r : 0;
+    const int32_t h = it.g * a.G + rc / it.O;
+    const int32_t o = rc - (rc / it.O) * it.O;
+    const uint16_t *qp = a.q + (((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o) * kHeadDim + 8 * half;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8 v = {};
-      if (ok) v = *(const bf16x8 *)(qp + 16 * s);
-      qa[t][s] = v;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int32_t rr = wr0 + 32 * t + 8 * (k >> 2) + 4 * half + (k & 3);
-      float v = __builtin_inff();
-      if (active && rr < R) {
-        const int32_t h = it.g * a.G + rr / it.O;
-        const int32_t o = rr % it.O;
-        v = a.lse[((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o] * kLog2e;
-      }
-      nl[t][k] = -v;
+      const bf16x8 v = *(const bf16x8 *)(qp + 16 * s);
+      const bf16x8 z = {};
+      qa[t][s] = ok ? v : z;
     }
   }
-
+  // LSE of the wave's rows, one per lane, then spread to the accumulator layout:
+  // register k of M tile t holds row 32t + 8(k/4) + 4h + k%4.
+  float my_nl;
+  {
+    const int32_t r = wr0 + lane;
+    const bool ok = active && r < R && lane < rw;
+    const int32_t rc = ok ? r : 0;
+    const int32_t h = it.g * a.G + rc / it.O;
+    const int32_t o = rc - (rc / it.O) * it.O;
+    const float v = a.lse[((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o] * kLog2e;
+    my_nl = ok ? -v : -__builtin_inff();
+  }
+  // the chunk's slice of the block table
   const int32_t s_begin = it.chunk * a.chunk_steps;
-  const int32_t s_end = min(s_begin + a.chunk_steps, it.nsteps);
-  const int32_t ntiles = (it.start + it.n + kTileKeys - 1) / kTileKeys;
+  const int32_t page0 = s_begin * kStepPages;
+  const int32_t page1 = min(it.npages, (s_begin + a.chunk_steps) * kStepPages);
+  const int32_t *bt_row = a.b.bt + (int64_t)it.i * a.b.max_pages;
+  for (int32_t p = page0 + (int32_t)threadIdx.x; p < page1; p += kThreads) bt_lds[p - page0] = bt_row[p];
+  float nl[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) nl[t][k] = __shfl(my_nl, 32 * t + 8 * (k >> 2) + 4 * half + (k & 3));
+  __syncthreads();
 
-  issue_step(a, it, s_begin, kbuf[0], wave, lane);
-  for (int32_t step = s_begin; step < s_end; ++step) {
-    const int cur = (step - s_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // combine the previous step's per-wave partials (row sets split over waves)
-    if (wpr > 1 && step > s_begin && wrow == 0 && active && lane < 32) {
-      const int pb = cur ^ 1;
-      for (int tt = phase; tt < kStepTiles; tt += nph) {
-        const int tile = (step - 1) * kStepTiles + tt;
-        if (tile >= ntiles) break;
-        float v = 0.f;
-        for (int w = 0; w < wpr; ++w) v += part[pb][tt][w][lane];
-        store_key(a, it, tile, lane, v);
-      }
-    }
-    if (step + 1 < s_end) issue_step(a, it, step + 1, kbuf[cur ^ 1], wave, lane);
-    if (!active) continue;
-
-    const uint8_t *buf = kbuf[cur];
-    for (int tt = phase; tt < kStepTiles; tt += nph) {
-      const int tile = step * kStepTiles + tt;
-      if (tile >= ntiles) break;
-      const uint8_t *tb = buf + tt * (kTileKeys * kHeadDim * 2) + col * (kHeadDim * 2);
-      bf16x8 kb[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = (2 * s + half) ^ (col & 15);
-        kb[s] = *(const bf16x8 *)(tb + c * 16);
-      }
-      float sum = 0.f;
-      if (mt_on0) {
-        floatx16 acc = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], acc, 0, 0, 0);
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < 16; k += 2) {
-          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k], a.alpha, nl[0][k]));
-          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k + 1], a.alpha, nl[0][k + 1]));
-        }
-        sum += s0 + s1;
-      }
-      if (mt_on1) {
-        floatx16 acc = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], acc, 0, 0, 0);
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < 16; k += 2) {
-          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k], a.alpha, nl[1][k]));
-          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[k + 1], a.alpha, nl[1][k + 1]));
-        }
-        sum += s0 + s1;
-      }
-      sum += __shfl_xor(sum, 32);
-      if (wpr == 1) {
-        if (lane < 32) store_key(a, it, tile, col, sum);
-      } else if (lane < 32) {
-        part[cur][tt][wrow][lane] = sum;
-      }
-    }
-  }
-  if (wpr > 1) {
-    __syncthreads();
-    const int step = s_end - 1;
-    const int pb = (step - s_begin) & 1;
-    if (wrow == 0 && active && lane < 32) {
-      for (int tt = phase; tt < kStepTiles; tt += nph) {
-        const int tile = step * kStepTiles + tt;
-        if (tile >= ntiles) break;
-        float v = 0.f;
-        for (int w = 0; w < wpr; ++w) v += part[pb][tt][w][lane];
-        store_key(a, it, tile, lane, v);
-      }
-    }
-  }
+  if (nph == 1)
+    score_steps<1>(a, it, ring, part, bt_lds, page0, wave, lane, wpr, phase, wrow, active, on0, on1, qa, nl);
+  else
+    score_steps<2>(a, it, ring, part, bt_lds, page0, wave, lane, wpr, phase, wrow, active, on0, on1, qa, nl);
 }
 
 // VALU path: each wave owns whole 64-key quads (4 pages) of the chunk -- quad q goes
@@ -306,11 +394,11 @@ __global__ __launch_bounds__(kThreads, 2) void score_valu_kernel(ScoreArgs a) {
   const int32_t R = it.O * a.G;
   const int32_t r0 = it.rg * kRowsPerGroup;
   const int32_t r1 = min(R, r0 + kRowsPerGroup);
-  const int32_t q_end = min(it.chunk * a.chunk_steps + a.chunk_steps, it.nsteps) * 2;
+  const int32_t q_end = min(it.chunk * a.chunk_steps + a.chunk_steps, it.nsteps);
   const int32_t nquads = (it.npages + 3) / 4;
   uint8_t *mybuf = kbuf[wave];
 
-  int32_t quad = it.chunk * a.chunk_steps * 2 + wave;
+  int32_t quad = it.chunk * a.chunk_steps + wave;
   if (quad < q_end && quad < nquads) issue_quad(a, it, quad, mybuf, lane);
   for (; quad < q_end && quad < nquads; quad += kWaves) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -427,6 +515,16 @@ struct Plan {
   bool need_zero;
 };
 
+// Work items of sequence i on one path: (row groups) x (chunks of chunk_steps steps).
+inline int64_t seq_items(int32_t start, int32_t len, int64_t O, int32_t G, int32_t chunk_steps) {
+  if (len <= 0 || O <= 0) return 0;
+  const int32_t npages = (start + len + kPage - 1) / kPage;
+  const int32_t nsteps = (npages + kStepPages - 1) / kStepPages;
+  const int32_t nch = (nsteps + chunk_steps - 1) / chunk_steps;
+  const int32_t nrg = (int32_t)((O * G + kRowsPerGroup - 1) / kRowsPerGroup);
+  return (int64_t)nch * nrg;
+}
+
 Plan make_plan(const Batch &b, int32_t G, const int64_t *obs_off_h, const int32_t *len_h,
                const int32_t *start_h) {
   Plan p{};
@@ -449,20 +547,16 @@ Plan make_plan(const Batch &b, int32_t G, const int64_t *obs_off_h, const int32_
     if (O <= 0 || nrg < p.max_rg) p.need_zero = true;
   }
   total_steps *= (int64_t)b.L * b.Hkv;
-  // aim for ~8 work items per resident workgroup slot (256 CUs x 2)
-  int64_t cs = total_steps / (256 * 2 * 8);
-  if (cs < 2) cs = 2;
-  if (cs > 64) cs = 64;
+  // aim for ~4 work items per resident workgroup slot (256 CUs x 2)
+  int64_t cs = total_steps / (256 * 2 * 4);
+  if (cs < 4) cs = 4;
+  if (cs > kMaxChunkSteps) cs = kMaxChunkSteps;
   p.chunk_steps = (int32_t)cs;
   p.items_mfma = p.items_valu = 0;
   for (int i = 0; i < b.S; ++i) {
     const int64_t O = obs_off_h[i + 1] - obs_off_h[i];
-    if (len_h[i] <= 0 || O <= 0) continue;
-    const int32_t npages = (start_h[i] + len_h[i] + kPage - 1) / kPage;
-    const int32_t nsteps = (npages + kStepPages - 1) / kStepPages;
-    const int32_t nch = (nsteps + p.chunk_steps - 1) / p.chunk_steps;
-    const int32_t nrg = (int32_t)((O * G + kRowsPerGroup - 1) / kRowsPerGroup);
-    if (O >= kMfmaMinObservers) p.items_mfma += (int64_t)nch * nrg; else p.items_valu += (int64_t)nch * nrg;
+    const int64_t it = seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
+    if (O >= kMfmaMinObservers) p.items_mfma += it; else p.items_valu += it;
   }
   p.any_partial = p.max_rg > 1;
   return p;
@@ -474,8 +568,8 @@ size_t score_workspace_bytes(const Batch &b, int32_t Hq, const int64_t *obs_off_
                              const int32_t *len_h, const int32_t *start_h) {
   const int32_t G = Hq / b.Hkv;
   const Plan p = make_plan(b, G, obs_off_h, len_h, start_h);
-  size_t bytes = 2 * ((size_t)b.S + 1) * sizeof(int32_t);
-  bytes = (bytes + 255) & ~(size_t)255;
+  size_t bytes = 0;
+  if (b.S > kSmallSeqs) bytes = ((2 * ((size_t)b.S + 1) * sizeof(int32_t)) + 255) & ~(size_t)255;
   if (p.any_partial) bytes += (size_t)p.max_rg * b.L * b.Hkv * b.E * sizeof(float);
   return bytes;
 }
@@ -483,15 +577,19 @@ size_t score_workspace_bytes(const Batch &b, int32_t Hq, const int64_t *obs_off_
 hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale,
                         float *scores, void *ws, size_t ws_bytes, const int64_t *obs_off_h,
                         const int32_t *len_h, const int32_t *start_h, hipStream_t st) {
+  (void)ws_bytes;
   const int32_t G = o.num_q_heads / b.Hkv;
   const Plan p = make_plan(b, G, obs_off_h, len_h, start_h);
   const int64_t LHE = (int64_t)b.L * b.Hkv * b.E;
-  int32_t *off_m = (int32_t *)ws;
-  int32_t *off_v = off_m + (b.S + 1);
-  size_t head = 2 * ((size_t)b.S + 1) * sizeof(int32_t);
-  head = (head + 255) & ~(size_t)255;
+  const bool small = b.S <= kSmallSeqs;
+  int32_t *off_m = nullptr, *off_v = nullptr;
+  size_t head = 0;
+  if (!small) {
+    off_m = (int32_t *)ws;
+    off_v = off_m + (b.S + 1);
+    head = ((2 * ((size_t)b.S + 1) * sizeof(int32_t)) + 255) & ~(size_t)255;
+  }
   float *partial = p.any_partial ? (float *)((uint8_t *)ws + head) : nullptr;
-  (void)ws_bytes;
 
   // Every live entry of a scored sequence is written by exactly one work item (or,
   // with several row groups, one per group).  Zero-fill is needed only for
@@ -502,7 +600,8 @@ hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers 
     zero_kernel<<<(unsigned)((nz + 255) / 256), 256, 0, st>>>(z, nz);
   }
   if (p.items_mfma + p.items_valu == 0) return hipGetLastError();
-  score_items_kernel<<<1, 256, 0, st>>>(b.start, b.len, o.obs_off, b.S, G, p.chunk_steps, off_m, off_v);
+  if (!small)
+    score_items_kernel<<<1, 256, 0, st>>>(b.start, b.len, o.obs_off, b.S, G, p.chunk_steps, off_m, off_v);
 
   ScoreArgs a{};
   a.k = (const uint16_t *)c.k;
@@ -517,20 +616,30 @@ hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers 
   a.chunk_steps = p.chunk_steps;
   a.partials = p.any_partial ? 1 : 0;
   a.alpha = scale * kLog2e;
+  a.use_small = small ? 1 : 0;
   const int64_t LH = (int64_t)b.L * b.Hkv;
-  if (p.items_mfma > 0) {
-    a.item_off = off_m;
-    a.items_per_lg = (int32_t)p.items_mfma;
-    a.total_items = p.items_mfma * LH;
+  for (int path = 0; path < 2; ++path) {
+    const int64_t items = path == 0 ? p.items_mfma : p.items_valu;
+    if (items == 0) continue;
+    if (small) {
+      int32_t acc = 0;
+      for (int i = 0; i < b.S; ++i) {
+        a.small_off[i] = acc;
+        const int64_t O = obs_off_h[i + 1] - obs_off_h[i];
+        const bool mine = (O >= kMfmaMinObservers) == (path == 0);
+        if (mine) acc += (int32_t)seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
+      }
+      a.small_off[b.S] = acc;
+    } else {
+      a.item_off = path == 0 ? off_m : off_v;
+    }
+    a.items_per_lg = (int32_t)items;
+    a.total_items = items * LH;
     a.padded_items = (a.total_items + 7) & ~(int64_t)7;
-    score_mfma_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
-  }
-  if (p.items_valu > 0) {
-    a.item_off = off_v;
-    a.items_per_lg = (int32_t)p.items_valu;
-    a.total_items = p.items_valu * LH;
-    a.padded_items = (a.total_items + 7) & ~(int64_t)7;
-    score_valu_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
+    if (path == 0)
+      score_mfma_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
+    else
+      score_valu_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
   }
   if (p.any_partial) {
     score_combine_kernel<<<(unsigned)((LHE + 255) / 256), 256, 0, st>>>(partial, scores, LHE, p.max_rg);

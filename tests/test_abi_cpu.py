@@ -64,6 +64,7 @@ def status(code):
 
 
 def test_score_validation():
+    """Every call here is invalid, so none reaches a launch (the pointers are fake)."""
     L = K.lib()
     seqs = HostSeqs([[0, 1, 2]], [0], [40])
     obs, off = _obs(1)
@@ -79,7 +80,9 @@ def test_score_validation():
     assert call(cache=_cache(k=0)) == "KVS_ERR_NULL"
     assert call(scores=None) == "KVS_ERR_NULL"
     assert call(scale=float("nan")) == "KVS_ERR_SHAPE"
-    assert call(wsb=8) == "KVS_ERR_WORKSPACE"
+    # 65 observers x GQA 4 = 260 rows > 256: partial sums need workspace
+    obs65, _ = _obs(1, Hq=4, O_=65)
+    assert call(o=obs65, wsb=8) == "KVS_ERR_WORKSPACE"
     obs_bad, _ = _obs(1, Hq=6)   # not a multiple of Hkv = 4? (Hkv = 1 here, use Hkv=4 cache)
     assert call(cache=_cache(Hkv=4), o=obs_bad) == "KVS_ERR_SHAPE"
     bad = HostSeqs([[0, 1, 9]], [0], [40])          # page 9 outside an 8-page pool

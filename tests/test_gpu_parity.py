@@ -72,6 +72,9 @@ EDGE_CASES = [
     ("long_multi_chunk", 1, 1, 4, [5000, 3333], [0, 13], [24, 18], [700, 1000]),
     ("gqa1", 1, 4, 4, [300, 300], [0, 8], [16, 16], [30, 30]),
     ("valu_row_groups", 1, 1, 32, [300], [0], [15], [40]),
+    # more than 255 sequences: item tables built on the device
+    ("many_seqs", 1, 1, 4, [(37 * i) % 90 + 1 for i in range(300)], [(5 * i) % 16 for i in range(300)],
+     [16 + (i % 3) * 7 if i % 4 else 6 for i in range(300)], [(11 * i) % 50 for i in range(300)]),
 ]
 
 
