@@ -1,4 +1,8 @@
 // Device helpers for the per-stream kernels (one 1024-thread workgroup per stream).
+//
+// Wave-level sums and scans use DPP row shifts and row broadcasts (VALU only, no
+// LDS crossbar round trips): four row_shr steps scan each 16-lane row, then
+// row_bcast:15 and row_bcast:31 carry the row totals across the wave.
 #pragma once
 
 #include "kvs_internal.h"
@@ -8,38 +12,81 @@ namespace kvs {
 constexpr int kStreamThreads = 1024;
 constexpr int kStreamWaves = kStreamThreads / 64;
 
+// DPP controls (gfx9 encoding)
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+// Inclusive prefix sum over the wave (lane i gets lanes 0..i).
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr1, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr2, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr4, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr8, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false);
+  return x;
+}
+
+// Wave total of a u32 (exact while the total fits in 32 bits), uniform result.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(x), 63);
+}
+
+// Wave total of a u64 (mod 2^64), uniform result: DPP moves of both halves, then a
+// 64-bit add with carry.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum of a u64 over the wave (lane i gets lanes 0..i), mod 2^64.
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+  v += dpp_u64<kRowShr1, 0xF>(v);
+  v += dpp_u64<kRowShr2, 0xF>(v);
+  v += dpp_u64<kRowShr4, 0xF>(v);
+  v += dpp_u64<kRowShr8, 0xF>(v);
+  v += dpp_u64<kRowBcast15, 0xA>(v);
+  v += dpp_u64<kRowBcast31, 0xC>(v);
   return v;
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-    v += ((uint64_t)hi << 32) | lo;
-  }
-  return v;
+  v += dpp_u64<kRowShr1, 0xF>(v);
+  v += dpp_u64<kRowShr2, 0xF>(v);
+  v += dpp_u64<kRowShr4, 0xF>(v);
+  v += dpp_u64<kRowShr8, 0xF>(v);
+  v += dpp_u64<kRowBcast15, 0xA>(v);
+  v += dpp_u64<kRowBcast31, 0xC>(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v &= __shfl_xor(v, d);
-  return v;
+__device__ __forceinline__ uint32_t wave_and(uint32_t x) {
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowShr1, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowShr2, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowShr4, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowShr8, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowBcast15, 0xA, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, kRowBcast31, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v |= __shfl_xor(v, d);
-  return v;
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr1, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr2, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr4, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr8, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Block-wide reductions through a small LDS scratch (kStreamWaves slots).  Every
@@ -66,6 +113,24 @@ __device__ __forceinline__ void block_and_or(uint32_t &a, uint32_t &o, uint32_t 
   __syncthreads();
   a = ra;
   o = ro;
+}
+
+// Exclusive block-wide prefix sum of one u32 per thread (thread order), plus the
+// total.  scratch: kStreamWaves u32.  One barrier pair.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t &total, uint32_t *scratch) {
+  const uint32_t incl = wave_scan_u32(x);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    const uint32_t c = scratch[w];
+    before += (w < wave) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - x;
 }
 
 // Exclusive rank of this thread's flag among all flags of the block in thread order,
@@ -95,7 +160,7 @@ __device__ __forceinline__ uint64_t fixed_mass(uint32_t bits) {
   if (e == 255) return 0;
   const uint64_t mant = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
   const int sh = (int)(e ? e : 1u) - 118;     // s * 2^32 = mant * 2^(E - 118)
-  if (sh >= 0) return sh < 40 ? (mant << sh) : 0;
+  if (sh >= 0) return sh < 32 ? (mant << sh) : 0;
   return sh > -64 ? (mant >> (-sh)) : 0;
 }
 
@@ -107,30 +172,37 @@ __device__ __forceinline__ float *crf_slot(float *crf, const int32_t *bt_row, in
   return crf + (((int64_t)l * num_pages + phys) * Hkv + g) * kPage + (pos & 15);
 }
 
-// Add v into an LDS histogram bin.  Lanes whose bin equals the first valid lane's
-// bin are summed in registers first (one atomic for them), which removes the
-// contention of value distributions concentrated in one bin; the other lanes add
-// directly.
+// Add v into an LDS histogram bin.  When many lanes of the wave share the first
+// valid lane's bin (value distributions concentrated in one bin), those lanes are
+// summed in registers first and added with one atomic; every other lane adds
+// directly.  Must be called by all lanes of the wave.
 __device__ __forceinline__ void hist_add_u64(uint64_t *hist, bool valid, uint32_t bin, uint64_t v) {
   const uint64_t mask = __ballot(valid);
   if (mask == 0) return;
   const int leader = __ffsll((long long)mask) - 1;
-  const uint32_t lb = __shfl(bin, leader);
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
   const bool same = valid && bin == lb;
-  const uint64_t agg = wave_sum_u64(same ? v : 0ull);
-  if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[lb], (unsigned long long)agg);
-  if (valid && !same) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)v);
+  const uint64_t smask = __ballot(same);
+  if (__popcll(smask) >= 8) {
+    const uint64_t agg = wave_sum_u64(same ? v : 0ull);
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[lb], (unsigned long long)agg);
+    if (valid && !same) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)v);
+  } else if (valid) {
+    atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)v);
+  }
 }
 
-__device__ __forceinline__ void hist_add_u32(uint32_t *hist, bool valid, uint32_t bin) {
+// Count version: add 1 per valid lane; the lanes sharing the first valid lane's bin
+// are counted with a popcount and added once.
+__device__ __forceinline__ void hist_add_count(uint64_t *hist, bool valid, uint32_t bin) {
   const uint64_t mask = __ballot(valid);
   if (mask == 0) return;
   const int leader = __ffsll((long long)mask) - 1;
-  const uint32_t lb = __shfl(bin, leader);
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
   const bool same = valid && bin == lb;
-  const uint64_t sm = __ballot(same);
-  if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(sm));
-  if (valid && !same) atomicAdd(&hist[bin], 1u);
+  const uint64_t smask = __ballot(same);
+  if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[lb], (unsigned long long)__popcll(smask));
+  if (valid && !same) atomicAdd((unsigned long long *)&hist[bin], 1ull);
 }
 
 }  // namespace kvs

@@ -4,7 +4,8 @@
 // target region; survivors outside it are paired one-to-one with holes inside it.
 // With K kept and D = n - K, sources are the kept slots below D and destinations
 // the evicted slots at or above D, both ascending; pair t = (source t, dest t).
-// Ranks come from ballot scans in slot order.  Writes are bounded by the stream's
+// Slots are processed in rounds in which each thread takes 16 consecutive slots;
+// one block-wide scan per list and round gives every thread its starting ranks.  Writes are bounded by the stream's
 // capacity min(D, K) so that a keep mask with the wrong count cannot overrun.
 #include "kvs_device.h"
 
@@ -35,26 +36,48 @@ __global__ __launch_bounds__(kStreamThreads) void plan_kernel(PlanArgs a) {
   const int32_t cap = min(D, K);
   int32_t *pp = a.pairs + (((int64_t)lg * a.b.S + i) * a.P) * 2;
   const uint8_t *kp = a.keep + (int64_t)lg * a.b.E + a.b.entry_off[i];
-  uint32_t cs = 0, cd = 0;
+  uint32_t ts = 0, td = 0;
   if (cap > 0 && cap <= a.P) {
-    for (int32_t base = 0; base < n; base += blockDim.x) {
-      const int32_t j = base + threadIdx.x;
-      const bool valid = j < n;
-      const bool k = valid && kp[j] != 0;
-      const bool fs = valid && j < D && k;
-      const bool fd = valid && j >= D && !k;
-      uint32_t ts, td;
-      const uint32_t rs = block_flag_rank(fs, ts, sc1);
-      const uint32_t rd = block_flag_rank(fd, td, sc2);
-      if (fs && cs + rs < (uint32_t)cap) pp[(int64_t)(cs + rs) * 2] = j;
-      if (fd && cd + rd < (uint32_t)cap) pp[(int64_t)(cd + rd) * 2 + 1] = j;
-      cs += ts;
-      cd += td;
+    // rounds of 1024 x 16 slots: thread t owns 16 consecutive slots of the round; one
+    // block scan per list and round gives every thread its starting ranks
+    constexpr int U = 16;
+    uint32_t base_s = 0, base_d = 0;
+    for (int32_t r0 = 0; r0 < n; r0 += U * (int32_t)blockDim.x) {
+      const int32_t j0 = r0 + (int32_t)threadIdx.x * U;
+      uint8_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) kv[u] = (j0 + u < n) ? kp[j0 + u] : (uint8_t)0;
+      uint32_t cs = 0, cd = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t j = j0 + u;
+        cs += (j < n && j < D && kv[u]) ? 1u : 0u;
+        cd += (j < n && j >= D && !kv[u]) ? 1u : 0u;
+      }
+      uint32_t rts, rtd;
+      uint32_t rs = base_s + block_exclusive_scan(cs, rts, sc1);
+      uint32_t rd = base_d + block_exclusive_scan(cd, rtd, sc2);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t j = j0 + u;
+        if (j >= n) continue;
+        if (j < D && kv[u]) {
+          if (rs < (uint32_t)cap) pp[(int64_t)rs * 2] = j;
+          ++rs;
+        } else if (j >= D && !kv[u]) {
+          if (rd < (uint32_t)cap) pp[(int64_t)rd * 2 + 1] = j;
+          ++rd;
+        }
+      }
+      base_s += rts;
+      base_d += rtd;
     }
+    ts = base_s;
+    td = base_d;
   }
   if (threadIdx.x == 0) {
-    uint32_t c = cs < cd ? cs : cd;
-    if (c > (uint32_t)cap) c = (uint32_t)(cap > 0 ? cap : 0);
+    uint32_t c = ts < td ? ts : td;
+    if (c > (uint32_t)(cap > 0 ? cap : 0)) c = (uint32_t)(cap > 0 ? cap : 0);
     a.pair_count[(int64_t)lg * a.b.S + i] = (int32_t)c;
   }
 }

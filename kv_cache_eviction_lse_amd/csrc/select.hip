@@ -20,10 +20,15 @@ struct SelectArgs {
   uint8_t *keep;
   Batch b;
   int32_t cache_cap;
+  int32_t bt_cap;
 };
 
+constexpr int kU = 16;
+constexpr int kBtCap = 4096;
+constexpr int kCacheCap = 35 * 1024;
+
 __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t c_cache[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   __shared__ SelShared sh;
   __shared__ uint32_t flag_scratch[kStreamWaves];
 
@@ -46,24 +51,47 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
     return;
   }
   const bool cached = n <= a.cache_cap;
-  float *crf = (float *)a.crf;
+  uint32_t *c_cache = dyn;
+  int32_t *bt_lds = (int32_t *)(dyn + a.cache_cap);
+  const int32_t npages = (start + n + kPage - 1) / kPage;
+  const bool bt_cached = npages <= a.bt_cap;
+  if (bt_cached) {
+    for (int32_t p = threadIdx.x; p < npages; p += blockDim.x) bt_lds[p] = bt_row[p];
+    __syncthreads();
+  }
+  const int32_t *bt_use = bt_cached ? bt_lds : bt_row;
+  const uint32_t *crf_base = (const uint32_t *)a.crf + (((int64_t)l * a.b.num_pages) * a.b.Hkv + g) * kPage;
+  const int64_t page_stride = (int64_t)a.b.Hkv * kPage;
+  auto crf_addr = [&](int32_t j) -> const uint32_t * {
+    const int32_t pos = start + j;
+    return crf_base + (int64_t)bt_use[pos >> 4] * page_stride + (pos & 15);
+  };
+
   uint32_t band = ~0u, bor = 0u;
-  for (int32_t j = threadIdx.x; j < n; j += blockDim.x) {
-    const uint32_t bits = __float_as_uint(*crf_slot(crf, bt_row, start, j, l, g, a.b.num_pages, a.b.Hkv));
-    if (cached) c_cache[j] = bits;
-    band &= bits;
-    bor |= bits;
+  for (int32_t base = 0; base < n; base += kU * (int32_t)blockDim.x) {
+    uint32_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+      v[u] = j < n ? *crf_addr(j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+      if (j < n) {
+        if (cached) c_cache[j] = v[u];
+        band &= v[u];
+        bor |= v[u];
+      }
+    }
   }
   block_and_or(band, bor, (uint32_t *)sh.scratch);
-  auto crf_of = [&](int32_t j) -> uint32_t {
-    return cached ? c_cache[j]
-                  : __float_as_uint(*crf_slot(crf, bt_row, start, j, l, g, a.b.num_pages, a.b.Hkv));
-  };
+  auto crf_of = [&](int32_t j) -> uint32_t { return cached ? c_cache[j] : *crf_addr(j); };
   auto one = [](uint32_t) -> uint64_t { return 1; };
   auto all = [](int32_t) { return true; };
 
   // level 1: CRF
-  const SelResult r1 = radix_select32(n, crf_of, all, one, (uint64_t)K, band, bor, sh);
+  const SelResult r1 = radix_select32<true>(n, crf_of, all, one, (uint64_t)K, band, bor, sh);
   const uint32_t cstar = r1.key;
   const uint64_t need = K - r1.above;                 // entries to keep among CRF == c*
   const bool lvl2 = need < r1.at;
@@ -72,44 +100,60 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
   if (lvl2) {
     // level 2: s among the CRF ties
     uint32_t sa = ~0u, so = 0u;
-    for (int32_t j = threadIdx.x; j < n; j += blockDim.x) {
-      if (crf_of(j) == cstar) {
-        const uint32_t s = sp[j];
-        sa &= s;
-        so |= s;
+    for (int32_t base = 0; base < n; base += kU * (int32_t)blockDim.x) {
+      uint32_t c[kU], v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        c[u] = j < n ? crf_of(j) : ~cstar;
+        v[u] = j < n ? sp[j] : 0u;
       }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (c[u] == cstar) { sa &= v[u]; so |= v[u]; }
     }
     block_and_or(sa, so, (uint32_t *)sh.scratch);
     auto s_of = [&](int32_t j) -> uint32_t { return sp[j]; };
     auto in_tie = [&](int32_t j) { return crf_of(j) == cstar; };
-    const SelResult r2 = radix_select32(n, s_of, in_tie, one, need, sa, so, sh);
+    const SelResult r2 = radix_select32<true>(n, s_of, in_tie, one, need, sa, so, sh);
     sstar = r2.key;
     need2 = need - r2.above;
     at2 = r2.at;
   }
   const bool lvl3 = lvl2 && need2 < at2;
 
-  uint64_t carry = 0;
-  for (int32_t base = 0; base < n; base += blockDim.x) {
-    const int32_t j = base + threadIdx.x;
-    const bool valid = j < n;
-    const uint32_t c = valid ? crf_of(j) : 0u;
-    bool k;
-    if (!lvl2) {
-      k = valid && c >= cstar;
-    } else {
-      const uint32_t s = valid && c == cstar ? sp[j] : 0u;
-      if (lvl3) {
-        const bool tie = valid && c == cstar && s == sstar;
-        uint32_t tot;
-        const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
-        k = valid && (c > cstar || (c == cstar && (s > sstar || (tie && carry + rk < need2))));
-        carry += tot;
-      } else {
-        k = valid && (c > cstar || (c == cstar && s >= sstar));
+  if (!lvl3) {
+    for (int32_t base = 0; base < n; base += kU * (int32_t)blockDim.x) {
+      uint32_t c[kU], v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        c[u] = j < n ? crf_of(j) : 0u;
+        v[u] = (lvl2 && j < n) ? sp[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        if (j < n) {
+          const bool k = lvl2 ? (c[u] > cstar || (c[u] == cstar && v[u] >= sstar)) : c[u] >= cstar;
+          kp[j] = k ? 1 : 0;
+        }
       }
     }
-    if (valid) kp[j] = k ? 1 : 0;
+  } else {
+    uint64_t carry = 0;
+    for (int32_t base = 0; base < n; base += blockDim.x) {
+      const int32_t j = base + threadIdx.x;
+      const bool valid = j < n;
+      const uint32_t c = valid ? crf_of(j) : 0u;
+      const uint32_t s = valid && c == cstar ? sp[j] : 0u;
+      const bool tie = valid && c == cstar && s == sstar;
+      uint32_t tot;
+      const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
+      const bool k = valid && (c > cstar || (c == cstar && (s > sstar || (tie && carry + rk < need2))));
+      carry += tot;
+      if (valid) kp[j] = k ? 1 : 0;
+    }
   }
 }
 
@@ -118,11 +162,11 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
 hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores,
                          const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st) {
   static bool attr_set = false;
-  const int32_t cap = 39 * 1024;
-  const size_t dyn = (size_t)(max_len <= cap ? max_len : 0) * sizeof(uint32_t);
+  const int32_t cache = max_len <= kCacheCap ? max_len : 0;
+  const size_t dyn = ((size_t)cache + kBtCap) * sizeof(uint32_t);
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap * 4);
+    hipError_t e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (kCacheCap + kBtCap) * 4);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -132,7 +176,8 @@ hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores
   a.budget = budget;
   a.keep = keep;
   a.b = b;
-  a.cache_cap = max_len <= cap ? max_len : 0;
+  a.cache_cap = cache;
+  a.bt_cap = kBtCap;
   dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
   select_kernel<<<grid, kStreamThreads, dyn, st>>>(a);
   return hipGetLastError();

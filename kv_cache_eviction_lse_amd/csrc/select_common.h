@@ -25,8 +25,9 @@ struct SelShared {
   uint64_t found[4];
 };
 
-// key_of(j) -> uint32 key; ok(j) -> candidate?; weight_of(key) -> uint64
-template <typename KeyF, typename OkF, typename WF>
+// key_of(j) -> uint32 key; ok(j) -> candidate?; weight_of(key) -> uint64.
+// COUNT: every weight is 1 (weight_of is not called in the histogram passes).
+template <bool COUNT, typename KeyF, typename OkF, typename WF>
 __device__ SelResult radix_select32(int32_t n, KeyF key_of, OkF ok, WF weight_of, uint64_t target,
                                     uint32_t and_all, uint32_t or_all, SelShared &sh) {
   SelResult r;
@@ -54,40 +55,43 @@ __device__ SelResult radix_select32(int32_t n, KeyF key_of, OkF ok, WF weight_of
     for (int b = threadIdx.x; b < 256; b += blockDim.x) sh.hist[b] = 0;
     __syncthreads();
     const int hs = top + 1;
-    for (int32_t base = 0; base < n; base += blockDim.x) {
-      const int32_t j = base + threadIdx.x;
-      bool v = false;
-      uint32_t key = 0;
-      if (j < n && ok(j)) {
-        key = key_of(j);
-        v = hs >= 32 ? true : ((key >> hs) == (prefix >> hs));
+    // 8 keys per thread per round, loaded before any is used (latency overlap)
+    constexpr int U = 8;
+    for (int32_t base = 0; base < n; base += U * (int32_t)blockDim.x) {
+      uint32_t keys[U];
+      bool ok_[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        ok_[u] = j < n && ok(j);
+        keys[u] = ok_[u] ? key_of(j) : 0u;
       }
-      const uint32_t bin = (key >> lo) & (nb - 1u);
-      hist_add_u64(sh.hist, v, bin, v ? weight_of(key) : 0ull);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t key = keys[u];
+        const bool v = ok_[u] && (hs >= 32 ? true : ((key >> hs) == (prefix >> hs)));
+        const uint32_t bin = (key >> lo) & (nb - 1u);
+        if (COUNT) hist_add_count(sh.hist, v, bin);
+        else hist_add_u64(sh.hist, v, bin, v ? weight_of(key) : 0ull);
+      }
     }
     __syncthreads();
     if (threadIdx.x < 64) {
-      // lane L owns bins 4L .. 4L+3; suffix-scan the lane sums, then walk down
+      // lane L owns bins nb-1-4L .. nb-4-4L (descending), so an exclusive prefix sum
+      // over lanes is the weight of all higher bins
       uint64_t h[4], ls = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t b = 4 * lane + q;
-        h[q] = b < nb ? sh.hist[b] : 0ull;
+        const int b = (int)nb - 1 - (4 * lane + q);
+        h[q] = b >= 0 ? sh.hist[b] : 0ull;
         ls += h[q];
       }
-      uint64_t x = ls;
+      uint64_t acc = wave_scan_u64(ls) - ls;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t ylo = __shfl_down((uint32_t)x, d);
-        const uint32_t yhi = __shfl_down((uint32_t)(x >> 32), d);
-        if (lane + d < 64) x += ((uint64_t)yhi << 32) | ylo;
-      }
-      uint64_t acc = x - ls;     // weight of bins in higher lanes
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        const uint32_t b = 4 * lane + q;
-        if (b < nb && acc < need && need <= acc + h[q]) {
-          sh.found[0] = b;
+      for (int q = 0; q < 4; ++q) {
+        const int b = (int)nb - 1 - (4 * lane + q);
+        if (b >= 0 && acc < need && need <= acc + h[q]) {
+          sh.found[0] = (uint64_t)b;
           sh.found[1] = acc;
           sh.found[2] = h[q];
         }
