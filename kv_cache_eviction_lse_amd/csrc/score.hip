@@ -12,7 +12,8 @@
 //       observer rows on M and the keys on N, so each lane ends up holding one key
 //       and 16 rows: the exp and the row sum stay in-lane.  K pages stream from HBM
 //       straight into LDS (global_load_lds_dwordx4, 1 KiB per instruction, XOR-
-//       swizzled 16-byte chunks), double-buffered, shared by the 4 waves.
+//       swizzled 16-byte chunks) through a 4-step ring shared by the 4 waves; with more
+//       than 128 rows the MFMAs of one key tile overlap the exp work of the previous one.
 //   score_valu_kernel : observers < 16.  One key per lane, 64 keys per wave; the
 //       key row is pulled from LDS into registers and every observer row (uniform
 //       across the wave, so it lives in SGPRs) is dotted with v_dot2c_f32_bf16.
@@ -98,6 +99,31 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
   return true;
 }
 
+// One LDS DMA instruction: lane t's 16 bytes from src land at LDS byte address
+// lds + 16 t (lds is wave-uniform; M0 carries it).  Written as inline asm because the
+// compiler cannot tell which LDS bytes a pending DMA will write, so after the builtin
+// form it drains every outstanding vector load before the next LDS read, i.e. the
+// whole prefetch ring at every step.  Ordering is explicit instead: a slot is read
+// only after the ring barrier's vmcnt wait and s_barrier, and refilled only after
+// the barrier that follows the last read of it.  No output registers; the address
+// registers are consumed at issue.  M0 is saved and restored around the DMA.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
 // Issue this wave's page (page w of the 4-page step) into an LDS ring slot.  Lane t
 // of instruction r fills LDS chunk t%16 of page row 4r + t/16 with global chunk
 // (t%16) ^ row, so that a later read of chunk c of row n lands on c ^ (n%16).  Page
@@ -111,12 +137,12 @@ __device__ __forceinline__ int issue_step(const ScoreArgs &a, const Item &it, in
   const uint16_t *page = a.k + (((int64_t)it.l * a.b.num_pages + phys) * a.b.Hkv + it.g) * kPageElems;
   const int row_in_instr = lane >> 4;
   const int chunk = lane & 15;
+  const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(buf + wave * (kPageElems * 2)));
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * r + row_in_instr;
     const uint16_t *src = page + row * kHeadDim + ((chunk ^ row) << 3);
-    uint8_t *dst = buf + wave * (kPageElems * 2) + r * 1024;
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
+    lds_dma16(src, dst0 + r * 1024);
   }
   return 4;
 }
@@ -282,9 +308,143 @@ __device__ __forceinline__ void score_steps(const ScoreArgs &a, const Item &it, 
   }
 }
 
+// sum over both M tiles of exp2(acc * alpha - lse*log2e): 32 values per lane, four
+// independent partial sums.
+__device__ __forceinline__ float exp_rows2(const floatx16 &x0, const floatx16 &x1, float alpha,
+                                           const float (*nl)[16]) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) {
+    s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(x0[k], alpha, nl[0][k]));
+    s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(x0[k + 1], alpha, nl[0][k + 1]));
+    s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(x1[k], alpha, nl[1][k]));
+    s3 += __builtin_amdgcn_exp2f(__builtin_fmaf(x1[k + 1], alpha, nl[1][k + 1]));
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// One pipeline phase: the QK^T MFMAs of the next key tile (read from LDS into kb)
+// overlapped with the exp/sum of the previous tile's accumulators.  The scheduling
+// barriers fix the issue order: the 8 LDS reads first, then one MFMA per six VALU
+// operations, so that the matrix core runs while the exp work issues.
+__device__ __forceinline__ float pipe_phase(const uint8_t *buf, int tt, int col, int half,
+                                            const bf16x8 (*qa)[8], floatx16 &n0, floatx16 &n1,
+                                            const floatx16 &p0, const floatx16 &p1, float alpha,
+                                            const float (*nl)[16]) {
+  bf16x8 kb[8];
+  read_tile(buf, tt, col, half, kb);
+  floatx16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], c1, 0, 0, 0);
+  }
+  const float v = exp_rows2(p0, p1, alpha, nl);
+  n0 = c0;
+  n1 = c1;
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+  return v;
+}
+
+// Exp/sum of the last tile (no MFMA work left to overlap).
+__device__ __forceinline__ float pipe_drain(const floatx16 &p0, const floatx16 &p1, float alpha,
+                                            const float (*nl)[16]) {
+  return exp_rows2(p0, p1, alpha, nl);
+}
+
+// Main loop for row groups of more than 128 rows: every active wave owns 64 rows (two
+// M tiles; rows past the end have zero Q and LSE +inf, so they add exactly 0) and
+// takes both key tiles of every step.  Tile j's MFMAs overlap tile j-1's exp work:
+//   phase A of step k:  MFMA(k, tile 1)    || exp(k, tile 0)
+//   phase B of step k:  ring barrier(k+1), refill, combine;
+//                       MFMA(k+1, tile 0)  || exp(k, tile 1)
+// Each wave writes its per-lane partial sums (both lane halves) to part[k % 3]; wave
+// 0 combines tile 0 and wave 1 tile 1 of a step once a barrier has passed after every
+// wave wrote them.  Three partial buffers keep a buffer from being rewritten before
+// it is combined (a wave can be at most one barrier ahead of the combining wave).
+__device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item &it,
+                                                 uint8_t (*ring)[kStepBytes],
+                                                 float (*part)[kStepTiles][kWaves][64],
+                                                 const int32_t *bt_lds, int32_t page0, int wave, int lane,
+                                                 int wpr, int wrow, bool active, const bf16x8 (*qa)[8],
+                                                 const float (*nl)[16]) {
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int32_t s_begin = it.chunk * a.chunk_steps;
+  const int32_t s_end = min(s_begin + a.chunk_steps, it.nsteps);
+  const int32_t ntiles = (it.start + it.n + kTileKeys - 1) / kTileKeys;
+  auto nloads = [&](int32_t j) -> int { return (j < s_end && j * kStepPages + wave < it.npages) ? 4 : 0; };
+  // sum the wpr partials of (step, tt) and store the 32 keys
+  auto combine = [&](int32_t step, int tt) {
+    const float *pp = &part[(step - s_begin) % 3][tt][0][0];
+    float v = 0.f;
+    for (int w = 0; w < wpr; ++w) v += pp[w * 64 + lane] + pp[w * 64 + 32 + lane];
+    const int32_t tile = step * kStepTiles + tt;
+    if (tile < ntiles) store_key(a, it, tile, lane, v);
+  };
+
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u)
+    if (s_begin + u < s_end) issue_step(a, it, s_begin + u, ring[u], bt_lds, page0, wave, lane);
+  ring_barrier(nloads(s_begin + 1) + nloads(s_begin + 2));
+  if (s_begin + kRing - 1 < s_end)
+    issue_step(a, it, s_begin + kRing - 1, ring[kRing - 1], bt_lds, page0, wave, lane);
+
+  floatx16 t0a = {}, t0b = {}, t1a = {}, t1b = {};
+  if (active) {
+    bf16x8 kb[8];
+    read_tile(ring[0], 0, col, half, kb);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      t0a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], t0a, 0, 0, 0);
+      t0b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], t0b, 0, 0, 0);
+    }
+  }
+  for (int32_t step = s_begin; step < s_end; ++step) {
+    const int k = step - s_begin;
+    const int cur = k & (kRing - 1);
+    float *mine = &part[k % 3][0][wrow][0];
+    // phase A
+    if (active) {
+      const float v = pipe_phase(ring[cur], 1, col, half, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
+      mine[lane] = v;                                   // part[k % 3][0][wrow][lane]
+    }
+    // phase B
+    const bool more = step + 1 < s_end;
+    if (more) {
+      ring_barrier(nloads(step + 2) + nloads(step + 3));
+      if (step + kRing < s_end)
+        issue_step(a, it, step + kRing, ring[cur], bt_lds, page0, wave, lane);
+      if (lane < 32) {
+        if (wave == 0) combine(step, 0);
+        else if (wave == 1 && step > s_begin) combine(step - 1, 1);
+      }
+      if (active) {
+        const float v = pipe_phase(ring[(k + 1) & (kRing - 1)], 0, col, half, qa, t0a, t0b, t1a, t1b,
+                                   a.alpha, nl);
+        mine[kWaves * 64 + lane] = v;                   // part[k % 3][1][wrow][lane]
+      }
+    } else if (active) {
+      mine[kWaves * 64 + lane] = pipe_drain(t1a, t1b, a.alpha, nl);
+    }
+  }
+  __syncthreads();
+  if (lane < 32) {
+    const int32_t last = s_end - 1;
+    if (wave == 0) combine(last, 0);
+    else if (wave == 1) combine(last, 1);
+    else if (wave == 2 && last > s_begin) combine(last - 1, 1);
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
-  __shared__ float part[2][kStepTiles][kWaves][kTileKeys];
+  __shared__ float part[3][kStepTiles][kWaves][64];
   __shared__ int32_t bt_lds[kMaxChunkSteps * kStepPages];
 
   Item it;
@@ -355,9 +515,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
   __syncthreads();
 
   if (nph == 1)
-    score_steps<1>(a, it, ring, part, bt_lds, page0, wave, lane, wpr, phase, wrow, active, on0, on1, qa, nl);
+    score_steps_pipe(a, it, ring, part, bt_lds, page0, wave, lane, wpr, wrow, active, qa, nl);
   else
-    score_steps<2>(a, it, ring, part, bt_lds, page0, wave, lane, wpr, phase, wrow, active, on0, on1, qa, nl);
+    score_steps<2>(a, it, ring, (float (*)[kStepTiles][kWaves][kTileKeys])part, bt_lds, page0, wave, lane,
+                   wpr, phase, wrow, active, on0, on1, qa, nl);
 }
 
 // VALU path: each wave owns whole 64-key quads (4 pages) of the chunk -- quad q goes
@@ -373,12 +534,12 @@ __device__ __forceinline__ void issue_quad(const ScoreArgs &a, const Item &it, i
     if (lp < it.npages) {
       const int64_t phys = bt[lp];
       const uint16_t *page = a.k + (((int64_t)it.l * a.b.num_pages + phys) * a.b.Hkv + it.g) * kPageElems;
+      const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(buf + pp * (kPageElems * 2)));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * r + (lane >> 4);
         const uint16_t *src = page + row * kHeadDim + (((lane & 15) ^ row) << 3);
-        __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (lds_void *)(buf + pp * (kPageElems * 2) + r * 1024), 16, 0, 0);
+        lds_dma16(src, dst0 + r * 1024);
       }
     }
   }
