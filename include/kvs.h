@@ -10,6 +10,7 @@
  *   kvs_lrfu_update  the attention-mass cut ("action-critical" hits) and the LRFU
  *                    update of each entry's combined recency-frequency value (CRF)
  *   kvs_select       the per-(layer, KV head) keep set of exactly min(B, n) entries
+ *   kvs_lrfu_select  the two calls above fused (same results, one pass over the data)
  *   kvs_plan         the conflict-free slot plan: kept rows outside the tail paired
  *                    with evicted slots inside it; the freed pages (host side)
  *   kvs_compact      one in-place pass that moves K row, V row and CRF per pair
@@ -183,6 +184,16 @@ float kvs_lrfu_decay(double lambda, int32_t dt);
 kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
                       const int32_t *budget, const int32_t *budget_h, uint8_t *keep,
                       void *stream);
+
+/*
+ * kvs_lrfu_select -- kvs_lrfu_update followed by kvs_select in one call, with the
+ * same arguments, validation and results (crf, hit and keep are written exactly as
+ * the two calls would write them).  Each stream's scores and CRF are read once.
+ */
+kvs_status kvs_lrfu_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
+                           uint32_t mass_num, uint32_t mass_den, const float *decay,
+                           const int32_t *n_prev, uint8_t *hit, const int32_t *budget,
+                           const int32_t *budget_h, uint8_t *keep, void *stream);
 
 /*
  * Per-stream capacity of the move-pair buffer for this batch and budget:

@@ -21,7 +21,8 @@ STATUS = {0: "KVS_OK", 1: "KVS_ERR_NULL", 2: "KVS_ERR_SHAPE", 3: "KVS_ERR_UNSUPP
           4: "KVS_ERR_WORKSPACE", 5: "KVS_ERR_HIP"}
 
 EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_workspace_size",
-           "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_pair_capacity",
+           "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_lrfu_select",
+           "kvs_pair_capacity",
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_budget_ratchet")
 
 
@@ -77,6 +78,8 @@ def lib() -> C.CDLL:
         L.kvs_lrfu_decay.argtypes = [C.c_double, C.c_int32]
         L.kvs_select.restype = C.c_int
         L.kvs_select.argtypes = [P, P, P, P, P, P, P]
+        L.kvs_lrfu_select.restype = C.c_int
+        L.kvs_lrfu_select.argtypes = [P, P, P, C.c_uint32, C.c_uint32, P, P, P, P, P, P, P]
         L.kvs_pair_capacity.restype = C.c_int64
         L.kvs_pair_capacity.argtypes = [P, P]
         L.kvs_plan.restype = C.c_int
@@ -214,6 +217,14 @@ def kvs_select(cache: PagedCache, seqs: SeqBatch, scores, budget, budget_h: np.n
     budget_h = np.ascontiguousarray(budget_h, np.int32)
     _check(lib().kvs_select(cache.ref, seqs.ref, _ptr(scores), _ptr(budget), _ptr(budget_h),
                             _ptr(keep), _stream(stream)))
+
+
+def kvs_lrfu_select(cache: PagedCache, seqs: SeqBatch, scores, mass_num: int, mass_den: int, decay, n_prev,
+                    budget, budget_h: np.ndarray, keep, hit=None, stream=None) -> None:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    _check(lib().kvs_lrfu_select(cache.ref, seqs.ref, _ptr(scores), mass_num, mass_den, _ptr(decay),
+                                 _ptr(n_prev), _ptr(hit), _ptr(budget), _ptr(budget_h), _ptr(keep),
+                                 _stream(stream)))
 
 
 def kvs_pair_capacity(seqs: SeqBatch, budget_h: np.ndarray) -> int:

@@ -194,8 +194,12 @@ kvs_status kvs_lrfu_update(const kvs_cache *cache, const kvs_seqs *seqs, const f
   const kvs::Batch b = make_batch(cache, seqs);
   if (b.E == 0) return ok();
   if (!scores || !decay || !n_prev) return fail(KVS_ERR_NULL, "scores/decay/n_prev is NULL");
-  return hip_status(kvs::launch_lrfu(*cache, b, scores, mass_num, mass_den, decay, n_prev, hit,
-                                     max_len_of(seqs), (hipStream_t)stream));
+  const int32_t max_len = max_len_of(seqs);
+  if (kvs::stream_reg_fits(max_len, cache->num_pages, cache->num_kv_heads))
+    return hip_status(kvs::launch_stream_reg(*cache, b, scores, true, false, mass_num, mass_den, decay, n_prev, hit,
+                                             nullptr, nullptr, (hipStream_t)stream));
+  return hip_status(kvs::launch_lrfu(*cache, b, scores, mass_num, mass_den, decay, n_prev, hit, max_len,
+                                     (hipStream_t)stream));
 }
 
 kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, const int32_t *budget,
@@ -210,7 +214,36 @@ kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float 
   const kvs::Batch b = make_batch(cache, seqs);
   if (b.E == 0) return ok();
   if (!scores || !keep) return fail(KVS_ERR_NULL, "scores/keep is NULL");
-  return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len_of(seqs), (hipStream_t)stream));
+  const int32_t max_len = max_len_of(seqs);
+  if (kvs::stream_reg_fits(max_len, cache->num_pages, cache->num_kv_heads))
+    return hip_status(kvs::launch_stream_reg(*cache, b, scores, false, true, 0, 1, nullptr, nullptr, nullptr,
+                                             budget, keep, (hipStream_t)stream));
+  return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, (hipStream_t)stream));
+}
+
+kvs_status kvs_lrfu_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, uint32_t mass_num,
+                           uint32_t mass_den, const float *decay, const int32_t *n_prev, uint8_t *hit,
+                           const int32_t *budget, const int32_t *budget_h, uint8_t *keep, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, false, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if (mass_den == 0 || mass_num > mass_den)
+    return fail(KVS_ERR_SHAPE, "mass fraction %u/%u must satisfy 0 <= num <= den, den > 0", mass_num, mass_den);
+  if (seqs->num_seqs == 0) return ok();
+  if (!budget || !budget_h) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  if (!scores || !decay || !n_prev || !keep) return fail(KVS_ERR_NULL, "scores/decay/n_prev/keep is NULL");
+  const int32_t max_len = max_len_of(seqs);
+  if (kvs::stream_reg_fits(max_len, cache->num_pages, cache->num_kv_heads))
+    return hip_status(kvs::launch_stream_reg(*cache, b, scores, true, true, mass_num, mass_den, decay, n_prev, hit,
+                                             budget, keep, (hipStream_t)stream));
+  hipError_t e = kvs::launch_lrfu(*cache, b, scores, mass_num, mass_den, decay, n_prev, hit, max_len,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, (hipStream_t)stream));
 }
 
 int64_t kvs_pair_capacity(const kvs_seqs *seqs, const int32_t *budget_h) {

@@ -1,0 +1,409 @@
+// Register-resident per-stream kernels: the attention-mass cut with the LRFU update,
+// the top-B keep set, or both in one pass over the data.  One 1024-thread workgroup
+// per stream; thread t holds the scores and CRF of slots u * 1024 + t (u < kRegU) in
+// registers, so each input is read from memory once and every selection pass runs
+// on registers.  Streams longer than kRegU * 1024 entries take the kernels of
+// lrfu.hip and select.hip.
+//
+// ActKV Dissected, Component 1: hits are the shortest prefix of (s desc, slot asc)
+// holding the mass fraction num/den of the stream's integer attention mass
+// m = floor(s * 2^32); LRFU with lambda = 0.5 gives CRF <- fma(d, CRF, hit), the prior
+// taken as 0 for entries appended since the previous round.  Summary / Results: a
+// fixed entry budget per head keeps the first K = min(B, n) entries of
+// (CRF desc, s desc, slot asc).  Both orders compare fp32 bit patterns (values >= 0)
+// and ties at a threshold go to the lowest slots, so the results are exact.
+//
+// Selection: radix search on the key bits below the candidates' common prefix (from
+// the AND and OR of their keys), 12 bits per pass, with a 4096-bin LDS histogram of
+// counts or of integer masses; the crossing bin is found with one block-wide scan.
+#include "kvs_device.h"
+
+namespace kvs {
+
+constexpr int kRegU = 33;                                        // slots per thread
+constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 33792 entries per stream
+constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+
+namespace {
+
+struct StreamArgs {
+  const float *scores;
+  float *crf;
+  uint8_t *hit;          // nullable
+  const float *decay;
+  const int32_t *n_prev;
+  const int32_t *budget;
+  uint8_t *keep;
+  Batch b;
+  uint32_t num, den;
+};
+
+struct RegShared {
+  uint64_t hist[kBins];
+  uint64_t scratch[kStreamWaves];
+  uint64_t found[3];
+};
+
+struct Sel {
+  uint32_t key;     // v*
+  uint64_t above;   // weight of candidates with key > v*
+  uint64_t at;      // weight of candidates with key == v*
+};
+
+// Exclusive block-wide prefix sum of a u64 (thread order).  One barrier pair.
+__device__ __forceinline__ uint64_t block_excl_u64(uint64_t x, uint64_t *scratch) {
+  const uint64_t incl = wave_scan_u64(x);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) scratch[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += scratch[w];
+  __syncthreads();
+  return before + incl - x;
+}
+
+// A copy of x the compiler cannot see through: index arithmetic derived from it is
+// recomputed where it is used instead of being kept live (and spilled) across the
+// whole kernel (per-row masks and indices would otherwise be hoisted out of the
+// pass loops).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// v* with weight(keys > v*) < target <= weight(keys >= v*) over the candidates
+// (slot valid and cand(u)); key[u] holds the key of this thread's row u.
+template <bool COUNT, typename CandF, typename WF>
+__device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt, CandF cand, WF weight_of,
+                                          uint64_t target, uint32_t and_all, uint32_t or_all, RegShared &sh) {
+  Sel r;
+  const uint32_t diff = and_all ^ or_all;
+  if (diff == 0) {
+    uint64_t w = 0;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u)
+      if (u < cnt && cand(u)) w += COUNT ? 1ull : weight_of(key[u]);
+    r.key = and_all;
+    r.above = 0;
+    r.at = block_sum_u64(w, sh.scratch);
+    return r;
+  }
+  int top = 31 - __clz(diff);
+  uint32_t prefix = top == 31 ? 0u : (and_all & ~((2u << top) - 1u));
+  uint64_t need = target, above = 0, at = 0;
+  while (top >= 0) {
+    const int width = top + 1 < kDigitBits ? top + 1 : kDigitBits;
+    const int lo = top - width + 1;
+    const uint32_t nb = 1u << width;
+    for (uint32_t b = threadIdx.x; b < nb; b += kStreamThreads) sh.hist[b] = 0;
+    __syncthreads();
+    const int hs = top + 1;
+    const int cnt_p = opaque(cnt);
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      // (the weight of a key is pass-invariant; computing it from an opaque copy keeps
+      // the compiler from hoisting all kRegU weights out of the pass loop)
+      const uint32_t k = COUNT ? key[u] : (uint32_t)opaque((int)key[u]);
+      const bool v = u < cnt_p && cand(u) && (hs >= 32 || (k >> hs) == (prefix >> hs));
+      const uint32_t bin = (k >> lo) & (nb - 1u);
+      if (COUNT) hist_add_count(sh.hist, v, bin);
+      else hist_add_u64(sh.hist, v, bin, v ? weight_of(k) : 0ull);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // bins in descending order, 4 per thread; the exclusive scan is the weight of all
+    // higher bins
+    uint64_t h[4], ls = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = (int)nb - 1 - (4 * (int)threadIdx.x + q);
+      h[q] = b >= 0 ? sh.hist[b] : 0ull;
+      ls += h[q];
+    }
+    uint64_t acc = block_excl_u64(ls, sh.scratch);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = (int)nb - 1 - (4 * (int)threadIdx.x + q);
+      if (b >= 0 && acc < need && need <= acc + h[q]) {
+        sh.found[0] = (uint64_t)b;
+        sh.found[1] = acc;
+        sh.found[2] = h[q];
+      }
+      acc += h[q];
+    }
+    __syncthreads();
+    const uint32_t b = (uint32_t)sh.found[0];
+    const uint64_t a = sh.found[1];
+    at = sh.found[2];
+    __syncthreads();
+    prefix |= b << lo;
+    need -= a;
+    above += a;
+    top = lo - 1;
+  }
+  r.key = prefix;
+  r.above = above;
+  r.at = at;
+  return r;
+}
+
+// Stores for slot rows: rows u < full exist in every thread (uniform branch); the
+// partial row after them is predicated per lane.
+#define KVS_FOR_VALID(u, ...)   \
+  if ((u) < full) {             \
+    __VA_ARGS__                 \
+  } else if ((u) < cnt) {       \
+    __VA_ARGS__                 \
+  }
+
+template <bool LRFU, bool SELECT>
+__global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a) {
+  __shared__ int32_t bt_lds[kRegBtCap];
+  __shared__ RegShared sh;
+  __shared__ uint32_t flag_scratch[kStreamWaves];
+
+  const int32_t i = blockIdx.y;
+  const int32_t lg = blockIdx.x;
+  const int32_t n = a.b.len[i];
+  if (n <= 0) return;
+  const int32_t l = lg / a.b.Hkv;
+  const int32_t g = lg - l * a.b.Hkv;
+  const int64_t e0 = a.b.entry_off[i];
+  const int32_t start = a.b.start[i];
+  const int32_t tid = threadIdx.x;
+  const int cnt = tid < n ? (n - tid + kStreamThreads - 1) / kStreamThreads : 0;   // rows of this thread
+  const int full = n / kStreamThreads;                                              // rows of every thread
+  const int rounds = (n + kStreamThreads - 1) / kStreamThreads;
+  const uint32_t *sp = (const uint32_t *)(a.scores + (int64_t)lg * a.b.E + e0);
+  // CRF of (layer, head) at 32-bit offsets page * Hkv * 16 + slot-in-page (the host
+  // checks that every offset fits)
+  float *crf_base = a.crf + (((int64_t)l * a.b.num_pages) * a.b.Hkv + g) * kPage;
+  const uint32_t page_stride = (uint32_t)a.b.Hkv * kPage;
+  uint8_t *kp = a.keep + (int64_t)lg * a.b.E + e0;
+
+  int32_t K = 0;
+  if (SELECT) {
+    const int32_t bud = a.budget[i];
+    K = bud < n ? (bud > 0 ? bud : 0) : n;
+    if (!LRFU && (K == 0 || K == n)) {
+      for (int32_t j = tid; j < n; j += kStreamThreads) kp[j] = K == n ? 1 : 0;
+      return;
+    }
+  }
+  const int32_t npages = (start + n + kPage - 1) / kPage;
+  const int32_t *bt_row = a.b.bt + (int64_t)i * a.b.max_pages;
+  for (int32_t p = tid; p < npages; p += kStreamThreads) bt_lds[p] = bt_row[p];
+  // slot of row u (t = this thread's index), clamped to the last live slot so that
+  // loads can be unconditional
+  auto slot = [&](int u, int t) -> int32_t { return min(u * kStreamThreads + t, n - 1); };
+  auto crf_off = [&](int u, int t) -> uint32_t {
+    const int32_t pos = start + slot(u, t);
+    return (uint32_t)bt_lds[pos >> 4] * page_stride + (uint32_t)(pos & 15);
+  };
+
+  uint32_t s[kRegU];
+  uint32_t c[kRegU];
+  bool have_s = false;
+  auto load_s = [&]() {
+    // 11 loads in flight per thread and chunk; a chunk's offsets die at issue
+#pragma unroll
+    for (int u0 = 0; u0 < kRegU; u0 += 11) {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int u = u0; u < u0 + 11; ++u) s[u] = sp[slot(u, t)];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) s[u] = u < cnt ? s[u] : 0u;
+  };
+  auto all = [](int) { return true; };
+  auto one = [](uint32_t) -> uint64_t { return 1; };
+  __syncthreads();   // block-table slice visible
+
+  if (LRFU) {
+    load_s();
+    have_s = true;
+    uint64_t msum = 0;
+    uint32_t band = ~0u, bor = 0u;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      msum += fixed_mass(s[u]);                 // 0 for rows without an entry
+      band &= u < cnt ? s[u] : ~0u;
+      bor |= s[u];
+    }
+    const uint64_t M = block_sum_u64(msum, sh.scratch);
+    block_and_or(band, bor, (uint32_t *)sh.scratch);
+    const uint64_t T = (M / a.den) * a.num + ((M % a.den) * a.num + a.den - 1) / a.den;
+    const bool none = T == 0;
+    uint32_t vstar = 0xFFFFFFFFu;
+    uint64_t k_needed = 0, ties = 0;
+    if (!none) {
+      const Sel r = reg_select<false>(s, cnt, all, fixed_mass, T, band, bor, sh);
+      vstar = r.key;
+      const uint64_t mstar = fixed_mass(vstar);
+      k_needed = (T - r.above + mstar - 1) / mstar;
+      ties = r.at / mstar;
+    }
+    // hit bits (bit u)
+    uint64_t hbits = 0;
+    if (!none && k_needed < ties) {
+      // ties at the threshold exceed the hits still needed: lowest slots first
+      uint64_t carry = 0;
+#pragma unroll
+      for (int u = 0; u < kRegU; ++u) {
+        if (u < rounds) {
+          const bool valid = u < cnt;
+          const bool tie = valid && s[u] == vstar;
+          uint32_t tot;
+          const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
+          const bool h = valid && (s[u] > vstar || (tie && carry + rk < k_needed));
+          carry += tot;
+          hbits |= (uint64_t)h << u;
+        }
+      }
+    } else if (!none) {
+#pragma unroll
+      for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(u < cnt && s[u] >= vstar) << u;
+    }
+    // LRFU update of the paged CRF, 11 rows at a time
+    const float d = a.decay[i];
+    const int32_t np = a.n_prev[i];
+    constexpr int kChunk = 11;
+    const int np_rel = np - tid;               // row u has a prior iff u * 1024 < np_rel
+#pragma unroll
+    for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
+      const int t = opaque(tid);
+      uint32_t off[kChunk];
+      float prior[kChunk];
+#pragma unroll
+      for (int v = 0; v < kChunk; ++v) {
+        off[v] = crf_off(u0 + v, t);
+        prior[v] = crf_base[off[v]];
+      }
+#pragma unroll
+      for (int v = 0; v < kChunk; ++v) {
+        const int u = u0 + v;
+        const bool h = (hbits >> u) & 1;
+        const float p = u * kStreamThreads < np_rel ? prior[v] : 0.f;
+        const float nv = __builtin_fmaf(d, p, h ? 1.f : 0.f);
+        c[u] = u < cnt ? __float_as_uint(nv) : 0u;
+        KVS_FOR_VALID(u, crf_base[off[v]] = nv;)
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (a.hit) {
+      uint8_t *hp = a.hit + (int64_t)lg * a.b.E + e0;
+      const int t = opaque(tid);
+#pragma unroll
+      for (int u = 0; u < kRegU; ++u) {
+        KVS_FOR_VALID(u, hp[u * kStreamThreads + t] = (uint8_t)((hbits >> u) & 1);)
+      }
+    }
+    if (!SELECT) return;
+    if (K == 0 || K == n) {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int u = 0; u < kRegU; ++u) {
+        KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = K == n ? 1 : 0;)
+      }
+      return;
+    }
+  } else {
+    constexpr int kChunk = 11;
+#pragma unroll
+    for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int v = 0; v < kChunk; ++v) c[u0 + v] = __float_as_uint(crf_base[crf_off(u0 + v, t)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) c[u] = u < cnt ? c[u] : 0u;
+  }
+
+  // ---- top-K keep set ----
+  uint32_t band = ~0u, bor = 0u;
+#pragma unroll
+  for (int u = 0; u < kRegU; ++u) {
+    band &= u < cnt ? c[u] : ~0u;
+    bor |= c[u];
+  }
+  block_and_or(band, bor, (uint32_t *)sh.scratch);
+  const Sel r1 = reg_select<true>(c, cnt, all, one, (uint64_t)K, band, bor, sh);
+  const uint32_t cstar = r1.key;
+  const uint64_t need = K - r1.above;          // entries to keep among CRF == c*
+  const bool lvl2 = need < r1.at;
+  uint32_t sstar = 0;
+  uint64_t need2 = 0, at2 = 0;
+  if (lvl2) {
+    if (!have_s) load_s();
+    uint32_t sa = ~0u, so = 0u;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      const bool t = u < cnt && c[u] == cstar;
+      sa &= t ? s[u] : ~0u;
+      so |= t ? s[u] : 0u;
+    }
+    block_and_or(sa, so, (uint32_t *)sh.scratch);
+    auto in_tie = [&](int u) { return c[u] == cstar; };
+    const Sel r2 = reg_select<true>(s, cnt, in_tie, one, need, sa, so, sh);
+    sstar = r2.key;
+    need2 = need - r2.above;
+    at2 = r2.at;
+  }
+  if (!(lvl2 && need2 < at2)) {
+    const int t = opaque(tid);
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      const bool k = lvl2 ? (c[u] > cstar || (c[u] == cstar && s[u] >= sstar)) : c[u] >= cstar;
+      KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = k ? 1 : 0;)
+    }
+  } else {
+    uint64_t carry = 0;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      if (u < rounds) {
+        const bool valid = u < cnt;
+        const bool tie = valid && c[u] == cstar && s[u] == sstar;
+        uint32_t tot;
+        const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
+        const bool k = c[u] > cstar || (c[u] == cstar && (s[u] > sstar || (tie && carry + rk < need2)));
+        carry += tot;
+        if (valid) kp[u * kStreamThreads + tid] = k ? 1 : 0;
+      }
+    }
+  }
+}
+
+#undef KVS_FOR_VALID
+
+}  // namespace
+
+bool stream_reg_fits(int32_t max_len, int64_t num_pages, int32_t Hkv) {
+  return max_len <= kRegMaxLen && num_pages * Hkv * kPage < (int64_t(1) << 31);
+}
+
+hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *scores, bool lrfu, bool select,
+                             uint32_t num, uint32_t den, const float *decay, const int32_t *n_prev,
+                             uint8_t *hit, const int32_t *budget, uint8_t *keep, hipStream_t st) {
+  StreamArgs a{};
+  a.scores = scores;
+  a.crf = c.crf;
+  a.hit = hit;
+  a.decay = decay;
+  a.n_prev = n_prev;
+  a.budget = budget;
+  a.keep = keep;
+  a.b = b;
+  a.num = num;
+  a.den = den;
+  dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
+  if (lrfu && select) stream_reg_kernel<true, true><<<grid, kStreamThreads, 0, st>>>(a);
+  else if (lrfu) stream_reg_kernel<true, false><<<grid, kStreamThreads, 0, st>>>(a);
+  else stream_reg_kernel<false, true><<<grid, kStreamThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

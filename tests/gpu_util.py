@@ -30,8 +30,9 @@ def upload(lay, inp):
     return cache, seqs, obs
 
 
-def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None):
-    """Run the round stage by stage on the GPU; return every intermediate on the host."""
+def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None, fused=False):
+    """Run the round stage by stage on the GPU; return every intermediate on the host.
+    fused: run the cut, LRFU update and keep set through kvs_lrfu_select."""
     import torch
     import kv_cache_eviction_lse_amd as K
     dev = _dev()
@@ -45,12 +46,19 @@ def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None):
     torch.cuda.synchronize()
     out["s"] = bufs.scores.cpu().numpy()
     out["crf0"] = cache.crf.cpu().numpy()
-    K.kvs_lrfu_update(cache, seqs, bufs.scores, mass[0], mass[1], decay, n_prev, bufs.hit)
-    torch.cuda.synchronize()
-    out["hit"] = bufs.hit.cpu().numpy().astype(bool)
-    out["crf1"] = cache.crf.cpu().numpy()
-    K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
-    torch.cuda.synchronize()
+    if fused:
+        K.kvs_lrfu_select(cache, seqs, bufs.scores, mass[0], mass[1], decay, n_prev, bufs.budget,
+                          bufs.budget_h, bufs.keep, hit=bufs.hit)
+        torch.cuda.synchronize()
+        out["hit"] = bufs.hit.cpu().numpy().astype(bool)
+        out["crf1"] = cache.crf.cpu().numpy()
+    else:
+        K.kvs_lrfu_update(cache, seqs, bufs.scores, mass[0], mass[1], decay, n_prev, bufs.hit)
+        torch.cuda.synchronize()
+        out["hit"] = bufs.hit.cpu().numpy().astype(bool)
+        out["crf1"] = cache.crf.cpu().numpy()
+        K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
+        torch.cuda.synchronize()
     out["keep"] = bufs.keep.cpu().numpy().astype(bool)
     plan = K.kvs_plan(seqs, cache.c.num_layers, cache.c.num_kv_heads, bufs.keep, bufs.budget,
                       bufs.budget_h, bufs.pairs, bufs.pair_count)
