@@ -17,7 +17,6 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
-import hashlib
 import json
 import os
 import platform
@@ -57,14 +56,10 @@ def host_samples(wname, streams, workers):
         return list(ex.map(_stream_job, jobs))
 
 
-def score_source_sha():
-    p = os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc", "score.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-
-
-def load_traffic(entries_per_launch):
+def load_traffic():
     """HBM bytes per scorer launch from the committed rocprofv3 counter summary, if it
     was taken on the current scorer source; else None."""
+    from kv_cache_eviction_lse_amd.profiling import score_source_sha
     p = os.path.join(ROOT, "profiles", "score_mfma_llama3_8b_32k_traffic.json")
     if not os.path.exists(p):
         return None
@@ -83,6 +78,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-streams", type=int, default=8, help="streams in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle CPU time")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MiB",
+                    help="after timing, copy MiB of device memory 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the eviction path "
@@ -171,7 +168,7 @@ def main():
     gbps = req_bytes / (ms_per_step / 1000.0) / 1e9
     score_bytes = entries * (2 * D + 4) + rows * (2 * D + 4)
     score_gbps = score_bytes / (score_ms / 1000.0) / 1e9
-    traffic = load_traffic(entries)
+    traffic = load_traffic()
 
     out = {
         "metric": METRIC,
@@ -246,6 +243,14 @@ def main():
         }
         out["parity"] = {"streams": len(sample), "max_rel_score_err": worst,
                          "keep_pinned": pinned_total, "keep_pinned_mismatch": bad}
+    if args.calibration_copy:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     out["setup_s"] = {"host_samples": round(t_host, 2), "device_fill": round(t_fill, 2)}
     print(json.dumps(out), flush=True)
 

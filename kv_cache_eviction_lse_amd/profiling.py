@@ -1,0 +1,142 @@
+"""Text summaries of rocprofv3 output for the eviction round (kernel statistics and the
+scorer's HBM traffic), as kept under profiles/.
+
+Kernel statistics (from `rocprofv3 --kernel-trace --stats --output-format csv`):
+
+    python -m kv_cache_eviction_lse_amd.profiling stats --dir DIR --command "..." > summary.md
+
+HBM traffic of the scorer per launch, from two counter runs of bench.py with a plain
+copy of known size (`--calibration-copy MiB`) in the same process: FETCH_SIZE and
+WRITE_SIZE of each kernel are scaled by bytes / counter of the copy kernel.
+
+    python -m kv_cache_eviction_lse_amd.profiling traffic --fetch DIR1 --write DIR2 \
+        --copy-mib 2048 --json out.json --command "..." > summary.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SCORER = "score_mfma_kernel"
+
+
+def _rows(directory: str, suffix: str) -> list[dict]:
+    out = []
+    for p in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(p, newline="") as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def _short(name: str) -> str:
+    name = re.sub(r"kvs::\(anonymous namespace\)::", "", name)
+    name = name.replace("void ", "")
+    return name.split("(")[0][:60]
+
+
+def score_source_sha() -> str:
+    p = os.path.join(HERE, "csrc", "score.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def stats(args) -> None:
+    rows = _rows(args.dir, "kernel_stats.csv")
+    if not rows:
+        sys.exit(f"no kernel_stats.csv under {args.dir}")
+    print("# Kernel time per launch, one eviction round = one call of each kvs kernel\n")
+    print(f"Command: `{args.command}`\n")
+    print("| kernel | calls | average us | min us | max us | share of all GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        nm = r["Name"]
+        if "kvs::" not in nm and not args.all:
+            continue
+        print(f"| {_short(nm)} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} % |")
+
+
+def _counter(directory: str, counter: str) -> dict[str, list[float]]:
+    per = {}
+    for r in _rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        sys.exit(f"no {counter} rows under {directory}")
+    return per
+
+
+def traffic(args) -> None:
+    copy_bytes = args.copy_mib * 2**20
+    out = {"score_source_sha": score_source_sha(), "copy_bytes": copy_bytes}
+    factors = {}
+    for counter, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+        per = _counter(d, counter)
+        # the calibration copy: the copy dispatches with the largest counter value
+        copies = [v for k, vs in per.items() if "copy" in k.lower() for v in vs]
+        if not copies:
+            sys.exit(f"no copy kernel in the {counter} run")
+        c_kib = max(copies)
+        factor = copy_bytes / (c_kib * 1024.0)
+        sc = [v for k, vs in per.items() if SCORER in k for v in vs]
+        if not sc:
+            sys.exit(f"no {SCORER} dispatch in the {counter} run")
+        s_kib = sum(sc) / len(sc)
+        key = counter.lower()
+        out[f"{key}_kib_per_dispatch"] = s_kib
+        out[f"copy_{key}_kib"] = c_kib
+        out[f"{key}_factor"] = factor
+        out[f"{key}_bytes_per_launch"] = s_kib * 1024.0 * factor
+        out[f"{key}_dispatches"] = len(sc)
+        factors[counter] = factor
+    out["hbm_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + out["write_size_bytes_per_launch"]
+    if args.algorithmic_bytes:
+        out["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
+    out["commands"] = args.command
+    with open(args.json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"# {SCORER}: HBM traffic per launch (llama3_8b_32k)\n")
+    for c in args.command:
+        print(f"Command: `{c}`\n")
+    print("| counter | scorer KiB/dispatch | copy KiB ({} MiB copy) | bytes per counted byte | scorer bytes/launch |".format(args.copy_mib))
+    print("|---|---|---|---|---|")
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        k = counter.lower()
+        print(f"| {counter} | {out[f'{k}_kib_per_dispatch']:.0f} | {out[f'copy_{k}_kib']:.0f} | "
+              f"{out[f'{k}_factor']:.4f} | {out[f'{k}_bytes_per_launch']:.4e} |")
+    print(f"\nHBM traffic per launch: {out['hbm_bytes_per_launch']:.4e} bytes", end="")
+    if args.algorithmic_bytes:
+        print(f" ({out['hbm_bytes_per_launch'] / args.algorithmic_bytes:.3f} x the algorithmic "
+              f"{args.algorithmic_bytes:.4e})")
+    else:
+        print()
+    print(f"\nscore.hip sha256[:16] = {out['score_source_sha']}")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--dir", required=True)
+    s.add_argument("--command", default="")
+    s.add_argument("--all", action="store_true")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    t.add_argument("--command", action="append", default=[])
+    args = ap.parse_args()
+    stats(args) if args.cmd == "stats" else traffic(args)
+
+
+if __name__ == "__main__":
+    main()
