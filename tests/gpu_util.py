@@ -166,3 +166,146 @@ def pinned_keep_check(s_ora, crf_ora, keep_ora, hit_ora, s_gpu, crf_gpu, keep_gp
     by_s = same_crf & (np.abs(s64 - sb) > tol * sb)
     pinned = unamb & (by_crf | by_s)
     return int(pinned.sum()), int((keep_gpu[pinned] != keep_ora[pinned]).sum())
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: the whole cache on the GPU, sampled streams checked
+# ---------------------------------------------------------------------------
+
+
+def _stream_pages(lay, i):
+    n, st = int(lay.length[i]), int(lay.start[i])
+    npg = (st + n + 15) // 16
+    return lay.block_table[i][:npg].astype(np.int64)
+
+
+def run_config_sampled(w, lay, q_host, sample, scale=None, fused=False):
+    """One round of workload w over its whole cache on the GPU (device-drawn data, the
+    sampled streams overwritten with host-generated bytes), stage by stage; returns the
+    GPU's intermediates for the sampled streams only."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import device as DV
+    dev = _dev()
+    d = DV.fill(w, lay, q_host, dev, exact_streams=sample)
+    torch.cuda.synchronize()
+    L, Hkv = w.num_layers, w.num_kv_heads
+    cache = K.PagedCache(d.k, d.v, d.crf)
+    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
+    obs = K.ObserverSet(d.q, d.lse, lay.obs_off, device=dev)
+    budget_h = np.full(w.num_seqs, w.budget, np.int32)
+    bufs = K.RoundBuffers(cache, seqs, obs, budget_h, keep_hits=True)
+    decay_h = np.array([K.kvs_lrfu_decay(0.5, int(x)) for x in lay.dt], np.float32)
+    decay = torch.from_numpy(decay_h).to(dev)
+    n_prev = torch.from_numpy(lay.n_prev.astype(np.int32)).to(dev)
+    scale = w.scale if scale is None else scale
+    pages = {s: torch.from_numpy(_stream_pages(lay, s[0])).to(dev) for s in sample}
+    rec = {s: {} for s in sample}
+
+    def grab(tag, fn):
+        torch.cuda.synchronize()
+        for s in sample:
+            rec[s][tag] = fn(s)
+
+    def ent(buf, s):
+        i, l, g = s
+        return buf[l, g, int(lay.entry_off[i]):int(lay.entry_off[i + 1])].cpu().numpy()
+
+    def crf_pages(s):
+        i, l, g = s
+        return d.crf[l][pages[s], g].cpu().numpy()          # [npg][16]
+
+    def kv_pages(s):
+        i, l, g = s
+        return (d.k[l][pages[s], g].cpu().numpy().view(np.uint16),
+                d.v[l][pages[s], g].cpu().numpy().view(np.uint16))
+
+    grab("crf0", crf_pages)
+    K.kvs_score(cache, seqs, obs, scale, bufs.scores, bufs.workspace)
+    grab("s", lambda s: ent(bufs.scores, s))
+    if fused:
+        K.kvs_lrfu_select(cache, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h,
+                          bufs.keep, hit=bufs.hit)
+    else:
+        K.kvs_lrfu_update(cache, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.hit)
+    grab("hit", lambda s: ent(bufs.hit, s).astype(bool))
+    grab("crf1", crf_pages)
+    if not fused:
+        K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
+    grab("keep", lambda s: ent(bufs.keep, s).astype(bool))
+    plan = K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    grab("pairs", lambda s: bufs.pairs[s[1], s[2], s[0], :max(int(bufs.pair_count[s[1], s[2], s[0]]), 0)]
+         .cpu().numpy())
+    grab("kv0", kv_pages)
+    K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    grab("kv1", kv_pages)
+    grab("crf2", crf_pages)
+    torch.cuda.synchronize()
+    out = {"rec": rec, "plan": plan, "decay": decay_h}
+    del bufs, cache, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def check_config_sampled(w, lay, q_host, sample, out, score_rtol=1e-3):
+    """Sampled-stream parity of a full-size round: scores against the oracle on the same
+    bytes; cut, LRFU, keep set, pairs and moved bytes exact on the GPU's own inputs; the
+    end-to-end keep set exact wherever the oracle's margins pin it.  Returns
+    (worst relative score error, pinned entries, pinned mismatches)."""
+    from workloads.device import host_stream_inputs
+    G = w.group
+    worst, pinned_all, bad_all = 0.0, 0, 0
+    for s in sample:
+        i, l, g = s
+        r = out["rec"][s]
+        n, st = int(lay.length[i]), int(lay.start[i])
+        B = int(w.budget)
+        mb = host_stream_inputs(w, lay, q_host, [s])
+        k, v, c, qq, lse, bt, stt, ln, oo = mb
+        res = O.eviction_round(k.copy(), v.copy(), c.copy(), qq, lse, oo, bt, stt, ln, G, w.scale, 0.5,
+                               np.array([lay.dt[i]]), np.array([lay.n_prev[i]]), np.array([B]))
+        s_ora = res["s"][(0, 0, 0)]
+        s_gpu = r["s"]
+        nz = s_ora > 0
+        err = np.abs(s_gpu.astype(np.float64) - s_ora) / np.maximum(np.abs(s_ora.astype(np.float64)), 1e-30)
+        if nz.any():
+            worst = max(worst, float(err[nz].max()))
+            assert err[nz].max() <= score_rtol, (s, float(err[nz].max()))
+        # components on the GPU's own inputs
+        pos = st + np.arange(n)
+        pi, row = pos // 16, pos % 16
+        hit = O.mass_cut(s_gpu)
+        np.testing.assert_array_equal(r["hit"], hit, err_msg=f"hit {s}")
+        prior = r["crf0"][pi, row]
+        crf_new = O.lrfu_update(prior, hit, np.float32(out["decay"][i]), int(lay.n_prev[i]))
+        got = r["crf1"][pi, row]
+        np.testing.assert_array_equal(got.view(np.uint32), crf_new.view(np.uint32), err_msg=f"crf {s}")
+        keep = O.select_top_b(got, s_gpu, B)
+        np.testing.assert_array_equal(r["keep"], keep, err_msg=f"keep {s}")
+        src, dst = O.plan_stream(r["keep"])
+        assert len(r["pairs"]) == len(src), (s, len(r["pairs"]), len(src))
+        if len(src):
+            np.testing.assert_array_equal(r["pairs"][:, 0], src)
+            np.testing.assert_array_equal(r["pairs"][:, 1], dst)
+        # moved bytes: the stream's pages after = before with the pairs applied
+        k0, v0 = r["kv0"]
+        c0 = r["crf1"].copy()
+        ek, ev, ec = k0.copy(), v0.copy(), c0.copy()
+        sp, sr = (st + src) // 16, (st + src) % 16
+        dp, dr = (st + dst) // 16, (st + dst) % 16
+        ek[dp, dr] = k0[sp, sr]
+        ev[dp, dr] = v0[sp, sr]
+        ec[dp, dr] = c0[sp, sr]
+        np.testing.assert_array_equal(r["kv1"][0], ek, err_msg=f"K bytes {s}")
+        np.testing.assert_array_equal(r["kv1"][1], ev, err_msg=f"V bytes {s}")
+        np.testing.assert_array_equal(r["crf2"].view(np.uint32), ec.view(np.uint32), err_msg=f"CRF {s}")
+        # host plan outputs
+        K_ = min(B, n)
+        sh, ns, nl, fr = O.plan_sequence(n, K_, st, lay.block_table[i])
+        assert (out["plan"].shift[i], out["plan"].new_start[i], out["plan"].new_len[i]) == (sh, ns, nl)
+        # end to end against the oracle's own round
+        pn, nb = pinned_keep_check(s_ora, res["crf"][(0, 0, 0)], res["keep"][(0, 0, 0)], res["hit"][(0, 0, 0)],
+                                   s_gpu, got, r["keep"])
+        pinned_all += pn
+        bad_all += nb
+    return worst, pinned_all, bad_all

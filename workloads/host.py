@@ -179,25 +179,62 @@ def kmeans_beacons(w: Workload, l: int, h: int) -> np.ndarray:
     return cent
 
 
-def observers(w: Workload, lay: Layout, rnd: int = 0, heads=None) -> np.ndarray:
+def observers(w: Workload, lay: Layout, rnd: int = 0, heads=None, only_heads: bool = False) -> np.ndarray:
     """Observer queries, bf16 bits [L][Hq][O_tot][D].
 
     heads: optional set of (l, h) for which k-means beacons are computed on the
     host; beacon rows of other heads are left as plain N(0,1) draws (callers that
     need them fill them in elsewhere).
+    only_heads: the listed heads get the counter-based draws; every other head gets
+    N(0,1) from numpy's seeded PCG64 (much faster, for full-size workloads whose
+    other heads are never compared with the oracle).
     """
     L, Hq, D = w.num_layers, w.num_q_heads, w.head_dim
     O_tot = int(lay.obs_off[-1])
     q = np.empty((L, Hq, O_tot, D), np.uint16)
-    for i in range(w.num_seqs):
-        o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+    if only_heads:
+        rng = np.random.default_rng([w.key & 0xFFFFFFFF, w.key >> 32, rnd])
         for l in range(L):
-            for h in range(Hq):
+            q[l] = philox.f32_to_bf16_bits(rng.standard_normal((Hq, O_tot, D), dtype=np.float32))
+        for (l, h) in sorted(heads or ()):
+            for i in range(w.num_seqs):
+                o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+                if o1 == o0:
+                    continue
                 z = observer_normals(w, rnd, i, l, h, np.arange(o1 - o0))
-                if w.beacons and (heads is None or (l, h) in heads):
+                if w.beacons:
                     z[:w.beacons] = kmeans_beacons(w, l, h)
                 q[l, h, o0:o1] = philox.f64_to_bf16_bits(z)
+        return q
+    for i in range(w.num_seqs):
+        o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+        if o1 == o0:
+            continue
+        for l in range(L):
+            # all heads of (sequence, layer) at once; the same draws as observer_normals
+            z = _observer_normals_heads(w, rnd, i, l, np.arange(o1 - o0))
+            if w.beacons:
+                for h in range(Hq):
+                    if heads is None or (l, h) in heads:
+                        z[h, :w.beacons] = kmeans_beacons(w, l, h)
+            q[l, :, o0:o1] = philox.f64_to_bf16_bits(z)
     return q
+
+
+def _observer_normals_heads(w: Workload, rnd: int, i: int, l: int, o: np.ndarray) -> np.ndarray:
+    """observer_normals for every query head of (round, sequence, layer): fp64 [Hq][len(o)][D]."""
+    D = w.head_dim
+    h = np.arange(w.num_q_heads, dtype=np.int64)
+    base = (((np.int64(rnd) * w.num_seqs + i) * w.num_layers + l) * w.num_q_heads + h) * OBS_MAX
+    tok = (base[:, None] + np.asarray(o, np.int64)[None, :]).reshape(-1).astype(np.uint64)
+    ctr = (tok[:, None] * np.uint64(D // 4) + np.arange(D // 4, dtype=np.uint64)[None, :]).reshape(-1)
+    w0, w1, w2, w3 = philox.words(w.key, TAG_Q, ctr)
+    u0, u1, u2, u3 = (philox.uniform01(x) for x in (w0, w1, w2, w3))
+    r0 = np.sqrt(-2.0 * np.log(u0))
+    r1 = np.sqrt(-2.0 * np.log(u2))
+    z = np.stack([r0 * np.cos(2.0 * np.pi * u1), r0 * np.sin(2.0 * np.pi * u1),
+                  r1 * np.cos(2.0 * np.pi * u3), r1 * np.sin(2.0 * np.pi * u3)], axis=1)
+    return z.reshape(w.num_q_heads, len(o), D)
 
 
 def stream_observer_rows(w: Workload, lay: Layout, q: np.ndarray, i: int, l: int, g: int) -> np.ndarray:
