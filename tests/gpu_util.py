@@ -257,55 +257,65 @@ def check_config_sampled(w, lay, q_host, sample, out, score_rtol=1e-3):
     worst, pinned_all, bad_all = 0.0, 0, 0
     for s in sample:
         i, l, g = s
-        r = out["rec"][s]
         n, st = int(lay.length[i]), int(lay.start[i])
         B = int(w.budget)
-        mb = host_stream_inputs(w, lay, q_host, [s])
-        k, v, c, qq, lse, bt, stt, ln, oo = mb
+        k, v, c, qq, lse, bt, stt, ln, oo = host_stream_inputs(w, lay, q_host, [s])
         res = O.eviction_round(k.copy(), v.copy(), c.copy(), qq, lse, oo, bt, stt, ln, G, w.scale, 0.5,
                                np.array([lay.dt[i]]), np.array([lay.n_prev[i]]), np.array([B]))
-        s_ora = res["s"][(0, 0, 0)]
-        s_gpu = r["s"]
-        nz = s_ora > 0
-        err = np.abs(s_gpu.astype(np.float64) - s_ora) / np.maximum(np.abs(s_ora.astype(np.float64)), 1e-30)
-        if nz.any():
-            worst = max(worst, float(err[nz].max()))
-            assert err[nz].max() <= score_rtol, (s, float(err[nz].max()))
-        # components on the GPU's own inputs
-        pos = st + np.arange(n)
-        pi, row = pos // 16, pos % 16
-        hit = O.mass_cut(s_gpu)
-        np.testing.assert_array_equal(r["hit"], hit, err_msg=f"hit {s}")
-        prior = r["crf0"][pi, row]
-        crf_new = O.lrfu_update(prior, hit, np.float32(out["decay"][i]), int(lay.n_prev[i]))
-        got = r["crf1"][pi, row]
-        np.testing.assert_array_equal(got.view(np.uint32), crf_new.view(np.uint32), err_msg=f"crf {s}")
-        keep = O.select_top_b(got, s_gpu, B)
-        np.testing.assert_array_equal(r["keep"], keep, err_msg=f"keep {s}")
-        src, dst = O.plan_stream(r["keep"])
-        assert len(r["pairs"]) == len(src), (s, len(r["pairs"]), len(src))
-        if len(src):
-            np.testing.assert_array_equal(r["pairs"][:, 0], src)
-            np.testing.assert_array_equal(r["pairs"][:, 1], dst)
-        # moved bytes: the stream's pages after = before with the pairs applied
-        k0, v0 = r["kv0"]
-        c0 = r["crf1"].copy()
-        ek, ev, ec = k0.copy(), v0.copy(), c0.copy()
-        sp, sr = (st + src) // 16, (st + src) % 16
-        dp, dr = (st + dst) // 16, (st + dst) % 16
-        ek[dp, dr] = k0[sp, sr]
-        ev[dp, dr] = v0[sp, sr]
-        ec[dp, dr] = c0[sp, sr]
-        np.testing.assert_array_equal(r["kv1"][0], ek, err_msg=f"K bytes {s}")
-        np.testing.assert_array_equal(r["kv1"][1], ev, err_msg=f"V bytes {s}")
-        np.testing.assert_array_equal(r["crf2"].view(np.uint32), ec.view(np.uint32), err_msg=f"CRF {s}")
-        # host plan outputs
-        K_ = min(B, n)
-        sh, ns, nl, fr = O.plan_sequence(n, K_, st, lay.block_table[i])
-        assert (out["plan"].shift[i], out["plan"].new_start[i], out["plan"].new_len[i]) == (sh, ns, nl)
-        # end to end against the oracle's own round
-        pn, nb = pinned_keep_check(s_ora, res["crf"][(0, 0, 0)], res["keep"][(0, 0, 0)], res["hit"][(0, 0, 0)],
-                                   s_gpu, got, r["keep"])
+        plan3 = (out["plan"].shift[i], out["plan"].new_start[i], out["plan"].new_len[i])
+        w_, pn, nb = check_stream_record(res, out["rec"][s], n, st, B, out["decay"][i], int(lay.n_prev[i]),
+                                         plan3, lay.block_table[i], score_rtol, s)
+        worst = max(worst, w_)
         pinned_all += pn
         bad_all += nb
     return worst, pinned_all, bad_all
+
+
+def check_stream_record(res, r, n, st, B, decay, n_prev, plan3, bt_row, score_rtol=1e-3, tag=None):
+    """One stream's GPU record r (scores, hit, keep, pairs; crf0/crf1/crf2 and kv0/kv1 as
+    the stream's pages) against the oracle round res on the same input bytes: scores
+    within score_rtol, every later stage exact on the GPU's own inputs, the keep set
+    exact where pinned.  Returns (worst relative score error, pinned, mismatches)."""
+    s_ora = res["s"][(0, 0, 0)]
+    s_gpu = r["s"]
+    worst = 0.0
+    nz = s_ora > 0
+    err = np.abs(s_gpu.astype(np.float64) - s_ora) / np.maximum(np.abs(s_ora.astype(np.float64)), 1e-30)
+    if nz.any():
+        worst = float(err[nz].max())
+        assert worst <= score_rtol, (tag, worst)
+    # components on the GPU's own inputs
+    pos = st + np.arange(n)
+    pi, row = pos // 16, pos % 16
+    hit = O.mass_cut(s_gpu)
+    np.testing.assert_array_equal(r["hit"], hit, err_msg=f"hit {tag}")
+    prior = r["crf0"][pi, row]
+    crf_new = O.lrfu_update(prior, hit, np.float32(decay), int(n_prev))
+    got = r["crf1"][pi, row]
+    np.testing.assert_array_equal(got.view(np.uint32), crf_new.view(np.uint32), err_msg=f"crf {tag}")
+    keep = O.select_top_b(got, s_gpu, B)
+    np.testing.assert_array_equal(r["keep"], keep, err_msg=f"keep {tag}")
+    src, dst = O.plan_stream(r["keep"])
+    assert len(r["pairs"]) == len(src), (tag, len(r["pairs"]), len(src))
+    if len(src):
+        np.testing.assert_array_equal(r["pairs"][:, 0], src)
+        np.testing.assert_array_equal(r["pairs"][:, 1], dst)
+    # moved bytes: the stream's pages after = before with the pairs applied
+    k0, v0 = r["kv0"]
+    c0 = r["crf1"].copy()
+    ek, ev, ec = k0.copy(), v0.copy(), c0.copy()
+    sp, sr = (st + src) // 16, (st + src) % 16
+    dp, dr = (st + dst) // 16, (st + dst) % 16
+    ek[dp, dr] = k0[sp, sr]
+    ev[dp, dr] = v0[sp, sr]
+    ec[dp, dr] = c0[sp, sr]
+    np.testing.assert_array_equal(r["kv1"][0], ek, err_msg=f"K bytes {tag}")
+    np.testing.assert_array_equal(r["kv1"][1], ev, err_msg=f"V bytes {tag}")
+    np.testing.assert_array_equal(r["crf2"].view(np.uint32), ec.view(np.uint32), err_msg=f"CRF {tag}")
+    # host plan outputs
+    sh, ns, nl, _ = O.plan_sequence(n, min(B, n), st, bt_row)
+    assert tuple(int(x) for x in plan3) == (sh, ns, nl), (tag, plan3, (sh, ns, nl))
+    # end to end against the oracle's own round
+    pn, nb = pinned_keep_check(s_ora, res["crf"][(0, 0, 0)], res["keep"][(0, 0, 0)], res["hit"][(0, 0, 0)],
+                               s_gpu, got, r["keep"])
+    return worst, pn, nb

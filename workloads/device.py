@@ -159,3 +159,18 @@ def host_stream_inputs(w: Workload, lay: H.Layout, q_host: np.ndarray, streams):
             q[0, hh, obs_off[s]:obs_off[s + 1]] = q_host[l, g * G + hh, o0:o1]
             lse[0, hh, obs_off[s]:obs_off[s + 1]] = lr[hh * O:(hh + 1) * O]
     return k_pool, v_pool, crf_pool, q, lse, bt, start, length, obs_off
+
+
+def live_lse(keys_f32, q_rows_f32, scale, chunk=256):
+    """Natural-log LSE of observer rows over live keys, fp32 logits as a paged decode
+    kernel would produce them.  keys_f32: [n][Hkv][D]; q_rows_f32: [Hkv][R][D] with the
+    rows of KV head g head-major.  Returns [Hkv][R] float32 (torch)."""
+    import torch
+    kt = keys_f32.permute(1, 2, 0).contiguous()                      # [Hkv][D][n]
+    R = q_rows_f32.shape[1]
+    out = torch.empty((q_rows_f32.shape[0], R), dtype=torch.float32, device=keys_f32.device)
+    for r0 in range(0, R, chunk):
+        r1 = min(R, r0 + chunk)
+        logits = torch.bmm(q_rows_f32[:, r0:r1, :].contiguous(), kt) * scale
+        out[:, r0:r1] = torch.logsumexp(logits, dim=2)
+    return out
