@@ -179,7 +179,8 @@ def kmeans_beacons(w: Workload, l: int, h: int) -> np.ndarray:
     return cent
 
 
-def observers(w: Workload, lay: Layout, rnd: int = 0, heads=None, only_heads: bool = False) -> np.ndarray:
+def observers(w: Workload, lay: Layout, rnd: int = 0, heads=None, only_heads: bool = False,
+              rest_zero: bool = False) -> np.ndarray:
     """Observer queries, bf16 bits [L][Hq][O_tot][D].
 
     heads: optional set of (l, h) for which k-means beacons are computed on the
@@ -187,15 +188,18 @@ def observers(w: Workload, lay: Layout, rnd: int = 0, heads=None, only_heads: bo
     need them fill them in elsewhere).
     only_heads: the listed heads get the counter-based draws; every other head gets
     N(0,1) from numpy's seeded PCG64 (much faster, for full-size workloads whose
-    other heads are never compared with the oracle).
+    other heads are never compared with the oracle), or zeros with rest_zero.
     """
     L, Hq, D = w.num_layers, w.num_q_heads, w.head_dim
     O_tot = int(lay.obs_off[-1])
     q = np.empty((L, Hq, O_tot, D), np.uint16)
     if only_heads:
-        rng = np.random.default_rng([w.key & 0xFFFFFFFF, w.key >> 32, rnd])
-        for l in range(L):
-            q[l] = philox.f32_to_bf16_bits(rng.standard_normal((Hq, O_tot, D), dtype=np.float32))
+        if rest_zero:
+            q[:] = 0
+        else:
+            rng = np.random.default_rng([w.key & 0xFFFFFFFF, w.key >> 32, rnd])
+            for l in range(L):
+                q[l] = philox.f32_to_bf16_bits(rng.standard_normal((Hq, O_tot, D), dtype=np.float32))
         for (l, h) in sorted(heads or ()):
             for i in range(w.num_seqs):
                 o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
