@@ -5,7 +5,8 @@ A step is one full round over the Llama-3-8B-shaped cache (32 layers x 8 KV head
 32 query heads, 32,768 live entries per stream in 16-token pages scattered over a
 4,096-page pool, 64 observers per sequence, budget 512):
 
-    kvs_score -> kvs_lrfu_update -> kvs_select -> kvs_plan -> kvs_compact
+    kvs_score -> kvs_lrfu_select -> kvs_plan_compact
+    (with --separate: kvs_score -> kvs_lrfu_update -> kvs_select -> kvs_plan -> kvs_compact)
 
 all enqueued on one stream with inputs resident in HBM.  Every step re-runs the
 round on the same 32K-entry layout (the evicted slots stand for freshly appended
@@ -84,6 +85,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-streams", type=int, default=8, help="streams in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle CPU time")
+    ap.add_argument("--separate", action="store_true",
+                    help="run cut/LRFU, keep set, plan and move as four calls instead of two fused ones")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MiB",
                     help="after timing, copy MiB of device memory 3 times (counter calibration)")
     args = ap.parse_args()
@@ -141,7 +144,7 @@ def main():
 
     # first round: keep the outputs of the sampled streams for a parity spot check
     if samples:
-        K.eviction_round(cache, seqs, obs, bufs, decay, n_prev, scale)
+        K.eviction_round(cache, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate)
         torch.cuda.synchronize()
         s_gpu = bufs.scores.cpu().numpy()
         keep_gpu = bufs.keep.cpu().numpy().astype(bool)
@@ -149,7 +152,7 @@ def main():
     else:
         first = None
     for wi in range(args.warmup):
-        K.eviction_round(caches[1 + wi], seqs, obs, bufs, decay, n_prev, scale)
+        K.eviction_round(caches[1 + wi], seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate)
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -161,10 +164,14 @@ def main():
         evs[k][0].record(st)
         K.kvs_score(c, seqs, obs, scale, bufs.scores, bufs.workspace)
         evs[k][1].record(st)
-        K.kvs_lrfu_update(c, seqs, bufs.scores, 9, 10, decay, n_prev, None)
-        K.kvs_select(c, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
-        K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
-        K.kvs_compact(c, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+        if args.separate:
+            K.kvs_lrfu_update(c, seqs, bufs.scores, 9, 10, decay, n_prev, None)
+            K.kvs_select(c, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
+            K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+            K.kvs_compact(c, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+        else:
+            K.kvs_lrfu_select(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h, bufs.keep)
+            K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps

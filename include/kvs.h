@@ -14,6 +14,7 @@
  *   kvs_plan         the conflict-free slot plan: kept rows outside the tail paired
  *                    with evicted slots inside it; the freed pages (host side)
  *   kvs_compact      one in-place pass that moves K row, V row and CRF per pair
+ *   kvs_plan_compact the two calls above fused (same results)
  *
  * Sources, cited by page title and section:
  *   "ActKV Dissected: 99% of an Agent's KV Cache Is Scratch Work, and the Budget
@@ -254,6 +255,19 @@ kvs_status kvs_plan_host(const kvs_seqs *seqs, const int32_t *budget_h, int32_t 
  */
 kvs_status kvs_compact(const kvs_cache *cache, const kvs_seqs *seqs, const int32_t *budget_h,
                        const int32_t *pairs, const int32_t *pair_count, void *stream);
+
+/*
+ * kvs_plan_compact -- kvs_plan followed by kvs_compact in one call, with the union of
+ * their arguments and validation, and the same results (pairs, pair_count, the host
+ * outputs and the moved K/V rows and CRF values).  While every stream has at most
+ * 8192 pairs and 8192 pages, one kernel plans and moves each stream, keeping the
+ * stream's pairs and block-table row on chip; otherwise the two kernels run in turn.
+ */
+kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const uint8_t *keep,
+                            const int32_t *budget, const int32_t *budget_h, int32_t *pairs,
+                            int32_t *pair_count, int32_t *shift_h, int32_t *new_start_h,
+                            int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                            int64_t *freed_count_h, void *stream);
 
 /*
  * Host-side budget ratchet (ActKV, Component 2 and Lineage): for each sequence

@@ -23,7 +23,7 @@ STATUS = {0: "KVS_OK", 1: "KVS_ERR_NULL", 2: "KVS_ERR_SHAPE", 3: "KVS_ERR_UNSUPP
 EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_workspace_size",
            "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_lrfu_select",
            "kvs_pair_capacity",
-           "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_budget_ratchet")
+           "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet")
 
 
 class KvsError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> C.CDLL:
         L.kvs_plan_host.argtypes = [P, P, P, P, P, P, C.c_int64, P]
         L.kvs_compact.restype = C.c_int
         L.kvs_compact.argtypes = [P, P, P, P, P, P]
+        L.kvs_plan_compact.restype = C.c_int
+        L.kvs_plan_compact.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.c_int64, P, P]
         L.kvs_budget_ratchet.restype = C.c_int
         L.kvs_budget_ratchet.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
         _lib = L
@@ -262,6 +264,22 @@ def kvs_compact(cache: PagedCache, seqs: SeqBatch, budget_h: np.ndarray, pairs, 
     budget_h = np.ascontiguousarray(budget_h, np.int32)
     _check(lib().kvs_compact(cache.ref, seqs.ref, _ptr(budget_h), _ptr(pairs), _ptr(pair_count),
                              _stream(stream)))
+
+
+def kvs_plan_compact(cache: PagedCache, seqs: SeqBatch, keep, budget, budget_h: np.ndarray, pairs,
+                     pair_count, stream=None) -> PlanHost:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    S = seqs.num_seqs
+    shift = np.zeros(S, np.int32)
+    new_start = np.zeros(S, np.int32)
+    new_len = np.zeros(S, np.int32)
+    cap = int(seqs.block_table_h.size)
+    freed = np.zeros(max(cap, 1), np.int32)
+    nfreed = np.zeros(1, np.int64)
+    _check(lib().kvs_plan_compact(cache.ref, seqs.ref, _ptr(keep), _ptr(budget), _ptr(budget_h), _ptr(pairs),
+                                  _ptr(pair_count), _ptr(shift), _ptr(new_start), _ptr(new_len), _ptr(freed),
+                                  cap, _ptr(nfreed), _stream(stream)))
+    return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
 
 
 def kvs_budget_ratchet(budget_h: np.ndarray, flags: np.ndarray, num: int = 7, den: int = 4,

@@ -331,6 +331,39 @@ kvs_status kvs_compact(const kvs_cache *cache, const kvs_seqs *seqs, const int32
   return hip_status(kvs::launch_compact(*cache, b, pairs, pair_count, P, (hipStream_t)stream));
 }
 
+kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const uint8_t *keep, const int32_t *budget,
+                            const int32_t *budget_h, int32_t *pairs, int32_t *pair_count, int32_t *shift_h,
+                            int32_t *new_start_h, int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                            int64_t *freed_count_h, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if (seqs->num_seqs > 0 && (!budget || !budget_h)) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const int64_t P = seqs->num_seqs ? pair_cap_of(seqs, budget_h) : 0;
+  if (seqs->num_seqs > 0 && (!keep || !pair_count || (P > 0 && !pairs)))
+    return fail(KVS_ERR_NULL, "keep/pairs/pair_count is NULL");
+  if ((st = kvs_plan_host(seqs, budget_h, shift_h, new_start_h, new_len_h, freed_h, freed_capacity,
+                          freed_count_h)) != KVS_OK)
+    return st;
+  if (seqs->num_seqs == 0) return ok();
+  const kvs::Batch b = make_batch(cache, seqs);
+  int32_t max_npages = 0;
+  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
+    const int32_t n = seqs->len_h[i];
+    const int32_t np = n == 0 ? 0 : (seqs->start_h[i] + n + kvs::kPage - 1) / kvs::kPage;
+    max_npages = np > max_npages ? np : max_npages;
+  }
+  if (kvs::plan_move_fits(P, max_npages))
+    return hip_status(kvs::launch_plan_move(*cache, b, keep, budget, pairs, pair_count, P, max_npages,
+                                            (hipStream_t)stream));
+  hipError_t e = kvs::launch_plan(b, keep, budget, pairs, pair_count, P, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (P == 0) return ok();
+  return hip_status(kvs::launch_compact(*cache, b, pairs, pair_count, P, (hipStream_t)stream));
+}
+
 kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs, int32_t num, int32_t den,
                               int32_t cap) {
   if (num_seqs < 0) return fail(KVS_ERR_SHAPE, "num_seqs < 0");

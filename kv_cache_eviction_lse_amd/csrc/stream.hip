@@ -20,10 +20,11 @@
 
 namespace kvs {
 
-constexpr int kRegU = 33;                                        // slots per thread
-constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 33792 entries per stream
+constexpr int kRegU = 32;                                        // slots per thread
+constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 32768 entries per stream
 constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
 constexpr int kDigitBits = 12;
+static_assert(kRegU % 8 == 0, "the 8-row load and CRF chunks tile the rows exactly");
 constexpr int kBins = 1 << kDigitBits;
 
 namespace {
@@ -207,12 +208,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   uint32_t c[kRegU];
   bool have_s = false;
   auto load_s = [&]() {
-    // 11 loads in flight per thread and chunk; a chunk's offsets die at issue
+    // 8 loads in flight per thread and chunk; a chunk's offsets die at issue
 #pragma unroll
-    for (int u0 = 0; u0 < kRegU; u0 += 11) {
+    for (int u0 = 0; u0 < kRegU; u0 += 8) {
       const int t = opaque(tid);
 #pragma unroll
-      for (int u = u0; u < u0 + 11; ++u) s[u] = sp[slot(u, t)];
+      for (int u = u0; u < u0 + 8; ++u) s[u] = sp[slot(u, t)];
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -267,10 +268,10 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
 #pragma unroll
       for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(u < cnt && s[u] >= vstar) << u;
     }
-    // LRFU update of the paged CRF, 11 rows at a time
+    // LRFU update of the paged CRF, 8 rows at a time
     const float d = a.decay[i];
     const int32_t np = a.n_prev[i];
-    constexpr int kChunk = 11;
+    constexpr int kChunk = 8;
     const int np_rel = np - tid;               // row u has a prior iff u * 1024 < np_rel
 #pragma unroll
     for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       return;
     }
   } else {
-    constexpr int kChunk = 11;
+    constexpr int kChunk = 8;
 #pragma unroll
     for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
       const int t = opaque(tid);

@@ -35,10 +35,16 @@ class RoundBuffers:
 
 def eviction_round(cache: K.PagedCache, seqs: K.SeqBatch, obs: K.ObserverSet, bufs: RoundBuffers,
                    decay, n_prev, scale: float, mass_num: int = 9, mass_den: int = 10,
-                   stream=None) -> K.PlanHost:
-    """Enqueue one full round; returns the host-side plan (shift, new start/len, freed pages)."""
+                   stream=None, fused: bool = True) -> K.PlanHost:
+    """Enqueue one full round; returns the host-side plan (shift, new start/len, freed pages).
+    fused: the cut/LRFU/keep set and the plan/move as one call each (same results)."""
     L, Hkv = cache.c.num_layers, cache.c.num_kv_heads
     K.kvs_score(cache, seqs, obs, scale, bufs.scores, bufs.workspace, stream)
+    if fused:
+        K.kvs_lrfu_select(cache, seqs, bufs.scores, mass_num, mass_den, decay, n_prev, bufs.budget,
+                          bufs.budget_h, bufs.keep, bufs.hit, stream)
+        return K.kvs_plan_compact(cache, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs,
+                                  bufs.pair_count, stream)
     K.kvs_lrfu_update(cache, seqs, bufs.scores, mass_num, mass_den, decay, n_prev, bufs.hit, stream)
     K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep, stream)
     plan = K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs,

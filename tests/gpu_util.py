@@ -32,7 +32,8 @@ def upload(lay, inp):
 
 def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None, fused=False):
     """Run the round stage by stage on the GPU; return every intermediate on the host.
-    fused: run the cut, LRFU update and keep set through kvs_lrfu_select."""
+    fused: run the cut, LRFU update and keep set through kvs_lrfu_select, and the plan
+    and the move through kvs_plan_compact."""
     import torch
     import kv_cache_eviction_lse_amd as K
     dev = _dev()
@@ -60,16 +61,21 @@ def run_stages(lay, inp, Hq, budget, decay_h, mass=(9, 10), scale=None, fused=Fa
         K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
         torch.cuda.synchronize()
     out["keep"] = bufs.keep.cpu().numpy().astype(bool)
-    plan = K.kvs_plan(seqs, cache.c.num_layers, cache.c.num_kv_heads, bufs.keep, bufs.budget,
-                      bufs.budget_h, bufs.pairs, bufs.pair_count)
+    out["k0"] = cache.k.cpu().numpy().view(np.uint16)
+    out["v0"] = cache.v.cpu().numpy().view(np.uint16)
+    if fused:
+        plan = K.kvs_plan_compact(cache, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs,
+                                  bufs.pair_count)
+    else:
+        plan = K.kvs_plan(seqs, cache.c.num_layers, cache.c.num_kv_heads, bufs.keep, bufs.budget,
+                          bufs.budget_h, bufs.pairs, bufs.pair_count)
     torch.cuda.synchronize()
     out["plan"] = plan
     out["pairs"] = bufs.pairs.cpu().numpy()
     out["pair_count"] = bufs.pair_count.cpu().numpy()
     out["P"] = bufs.P
-    out["k0"] = cache.k.cpu().numpy().view(np.uint16)
-    out["v0"] = cache.v.cpu().numpy().view(np.uint16)
-    K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    if not fused:
+        K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
     torch.cuda.synchronize()
     out["k1"] = cache.k.cpu().numpy().view(np.uint16)
     out["v1"] = cache.v.cpu().numpy().view(np.uint16)
@@ -233,11 +239,15 @@ def run_config_sampled(w, lay, q_host, sample, scale=None, fused=False):
     if not fused:
         K.kvs_select(cache, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
     grab("keep", lambda s: ent(bufs.keep, s).astype(bool))
-    plan = K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    grab("kv0", kv_pages)
+    if fused:
+        plan = K.kvs_plan_compact(cache, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    else:
+        plan = K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
     grab("pairs", lambda s: bufs.pairs[s[1], s[2], s[0], :max(int(bufs.pair_count[s[1], s[2], s[0]]), 0)]
          .cpu().numpy())
-    grab("kv0", kv_pages)
-    K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
+    if not fused:
+        K.kvs_compact(cache, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
     grab("kv1", kv_pages)
     grab("crf2", crf_pages)
     torch.cuda.synchronize()

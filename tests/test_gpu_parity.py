@@ -72,7 +72,7 @@ EDGE_CASES = [
     ("long_multi_chunk", 1, 1, 4, [5000, 3333], [0, 13], [24, 18], [700, 1000]),
     ("gqa1", 1, 4, 4, [300, 300], [0, 8], [16, 16], [30, 30]),
     ("valu_row_groups", 1, 1, 32, [300], [0], [15], [40]),
-    # streams longer than the register-resident per-stream kernels hold (33792 entries)
+    # streams longer than the register-resident per-stream kernels hold (32768 entries)
     ("long_stream", 1, 1, 4, [40000, 2000], [5, 0], [16, 16], [3000, 700]),
     # more than 255 sequences: item tables built on the device
     ("many_seqs", 1, 1, 4, [(37 * i) % 90 + 1 for i in range(300)], [(5 * i) % 16 for i in range(300)],
@@ -98,7 +98,8 @@ FUSED_CASES = ["page_edges_mfma", "mixed_paths", "empty_and_no_obs", "budget_all
 
 @pytest.mark.parametrize("name", FUSED_CASES)
 def test_fused_lrfu_select(name):
-    """kvs_lrfu_select writes the same CRF, hits and keep set as the two separate calls."""
+    """kvs_lrfu_select and kvs_plan_compact give the same CRF, hits, keep set, pairs and
+    moved bytes as the separate calls."""
     case = next(c for c in EDGE_CASES if c[0] == name)
     _, L, Hkv, Hq, lengths, starts, obs, budgets = case
     print(f"fused {name}: L{L} Hkv{Hkv} Hq{Hq} n={lengths}", flush=True)
