@@ -115,6 +115,24 @@ __device__ __forceinline__ void block_and_or(uint32_t &a, uint32_t &o, uint32_t 
   o = ro;
 }
 
+// Block-wide maximum of a u32.  scratch: kStreamWaves u32.  Every thread must call it.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t *scratch) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr2, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr4, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr8, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false));
+  x = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) scratch[wave] = x;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r = max(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
 // Exclusive block-wide prefix sum of one u32 per thread (thread order), plus the
 // total.  scratch: kStreamWaves u32.  One barrier pair.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t &total, uint32_t *scratch) {
@@ -152,16 +170,18 @@ __device__ __forceinline__ uint32_t block_flag_rank(bool flag, uint32_t &total, 
   return before + in_wave;
 }
 
-// floor(s * 2^32) for a finite fp32 s >= 0, from its bit pattern.  Negative values,
-// infinities and NaNs (outside the kernel contract) count as zero mass.
+// floor(s * 2^32) for a finite fp32 s >= 0, from its bit pattern, without branches:
+// the integer part of s and the fraction times 2^32, each by a truncating conversion.
+// Both steps are exact (the fraction of an fp32 value and its product with a power of
+// two are representable, and truncation is floor for s >= 0).  Negative values,
+// infinities and NaNs (outside the kernel contract) count as zero mass; values of 2^32
+// and more (also outside it) saturate.
 __device__ __forceinline__ uint64_t fixed_mass(uint32_t bits) {
-  if (bits & 0x80000000u) return 0;
-  const uint32_t e = bits >> 23;
-  if (e == 255) return 0;
-  const uint64_t mant = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-  const int sh = (int)(e ? e : 1u) - 118;     // s * 2^32 = mant * 2^(E - 118)
-  if (sh >= 0) return sh < 32 ? (mant << sh) : 0;
-  return sh > -64 ? (mant >> (-sh)) : 0;
+  const float s = __uint_as_float(bits);
+  const uint32_t hi = __float2uint_rz(s);
+  const uint32_t lo = __float2uint_rz((s - (float)hi) * 4294967296.0f);
+  const uint64_t m = ((uint64_t)hi << 32) | lo;
+  return bits < 0x7F800000u ? m : 0ull;
 }
 
 // Address of the CRF of live slot j of a stream.

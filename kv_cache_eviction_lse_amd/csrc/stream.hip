@@ -24,6 +24,10 @@ constexpr int kRegU = 32;                                        // slots per th
 constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 32768 entries per stream
 constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
 constexpr int kDigitBits = 12;
+constexpr int kTieList = 512;   // CRF ties at the threshold ranked directly up to this many
+#ifndef KVS_CRF_CHUNK
+#define KVS_CRF_CHUNK 8
+#endif
 static_assert(kRegU % 8 == 0, "the 8-row load and CRF chunks tile the rows exactly");
 constexpr int kBins = 1 << kDigitBits;
 
@@ -51,17 +55,28 @@ struct Sel {
   uint32_t key;     // v*
   uint64_t above;   // weight of candidates with key > v*
   uint64_t at;      // weight of candidates with key == v*
+  uint64_t target;  // the target the search used
 };
 
-// Exclusive block-wide prefix sum of a u64 (thread order).  One barrier pair.
-__device__ __forceinline__ uint64_t block_excl_u64(uint64_t x, uint64_t *scratch) {
+// Exclusive block-wide prefix sum of a u64 (thread order), and the block total.  One
+// barrier pair.
+__device__ __forceinline__ uint64_t block_excl_u64(uint64_t x, uint64_t *scratch, uint64_t &total) {
   const uint64_t incl = wave_scan_u64(x);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) scratch[wave] = incl;
   __syncthreads();
-  uint64_t before = 0;
-  for (int w = 0; w < wave; ++w) before += scratch[w];
+  // lane w < waves holds wave w's total; one wave scan gives every wave its offset
+  const int lane = threadIdx.x & 63;
+  const uint64_t wsc = wave_scan_u64(lane < kStreamWaves ? scratch[lane] : 0ull);
   __syncthreads();
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto lane_u64 = [&](int l) -> uint64_t {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wsc, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wsc >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+  };
+  const uint64_t before = wv ? lane_u64(wv - 1) : 0ull;
+  total = lane_u64(kStreamWaves - 1);
   return before + incl - x;
 }
 
@@ -75,25 +90,39 @@ __device__ __forceinline__ int opaque(int x) {
 }
 
 // v* with weight(keys > v*) < target <= weight(keys >= v*) over the candidates
-// (slot valid and cand(u)); key[u] holds the key of this thread's row u.
-template <bool COUNT, typename CandF, typename WF>
+// (slot valid and cand(u)); key[u] holds the key of this thread's row u.  With CUT the
+// target is ceil(num * W / den) for the candidates' total weight W, which the first
+// pass yields (so W needs no pass of its own); otherwise it is `target`.  A target of
+// 0 returns key ~0 and at = 0.
+template <bool COUNT, bool CUT, typename CandF, typename WF>
 __device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt, CandF cand, WF weight_of,
-                                          uint64_t target, uint32_t and_all, uint32_t or_all, RegShared &sh) {
+                                          uint64_t target, uint32_t num, uint32_t den, uint32_t and_all,
+                                          uint32_t or_all, RegShared &sh) {
+  auto target_of = [&](uint64_t W) -> uint64_t {
+    if constexpr (CUT) return (W / den) * num + ((W % den) * num + den - 1) / den;
+    else return target;
+  };
   Sel r;
   const uint32_t diff = and_all ^ or_all;
   if (diff == 0) {
     uint64_t w = 0;
 #pragma unroll
-    for (int u = 0; u < kRegU; ++u)
+    for (int u = 0; u < kRegU; ++u) {
       if (u < cnt && cand(u)) w += COUNT ? 1ull : weight_of(key[u]);
-    r.key = and_all;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint64_t tot = block_sum_u64(w, sh.scratch);
+    r.target = target_of(tot);
+    r.key = r.target ? and_all : ~0u;
     r.above = 0;
-    r.at = block_sum_u64(w, sh.scratch);
+    r.at = r.target ? tot : 0;
     return r;
   }
   int top = 31 - __clz(diff);
   uint32_t prefix = top == 31 ? 0u : (and_all & ~((2u << top) - 1u));
-  uint64_t need = target, above = 0, at = 0;
+  uint64_t need = CUT ? 0 : target, above = 0, at = 0;
+  r.target = need;
+  bool first = CUT;
   while (top >= 0) {
     const int width = top + 1 < kDigitBits ? top + 1 : kDigitBits;
     const int lo = top - width + 1;
@@ -123,7 +152,19 @@ __device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt,
       h[q] = b >= 0 ? sh.hist[b] : 0ull;
       ls += h[q];
     }
-    uint64_t acc = block_excl_u64(ls, sh.scratch);
+    uint64_t tot;
+    uint64_t acc = block_excl_u64(ls, sh.scratch, tot);
+    if (first) {
+      first = false;
+      need = target_of(tot);
+      r.target = need;
+      if (need == 0) {
+        r.key = ~0u;
+        r.above = 0;
+        r.at = 0;
+        return r;
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int b = (int)nb - 1 - (4 * (int)threadIdx.x + q);
@@ -164,6 +205,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   __shared__ int32_t bt_lds[kRegBtCap];
   __shared__ RegShared sh;
   __shared__ uint32_t flag_scratch[kStreamWaves];
+  __shared__ uint32_t tie_s[kTieList];
+  __shared__ int32_t tie_j[kTieList];
+  __shared__ uint32_t tie_count;
 
   const int32_t i = blockIdx.y;
   const int32_t lg = blockIdx.x;
@@ -219,6 +263,17 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) s[u] = u < cnt ? s[u] : 0u;
   };
+  // every row's CRF in flight at once, issued in 8-row groups so that only a group's
+  // offsets are live at a time (nothing waits between the groups)
+  auto gather_crf = [&]() {
+#pragma unroll
+    for (int u0 = 0; u0 < kRegU; u0 += 8) {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int u = u0; u < u0 + 8; ++u) c[u] = __float_as_uint(crf_base[crf_off(u, t)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto all = [](int) { return true; };
   auto one = [](uint32_t) -> uint64_t { return 1; };
   __syncthreads();   // block-table slice visible
@@ -226,22 +281,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   if (LRFU) {
     load_s();
     have_s = true;
-    uint64_t msum = 0;
     uint32_t band = ~0u, bor = 0u;
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) {
-      msum += fixed_mass(s[u]);                 // 0 for rows without an entry
       band &= u < cnt ? s[u] : ~0u;
       bor |= s[u];
     }
-    const uint64_t M = block_sum_u64(msum, sh.scratch);
     block_and_or(band, bor, (uint32_t *)sh.scratch);
-    const uint64_t T = (M / a.den) * a.num + ((M % a.den) * a.num + a.den - 1) / a.den;
+    // T = ceil(num * M / den), M = the stream's total integer mass (from the first pass)
+    const Sel r = reg_select<false, true>(s, cnt, all, fixed_mass, 0, a.num, a.den, band, bor, sh);
+    const uint64_t T = r.target;
     const bool none = T == 0;
     uint32_t vstar = 0xFFFFFFFFu;
     uint64_t k_needed = 0, ties = 0;
     if (!none) {
-      const Sel r = reg_select<false>(s, cnt, all, fixed_mass, T, band, bor, sh);
       vstar = r.key;
       const uint64_t mstar = fixed_mass(vstar);
       k_needed = (T - r.above + mstar - 1) / mstar;
@@ -268,11 +321,10 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
 #pragma unroll
       for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(u < cnt && s[u] >= vstar) << u;
     }
-    // LRFU update of the paged CRF, 8 rows at a time
+    // LRFU update of the paged CRF, KVS_CRF_CHUNK rows per round trip
     const float d = a.decay[i];
-    const int32_t np = a.n_prev[i];
-    constexpr int kChunk = 8;
-    const int np_rel = np - tid;               // row u has a prior iff u * 1024 < np_rel
+    const int np_rel = a.n_prev[i] - tid;       // row u has a prior iff u * 1024 < np_rel
+    constexpr int kChunk = KVS_CRF_CHUNK;
 #pragma unroll
     for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
       const int t = opaque(tid);
@@ -312,30 +364,83 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       return;
     }
   } else {
-    constexpr int kChunk = 8;
-#pragma unroll
-    for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
-      const int t = opaque(tid);
-#pragma unroll
-      for (int v = 0; v < kChunk; ++v) c[u0 + v] = __float_as_uint(crf_base[crf_off(u0 + v, t)]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    gather_crf();
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) c[u] = u < cnt ? c[u] : 0u;
   }
 
   // ---- top-K keep set ----
-  uint32_t band = ~0u, bor = 0u;
+  // Common case first: when at least K entries share the largest CRF (every recent hit
+  // has CRF exactly 1 once the decayed prior rounds away), that value is c* and no
+  // radix pass over CRF is needed.
+  uint32_t band = ~0u, bor = 0u, cmax = 0u;
 #pragma unroll
   for (int u = 0; u < kRegU; ++u) {
     band &= u < cnt ? c[u] : ~0u;
     bor |= c[u];
+    cmax = c[u] > cmax ? c[u] : cmax;
   }
   block_and_or(band, bor, (uint32_t *)sh.scratch);
-  const Sel r1 = reg_select<true>(c, cnt, all, one, (uint64_t)K, band, bor, sh);
+  cmax = block_max_u32(cmax, (uint32_t *)sh.scratch);
+  uint32_t at_max = 0;
+#pragma unroll
+  for (int u = 0; u < kRegU; ++u) at_max += (u < cnt && c[u] == cmax) ? 1u : 0u;
+  const uint64_t n_max = block_sum_u64(at_max, sh.scratch);
+  Sel r1;
+  if (n_max >= (uint64_t)K) {
+    r1.key = cmax;
+    r1.above = 0;
+    r1.at = n_max;
+  } else {
+    r1 = reg_select<true, false>(c, cnt, all, one, (uint64_t)K, 0, 1, band, bor, sh);
+  }
   const uint32_t cstar = r1.key;
   const uint64_t need = K - r1.above;          // entries to keep among CRF == c*
   const bool lvl2 = need < r1.at;
+  if (lvl2 && r1.at <= (uint64_t)kTieList) {
+    // Few entries tie at c*: gather them (s, slot) into LDS and rank each one among
+    // the ties by (s desc, slot asc) directly; the first `need` are kept.
+    if (!have_s) load_s();
+    if (tid == 0) tie_count = 0;
+    __syncthreads();
+    const int lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      const bool t = u < cnt && c[u] == cstar;
+      const uint64_t m = __ballot(t);
+      if (m) {
+        const int leader = __ffsll((long long)m) - 1;
+        uint32_t base = 0;
+        if (lane == leader) base = atomicAdd(&tie_count, (uint32_t)__popcll(m));
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+        const uint32_t idx = base + (uint32_t)__popcll(m & lanemask_lt());
+        if (t && idx < (uint32_t)kTieList) {
+          tie_s[idx] = s[u];
+          tie_j[idx] = u * kStreamThreads + tid;
+        }
+      }
+    }
+    __syncthreads();
+    const int nt = (int)r1.at;     // == tie_count (the entries equal to c*)
+    for (int x = tid; x < nt; x += kStreamThreads) {
+      const uint32_t sx = tie_s[x];
+      const int32_t jx = tie_j[x];
+      uint32_t rank = 0;
+      for (int y = 0; y < nt; ++y) {
+        const uint32_t sy = tie_s[y];
+        rank += (sy > sx || (sy == sx && tie_j[y] < jx)) ? 1u : 0u;
+      }
+      kp[jx] = rank < need ? 1 : 0;
+    }
+    const int t = opaque(tid);
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      if (c[u] != cstar) {
+        KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = c[u] > cstar ? 1 : 0;)
+      }
+    }
+    return;
+  }
   uint32_t sstar = 0;
   uint64_t need2 = 0, at2 = 0;
   if (lvl2) {
@@ -349,7 +454,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     }
     block_and_or(sa, so, (uint32_t *)sh.scratch);
     auto in_tie = [&](int u) { return c[u] == cstar; };
-    const Sel r2 = reg_select<true>(s, cnt, in_tie, one, need, sa, so, sh);
+    const Sel r2 = reg_select<true, false>(s, cnt, in_tie, one, need, 0, 1, sa, so, sh);
     sstar = r2.key;
     need2 = need - r2.above;
     at2 = r2.at;
