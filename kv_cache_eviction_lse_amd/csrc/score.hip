@@ -20,6 +20,8 @@
 // Both evaluate p = exp2(fma(dot, scale*log2 e, -LSE*log2 e)) and accumulate in fp32.
 #include "kvs_internal.h"
 
+#include <type_traits>
+
 namespace kvs {
 namespace {
 
@@ -309,12 +311,15 @@ __device__ __forceinline__ void score_steps(const ScoreArgs &a, const Item &it, 
 }
 
 // sum over both M tiles of exp2(acc * alpha - lse*log2e): 32 values per lane, four
-// independent partial sums.
+// independent partial sums, each started from its first term.
 __device__ __forceinline__ float exp_rows2(const floatx16 &x0, const floatx16 &x1, float alpha,
                                            const float (*nl)[16]) {
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0[0], alpha, nl[0][0]));
+  float s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0[1], alpha, nl[0][1]));
+  float s2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1[0], alpha, nl[1][0]));
+  float s3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1[1], alpha, nl[1][1]));
 #pragma unroll
-  for (int k = 0; k < 16; k += 2) {
+  for (int k = 2; k < 16; k += 2) {
     s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(x0[k], alpha, nl[0][k]));
     s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(x0[k + 1], alpha, nl[0][k + 1]));
     s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(x1[k], alpha, nl[1][k]));
@@ -323,16 +328,18 @@ __device__ __forceinline__ float exp_rows2(const floatx16 &x0, const floatx16 &x
   return (s0 + s1) + (s2 + s3);
 }
 
-// One pipeline phase: the QK^T MFMAs of the next key tile (read from LDS into kb)
-// overlapped with the exp/sum of the previous tile's accumulators.  The scheduling
-// barriers fix the issue order: the 8 LDS reads first, then one MFMA per six VALU
-// operations, so that the matrix core runs while the exp work issues.
-__device__ __forceinline__ float pipe_phase(const uint8_t *buf, int tt, int col, int half,
+// One pipeline phase: the QK^T MFMAs of the next key tile (LDS bytes tile_base + rd[s]
+// for k-step s) overlapped with the exp/sum of the previous tile's accumulators.  The
+// scheduling barriers fix the issue order: the 8 LDS reads first, then one MFMA per
+// six VALU operations, so that the matrix core runs while the exp work issues.  With
+// tile_base a compile-time constant the reads take it as their immediate offset.
+__device__ __forceinline__ float pipe_phase(const uint8_t *tile_base, const uint32_t rd[8],
                                             const bf16x8 (*qa)[8], floatx16 &n0, floatx16 &n1,
                                             const floatx16 &p0, const floatx16 &p1, float alpha,
                                             const float (*nl)[16]) {
   bf16x8 kb[8];
-  read_tile(buf, tt, col, half, kb);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kb[s] = *(const bf16x8 *)(tile_base + rd[s]);
   floatx16 c0 = {}, c1 = {};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -351,22 +358,17 @@ __device__ __forceinline__ float pipe_phase(const uint8_t *buf, int tt, int col,
   return v;
 }
 
-// Exp/sum of the last tile (no MFMA work left to overlap).
-__device__ __forceinline__ float pipe_drain(const floatx16 &p0, const floatx16 &p1, float alpha,
-                                            const float (*nl)[16]) {
-  return exp_rows2(p0, p1, alpha, nl);
-}
-
 // Main loop for row groups of more than 128 rows: every active wave owns 64 rows (two
 // M tiles; rows past the end have zero Q and LSE +inf, so they add exactly 0) and
 // takes both key tiles of every step.  Tile j's MFMAs overlap tile j-1's exp work:
 //   phase A of step k:  MFMA(k, tile 1)    || exp(k, tile 0)
 //   phase B of step k:  ring barrier(k+1), refill, combine;
 //                       MFMA(k+1, tile 0)  || exp(k, tile 1)
-// Each wave writes its per-lane partial sums (both lane halves) to part[k % 3]; wave
-// 0 combines tile 0 and wave 1 tile 1 of a step once a barrier has passed after every
-// wave wrote them.  Three partial buffers keep a buffer from being rewritten before
-// it is combined (a wave can be at most one barrier ahead of the combining wave).
+// The loop is unrolled over the 4 ring slots, so that every LDS address of a step is a
+// per-lane register plus an immediate.  Each wave writes its per-lane partial sums
+// (both lane halves) to part[k % 4]; wave 0 combines tile 0 and wave 1 tile 1 of a
+// step once a barrier has passed after every wave wrote them (a wave can be at most
+// one barrier ahead of the combining wave, so a buffer is never rewritten early).
 __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item &it,
                                                  uint8_t (*ring)[kStepBytes],
                                                  float (*part)[kStepTiles][kWaves][64],
@@ -381,12 +383,20 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
   auto nloads = [&](int32_t j) -> int { return (j < s_end && j * kStepPages + wave < it.npages) ? 4 : 0; };
   // sum the wpr partials of (step, tt) and store the 32 keys
   auto combine = [&](int32_t step, int tt) {
-    const float *pp = &part[(step - s_begin) % 3][tt][0][0];
+    // the buffer offset goes through an empty asm so that the compiler computes it here
+    // instead of keeping one address per (slot, tile) live across the loop
+    int off = (((step - s_begin) & (kRing - 1)) * kStepTiles + tt) * (kWaves * 64) + lane;
+    asm volatile("" : "+v"(off));
+    const float *pp = &part[0][0][0][0] + off;
     float v = 0.f;
-    for (int w = 0; w < wpr; ++w) v += pp[w * 64 + lane] + pp[w * 64 + 32 + lane];
+    for (int w = 0; w < wpr; ++w) v += pp[w * 64] + pp[w * 64 + 32];
     const int32_t tile = step * kStepTiles + tt;
     if (tile < ntiles) store_key(a, it, tile, lane, v);
   };
+  // B operand k-step s of key n = col: dims 16s + 8h .. +8, stored at chunk (2s+h) ^ (n % 16)
+  uint32_t rd[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rd[s] = (uint32_t)(col * (kHeadDim * 2) + (((2 * s + half) ^ (col & 15)) << 4));
 
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u)
@@ -395,43 +405,47 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
   if (s_begin + kRing - 1 < s_end)
     issue_step(a, it, s_begin + kRing - 1, ring[kRing - 1], bt_lds, page0, wave, lane);
 
+  constexpr int kTileBytes = kTileKeys * kHeadDim * 2;
   floatx16 t0a = {}, t0b = {}, t1a = {}, t1b = {};
   if (active) {
     bf16x8 kb[8];
-    read_tile(ring[0], 0, col, half, kb);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kb[s] = *(const bf16x8 *)(ring[0] + rd[s]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       t0a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], t0a, 0, 0, 0);
       t0b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], t0b, 0, 0, 0);
     }
   }
-  for (int32_t step = s_begin; step < s_end; ++step) {
-    const int k = step - s_begin;
-    const int cur = k & (kRing - 1);
-    float *mine = &part[k % 3][0][wrow][0];
+  // one step with its ring slot (== its part buffer) fixed at compile time
+  auto do_step = [&](auto slot_c, int32_t step) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr int NEXT = (SLOT + 1) & (kRing - 1);
+    float *mine = &part[SLOT][0][wrow][0];
     // phase A
-    if (active) {
-      const float v = pipe_phase(ring[cur], 1, col, half, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
-      mine[lane] = v;                                   // part[k % 3][0][wrow][lane]
-    }
+    if (active) mine[lane] = pipe_phase(ring[SLOT] + kTileBytes, rd, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
     // phase B
-    const bool more = step + 1 < s_end;
-    if (more) {
+    if (step + 1 < s_end) {
       ring_barrier(nloads(step + 2) + nloads(step + 3));
-      if (step + kRing < s_end)
-        issue_step(a, it, step + kRing, ring[cur], bt_lds, page0, wave, lane);
+      if (step + kRing < s_end) issue_step(a, it, step + kRing, ring[SLOT], bt_lds, page0, wave, lane);
       if (lane < 32) {
         if (wave == 0) combine(step, 0);
         else if (wave == 1 && step > s_begin) combine(step - 1, 1);
       }
-      if (active) {
-        const float v = pipe_phase(ring[(k + 1) & (kRing - 1)], 0, col, half, qa, t0a, t0b, t1a, t1b,
-                                   a.alpha, nl);
-        mine[kWaves * 64 + lane] = v;                   // part[k % 3][1][wrow][lane]
-      }
+      if (active)
+        mine[kWaves * 64 + lane] = pipe_phase(ring[NEXT], rd, qa, t0a, t0b, t1a, t1b, a.alpha, nl);
     } else if (active) {
-      mine[kWaves * 64 + lane] = pipe_drain(t1a, t1b, a.alpha, nl);
+      mine[kWaves * 64 + lane] = exp_rows2(t1a, t1b, a.alpha, nl);
     }
+  };
+  for (int32_t step = s_begin; step < s_end; step += kRing) {
+    do_step(std::integral_constant<int, 0>{}, step);
+    if (step + 1 >= s_end) break;
+    do_step(std::integral_constant<int, 1>{}, step + 1);
+    if (step + 2 >= s_end) break;
+    do_step(std::integral_constant<int, 2>{}, step + 2);
+    if (step + 3 >= s_end) break;
+    do_step(std::integral_constant<int, 3>{}, step + 3);
   }
   __syncthreads();
   if (lane < 32) {
@@ -444,7 +458,7 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
 
 __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
-  __shared__ float part[3][kStepTiles][kWaves][64];
+  __shared__ float part[kRing][kStepTiles][kWaves][64];
   __shared__ int32_t bt_lds[kMaxChunkSteps * kStepPages];
 
   Item it;
