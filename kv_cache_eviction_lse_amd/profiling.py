@@ -5,6 +5,10 @@ Kernel statistics (from `rocprofv3 --kernel-trace --stats --output-format csv`):
 
     python -m kv_cache_eviction_lse_amd.profiling stats --dir DIR --command "..." > summary.md
 
+Socket power and graphics clock while a command runs (amd-smi samples):
+
+    python -m kv_cache_eviction_lse_amd.profiling power --interval 0.5 -- python3 bench.py --hold 8
+
 HBM traffic of the scorer per launch, from two counter runs of bench.py with a plain
 copy of known size (`--calibration-copy MiB`) in the same process: FETCH_SIZE and
 WRITE_SIZE of each kernel are scaled by bytes / counter of the copy kernel.
@@ -120,6 +124,59 @@ def traffic(args) -> None:
     print(f"\nscore.hip sha256[:16] = {out['score_source_sha']}")
 
 
+def _smi_sample() -> tuple[float, float] | None:
+    """(socket power W, first GFX clock MHz) from `amd-smi metric -p -c`, or None."""
+    import subprocess
+    try:
+        txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except Exception:
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    ck = re.search(r"\bCLK:\s*([0-9.]+)\s*MHz", txt)
+    if not pw or not ck:
+        return None
+    return float(pw.group(1)), float(ck.group(1))
+
+
+def power(args) -> None:
+    """Run a command and sample socket power and graphics clock while it runs."""
+    import statistics
+    import subprocess
+    import time
+    cmd = args.cmd_args[1:] if args.cmd_args[:1] == ["--"] else args.cmd_args
+    child = subprocess.Popen(cmd, stdout=subprocess.PIPE, text=True)
+    samples = []
+    t0 = time.time()
+    while child.poll() is None:
+        time.sleep(args.interval)
+        s = _smi_sample()
+        if s is not None:
+            samples.append((time.time() - t0, *s))
+    out = child.stdout.read()
+    if child.returncode != 0:
+        sys.exit(f"command failed with status {child.returncode}")
+    if not samples:
+        sys.exit("no amd-smi samples")
+    top = max(p for _, p, _ in samples)
+    loaded = [(t, p, c) for t, p, c in samples if p >= 0.8 * top]
+    print("# Socket power and graphics clock while the command runs\n")
+    print(f"Command: `python -m kv_cache_eviction_lse_amd.profiling power --interval {args.interval} -- "
+          f"{' '.join(cmd)}`\n")
+    print(f"Samples: {len(samples)} every {args.interval} s; loaded samples (power >= 80 % of the "
+          f"largest): {len(loaded)}\n")
+    print("| | socket power W | graphics clock MHz |")
+    print("|---|---|---|")
+    print(f"| median of loaded samples | {statistics.median(p for _, p, _ in loaded):.0f} | "
+          f"{statistics.median(c for _, _, c in loaded):.0f} |")
+    print(f"| min / max of loaded samples | {min(p for _, p, _ in loaded):.0f} / "
+          f"{max(p for _, p, _ in loaded):.0f} | {min(c for _, _, c in loaded):.0f} / "
+          f"{max(c for _, _, c in loaded):.0f} |")
+    print("\nCommand output (last line):\n")
+    lines = [x for x in out.strip().splitlines() if x.strip()]
+    print("```\n" + (lines[-1] if lines else "") + "\n```")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,8 +191,11 @@ def main() -> None:
     t.add_argument("--json", required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
     t.add_argument("--command", action="append", default=[])
+    pw = sub.add_parser("power")
+    pw.add_argument("--interval", type=float, default=0.5)
+    pw.add_argument("cmd_args", nargs=argparse.REMAINDER)
     args = ap.parse_args()
-    stats(args) if args.cmd == "stats" else traffic(args)
+    {"stats": stats, "traffic": traffic, "power": power}[args.cmd](args)
 
 
 if __name__ == "__main__":
