@@ -9,3 +9,4 @@ from .kvs_oracle import (  # noqa: F401
     select_top_b, ratchet, RATCHET_INITIAL, RATCHET_NUM, RATCHET_DEN, RATCHET_CAP,
     plan_stream, plan_sequence, compact_stream, eviction_round, round_fraction_to_f32,
 )
+from . import confidence_oracle as confidence  # noqa: F401
