@@ -13,6 +13,11 @@ round on the same 32K-entry layout (the evicted slots stand for freshly appended
 tokens), so the work per step is constant.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+`--workload token_confidence` instead times the confidence monitor that drives the
+budget ratchet: kvs_token_confidence over one round's decode steps (64 sequences x
+64 steps = 4 096 rows of bf16 logits over the Llama-3 vocabulary, 128 256 tokens),
+and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -76,6 +81,76 @@ def load_traffic(workload):
     return float(t["hbm_bytes_per_launch"])
 
 
+CONF_METRIC = ("decode-step logit rows scored (top-20 mean NLL confidence)/sec; achieved HBM GB/s vs peak "
+               "(Llama-3 vocabulary)")
+
+
+def bench_confidence(args) -> None:
+    """kvs_token_confidence over 4 096 rows x 128 256 bf16 logits (one JSON line)."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import logits as LG
+    import oracle as O
+
+    rows, V, k = 4096, LG.LLAMA3_VOCAB, 20
+    dev = torch.device("cuda", 0)
+    x = LG.lm_rows_device(7, rows, V, dev, torch.bfloat16)
+    conf = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kvs_token_confidence_workspace_size(rows, V, k), 4), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            K.kvs_token_confidence(x, conf, k=k, workspace=ws)
+        torch.cuda.synchronize()
+    t_settle = time.perf_counter() - t_settle
+    for _ in range(args.warmup):
+        K.kvs_token_confidence(x, conf, k=k, workspace=ws)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(st)
+        K.kvs_token_confidence(x, conf, k=k, workspace=ws)
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    byts = rows * V * 2 + rows * 4          # logits read once, one fp32 per row written
+    gbps = byts / (ev_ms / 1000.0) / 1e9
+    out = {
+        "metric": CONF_METRIC, "value": rows / (ms / 1000.0), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "token_confidence", "rows": rows, "vocab": V, "k": k, "logits": "bf16",
+                   "rows_are": "64 sequences x 64 decode steps"},
+        "hbm_gbps": byts / (ms / 1000.0) / 1e9, "hbm_frac": byts / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "conf_chunk_kernel (+ conf_combine_kernel)", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "ms": ev_ms, "bytes_per_launch": byts},
+    }
+    if not args.no_cpu_baseline:
+        got = conf.cpu().numpy()
+        pick = np.random.default_rng(0).permutation(rows)
+        t_cpu, n_done, worst = 0.0, 0, 0.0
+        for r in pick:
+            bits = x[int(r)].view(torch.int16).cpu().numpy().view(np.uint16)
+            z = LG.bf16_bits_to_f64(bits)
+            ta = time.perf_counter()
+            want = O.confidence.token_confidence(z, k)
+            t_cpu += time.perf_counter() - ta
+            n_done += 1
+            worst = max(worst, abs(float(got[int(r)]) - want))
+            if t_cpu >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {"value": n_done / t_cpu, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n_done} of {rows} rows of the same batch, {t_cpu:.1f} s of fp64 "
+                                         f"numpy oracle time (one thread)"}
+        out["parity"] = {"rows": n_done, "max_abs_conf_err": worst}
+    out["setup_s"] = {"settle_s": round(t_settle, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +177,9 @@ def main():
               "runs and reports a single MI355X.", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "token_confidence":
+        bench_confidence(args)
+        return
     from workloads import ALL
     from workloads.host import make_layout, observers
     w = ALL[args.workload]

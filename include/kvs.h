@@ -16,6 +16,13 @@
  *   kvs_compact      one in-place pass that moves K row, V row and CRF per pair
  *   kvs_plan_compact the two calls above fused (same results)
  *
+ * and, for the budget that the rounds use (ActKV, Component 2):
+ *
+ *   kvs_token_confidence  per decode step, the mean negative log-probability of
+ *                         the k most probable tokens (the model's confidence)
+ *   kvs_confidence_trend  min-pooling of those values and the sign of a fitted
+ *                         line: the flag for kvs_budget_ratchet (host)
+ *
  * Sources, cited by page title and section:
  *   "ActKV Dissected: 99% of an Agent's KV Cache Is Scratch Work, and the Budget
  *   Follows Hesitation" (zhichai.net):  Summary; Component 1 (action-attention-
@@ -277,6 +284,59 @@ kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const 
  */
 kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs,
                               int32_t num, int32_t den, int32_t cap);
+
+/*
+ * Logit element types for kvs_token_confidence.
+ */
+enum { KVS_DTYPE_F32 = 0, KVS_DTYPE_BF16 = 1 };
+
+/*
+ * Bytes of device workspace kvs_token_confidence needs: fp32 partial results per
+ * (row, chunk of 32 768 logits) when vocab > 32 768, else 0.  Returns 0 (and sets
+ * kvs_last_error()) on invalid arguments.
+ */
+size_t kvs_token_confidence_workspace_size(int64_t rows, int64_t vocab, int32_t k);
+
+/*
+ * kvs_token_confidence -- ActKV, Component 2 (the model's hesitation at each step,
+ * read from the top-20 tokens of the step's output distribution).  For every row r
+ * (one decode step's logits z over the vocabulary, softmax at temperature 1):
+ *     conf[r] = (1/k) * sum over the k largest z_j of -ln softmax(z)_j
+ *             = LSE(z) - mean of the k largest z_j
+ * i.e. the mean negative log-probability of the k most probable tokens (the pages:
+ * k = 20).  A peaked distribution gives a large value, a flat one a value near
+ * ln(vocab).  fp32 arithmetic; which of several equal logits fill the k-th place
+ * does not change the result.
+ * logits: device, [rows][row_stride] elements of type dtype (KVS_DTYPE_F32 or
+ *   KVS_DTYPE_BF16), the first vocab of each row used.  -inf logits are tokens of
+ *   probability 0 (a row needs at least one finite logit; fewer than k finite ones
+ *   give +inf); NaN is undefined.
+ * conf: device fp32 [rows].  1 <= k <= 64, k <= vocab <= 2^20 (else
+ *   KVS_ERR_SHAPE / KVS_ERR_UNSUPPORTED).  workspace: device, at least
+ *   kvs_token_confidence_workspace_size bytes (scratch, overwritten), 4-byte aligned.
+ */
+kvs_status kvs_token_confidence(const void *logits, int32_t dtype, int64_t rows, int64_t vocab,
+                                int64_t row_stride, int32_t k, float *conf, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * kvs_confidence_trend (host) -- ActKV, Component 2 (token-level confidence
+ * min-pooled over sliding windows into a trajectory-level series; a fitted line
+ * with negative slope means the budget is too small).  From n token confidences
+ * conf_h (host, in step order):
+ *   pooled[w] = min(conf_h[w*stride .. w*stride + window - 1]), for every full
+ *               window, P = (n - window) / stride + 1 of them (0 if n < window);
+ *               the pages: window 64, stride 8;
+ *   slope     = ordinary least-squares slope of the last fit_last pooled values
+ *               (0 = all P) against their index 0, 1, ..., in fp64;
+ *   flag      = 1 if slope < 0, else 0 (also 0 when fewer than two values are fitted,
+ *               and then slope = NaN).
+ * pooled_h (nullable): host double [P]; pooled_count_h, slope_h (nullable): host.
+ * flag_h: host int32, feed it to kvs_budget_ratchet.
+ */
+kvs_status kvs_confidence_trend(const float *conf_h, int64_t n, int32_t window, int32_t stride,
+                                int64_t fit_last, double *pooled_h, int64_t *pooled_count_h,
+                                double *slope_h, int32_t *flag_h);
 
 /* Library version string. */
 const char *kvs_version(void);

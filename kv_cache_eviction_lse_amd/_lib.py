@@ -23,7 +23,10 @@ STATUS = {0: "KVS_OK", 1: "KVS_ERR_NULL", 2: "KVS_ERR_SHAPE", 3: "KVS_ERR_UNSUPP
 EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_workspace_size",
            "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_lrfu_select",
            "kvs_pair_capacity",
-           "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet")
+           "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
+           "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend")
+
+KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
 
 class KvsError(RuntimeError):
@@ -92,6 +95,13 @@ def lib() -> C.CDLL:
         L.kvs_plan_compact.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.c_int64, P, P]
         L.kvs_budget_ratchet.restype = C.c_int
         L.kvs_budget_ratchet.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+        L.kvs_token_confidence_workspace_size.restype = C.c_size_t
+        L.kvs_token_confidence_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int32]
+        L.kvs_token_confidence.restype = C.c_int
+        L.kvs_token_confidence.argtypes = [P, C.c_int32, C.c_int64, C.c_int64, C.c_int64, C.c_int32, P, P,
+                                           C.c_size_t, P]
+        L.kvs_confidence_trend.restype = C.c_int
+        L.kvs_confidence_trend.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, C.c_int64, P, P, P, P]
         _lib = L
     return _lib
 
@@ -288,6 +298,44 @@ def kvs_budget_ratchet(budget_h: np.ndarray, flags: np.ndarray, num: int = 7, de
     f = np.ascontiguousarray(flags, np.uint8)
     _check(lib().kvs_budget_ratchet(_ptr(b), _ptr(f), b.shape[0], num, den, cap))
     return b
+
+
+def kvs_token_confidence_workspace_size(rows: int, vocab: int, k: int = 20) -> int:
+    return int(lib().kvs_token_confidence_workspace_size(rows, vocab, k))
+
+
+def kvs_token_confidence(logits, conf, k: int = 20, vocab: int | None = None, workspace=None,
+                         stream=None) -> None:
+    """logits: device tensor [rows][row_stride] (float32 or bfloat16), the first `vocab`
+    (default: all) columns used; conf: device float32 [rows]."""
+    import torch
+    dtype = {torch.float32: KVS_DTYPE_F32, torch.bfloat16: KVS_DTYPE_BF16}.get(logits.dtype)
+    if dtype is None:
+        raise KvsError(3, f"logits dtype {logits.dtype} (float32 or bfloat16)")
+    rows, stride = int(logits.shape[0]), int(logits.stride(0))
+    assert logits.stride(1) == 1
+    V = int(logits.shape[1]) if vocab is None else int(vocab)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvs_token_confidence(C.c_void_p(logits.data_ptr()), dtype, rows, V, stride, k, _ptr(conf),
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+class Trend:
+    def __init__(self, pooled, slope, flag):
+        self.pooled, self.slope, self.flag = pooled, slope, flag
+
+
+def kvs_confidence_trend(conf_h: np.ndarray, window: int = 64, stride: int = 8, fit_last: int = 0) -> Trend:
+    c = np.ascontiguousarray(conf_h, np.float32)
+    n = c.shape[0]
+    P = (n - window) // stride + 1 if n >= window else 0
+    pooled = np.zeros(max(P, 1), np.float64)
+    cnt = np.zeros(1, np.int64)
+    slope = np.zeros(1, np.float64)
+    flag = np.zeros(1, np.int32)
+    _check(lib().kvs_confidence_trend(_ptr(c), n, window, stride, fit_last, _ptr(pooled), _ptr(cnt),
+                                      _ptr(slope), _ptr(flag)))
+    return Trend(pooled[:int(cnt[0])].copy(), float(slope[0]), bool(flag[0]))
 
 
 def kvs_version() -> str:

@@ -381,3 +381,87 @@ kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t 
 }
 
 }  // extern "C"
+
+// ---- confidence monitor ----
+
+namespace {
+
+kvs_status check_confidence(int32_t dtype, int64_t rows, int64_t vocab, int64_t row_stride, int32_t k) {
+  if (dtype != KVS_DTYPE_F32 && dtype != KVS_DTYPE_BF16) return fail(KVS_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (rows < 0) return fail(KVS_ERR_SHAPE, "rows < 0");
+  if (vocab <= 0 || vocab > kvs::conf_max_vocab())
+    return fail(vocab <= 0 ? KVS_ERR_SHAPE : KVS_ERR_UNSUPPORTED, "vocab %lld not in [1, %lld]", (long long)vocab,
+                (long long)kvs::conf_max_vocab());
+  if (k < 1 || k > kvs::conf_max_k()) return fail(KVS_ERR_UNSUPPORTED, "k %d not in [1, %d]", k, kvs::conf_max_k());
+  if (k > vocab) return fail(KVS_ERR_SHAPE, "k %d > vocab %lld", k, (long long)vocab);
+  if (row_stride < vocab) return fail(KVS_ERR_SHAPE, "row_stride %lld < vocab", (long long)row_stride);
+  if (rows * (int64_t)kvs::conf_chunks(vocab) > ((int64_t)1 << 31) - 1)
+    return fail(KVS_ERR_UNSUPPORTED, "rows x chunks exceeds the grid limit");
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvs_token_confidence_workspace_size(int64_t rows, int64_t vocab, int32_t k) {
+  if (check_confidence(KVS_DTYPE_F32, rows, vocab, vocab, k) != KVS_OK) return 0;
+  return kvs::conf_workspace_bytes(rows, vocab, k);
+}
+
+kvs_status kvs_token_confidence(const void *logits, int32_t dtype, int64_t rows, int64_t vocab, int64_t row_stride,
+                                int32_t k, float *conf, void *workspace, size_t workspace_bytes, void *stream) {
+  kvs_status st;
+  if ((st = check_confidence(dtype, rows, vocab, row_stride, k)) != KVS_OK) return st;
+  if (rows == 0) return ok();
+  if (!logits || !conf) return fail(KVS_ERR_NULL, "logits/conf is NULL");
+  const size_t need = kvs::conf_workspace_bytes(rows, vocab, k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  return hip_status(kvs::launch_confidence(logits, dtype == KVS_DTYPE_BF16, rows, vocab, row_stride, k, conf,
+                                           workspace, (hipStream_t)stream));
+}
+
+kvs_status kvs_confidence_trend(const float *conf_h, int64_t n, int32_t window, int32_t stride, int64_t fit_last,
+                                double *pooled_h, int64_t *pooled_count_h, double *slope_h, int32_t *flag_h) {
+  if (n < 0 || window < 1 || stride < 1 || fit_last < 0)
+    return fail(KVS_ERR_SHAPE, "need n >= 0, window >= 1, stride >= 1, fit_last >= 0");
+  if (n > 0 && !conf_h) return fail(KVS_ERR_NULL, "conf_h is NULL");
+  if (!flag_h) return fail(KVS_ERR_NULL, "flag_h is NULL");
+  const int64_t P = n >= window ? (n - window) / stride + 1 : 0;
+  if (pooled_count_h) *pooled_count_h = P;
+  // minimum of each full window, windows starting every `stride` values
+  std::vector<double> pooled((size_t)P);
+  for (int64_t w = 0; w < P; ++w) {
+    double m = (double)conf_h[w * stride];
+    for (int64_t j = 1; j < window; ++j) m = std::fmin(m, (double)conf_h[w * stride + j]);
+    pooled[(size_t)w] = m;
+  }
+  if (pooled_h)
+    for (int64_t w = 0; w < P; ++w) pooled_h[w] = pooled[(size_t)w];
+  // least-squares slope against the window index over the last fit_last values (0 = all)
+  const int64_t first = (fit_last > 0 && fit_last < P) ? P - fit_last : 0;
+  const int64_t m = P - first;
+  *flag_h = 0;
+  if (slope_h) *slope_h = std::nan("");
+  if (m < 2) return ok();
+  double xb = 0.0, yb = 0.0;
+  for (int64_t i = 0; i < m; ++i) {
+    xb += (double)i;
+    yb += pooled[(size_t)(first + i)];
+  }
+  xb /= (double)m;
+  yb /= (double)m;
+  double sxy = 0.0, sxx = 0.0;
+  for (int64_t i = 0; i < m; ++i) {
+    const double dx = (double)i - xb;
+    sxy += dx * (pooled[(size_t)(first + i)] - yb);
+    sxx += dx * dx;
+  }
+  const double slope = sxy / sxx;
+  if (slope_h) *slope_h = slope;
+  *flag_h = slope < 0.0 ? 1 : 0;
+  return ok();
+}
+
+}  // extern "C"

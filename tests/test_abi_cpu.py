@@ -179,3 +179,70 @@ def test_empty_batch_is_a_no_op():
     o = K.Observers(None, None, None, None, 4, 0)
     assert status(L.kvs_score(C.byref(c), C.byref(s), C.byref(o), C.c_float(0.1), None, None, 0, None)) == "KVS_OK"
     assert L.kvs_score_workspace_size(C.byref(c), C.byref(s), C.byref(o)) == 0
+
+
+# ---------------------------------------------------------------------------
+# confidence monitor: validation of kvs_token_confidence (no launch), host trend
+
+
+def test_token_confidence_validation():
+    L = K.lib()
+    f = L.kvs_token_confidence
+    ok_args = dict(logits=FAKE, dtype=K.KVS_DTYPE_BF16, rows=4, vocab=128256, stride=128256, k=20,
+                   conf=FAKE, ws=FAKE, ws_bytes=1 << 30)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["logits"], a["dtype"], a["rows"], a["vocab"], a["stride"], a["k"], a["conf"], a["ws"],
+                 a["ws_bytes"], None)
+
+    assert call(dtype=7) == 3                       # unsupported dtype
+    assert call(k=0) == 3 and call(k=65) == 3        # k outside [1, 64]
+    assert call(vocab=10, stride=10, k=20) == 2      # k > vocab
+    assert call(vocab=(1 << 20) + 1, stride=(1 << 20) + 1) == 3
+    assert call(vocab=0) == 2
+    assert call(stride=1000) == 2                    # row stride below the vocabulary
+    assert call(rows=-1) == 2
+    assert call(logits=None) == 1 and call(conf=None) == 1
+    assert call(ws=None) == 4 and call(ws_bytes=16) == 4
+    assert call(rows=0) == 0                         # nothing to do: no launch
+    need = L.kvs_token_confidence_workspace_size(4, 128256, 20)
+    assert need == 4 * 4 * (2 + 20) * 4              # 4 chunks of 32 768 logits per row
+    assert L.kvs_token_confidence_workspace_size(4, 32768, 20) == 0
+    assert L.kvs_token_confidence_workspace_size(4, 32769, 64) == 4 * 2 * 66 * 4
+
+
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 71, 72, 200, 4096])
+@pytest.mark.parametrize("fit_last", [0, 1, 2, 5])
+def test_confidence_trend_matches_oracle(n, fit_last):
+    from oracle import confidence as CO
+    rng = np.random.default_rng(n * 7 + fit_last)
+    for shape in ("noise", "down", "up"):
+        c = rng.standard_normal(n).astype(np.float32) * 0.3 + 10
+        if shape == "down":
+            c -= np.linspace(0, 2, n, dtype=np.float32)
+        elif shape == "up":
+            c += np.linspace(0, 2, n, dtype=np.float32)
+        t = K.kvs_confidence_trend(c, 64, 8, fit_last)
+        slope, P, flag = CO.trend_flag(c.astype(np.float64), 64, 8, fit_last)
+        np.testing.assert_array_equal(t.pooled, CO.min_pool(c.astype(np.float64), 64, 8))
+        assert len(t.pooled) == P and t.flag == flag
+        if slope is None:
+            assert np.isnan(t.slope)
+        else:
+            assert t.slope == pytest.approx(slope, rel=1e-12, abs=1e-14)
+
+
+def test_confidence_trend_validation_and_ratchet():
+    L = K.lib()
+    flag = np.zeros(1, np.int32)
+    c = np.ones(100, np.float32)
+    assert L.kvs_confidence_trend(c.ctypes.data, 100, 0, 8, 0, None, None, None, flag.ctypes.data) == 2
+    assert L.kvs_confidence_trend(c.ctypes.data, 100, 64, 0, 0, None, None, None, flag.ctypes.data) == 2
+    assert L.kvs_confidence_trend(None, 100, 64, 8, 0, None, None, None, flag.ctypes.data) == 1
+    assert L.kvs_confidence_trend(c.ctypes.data, 100, 64, 8, 0, None, None, None, None) == 1
+    # a declining trajectory raises the flag, which grows the budget by 7/4
+    down = (12 - 0.01 * np.arange(300)).astype(np.float32)
+    t = K.kvs_confidence_trend(down)
+    assert t.flag and t.slope < 0
+    assert K.kvs_budget_ratchet(np.array([512], np.int32), np.array([t.flag], np.uint8))[0] == 896
