@@ -291,9 +291,10 @@ kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t 
 enum { KVS_DTYPE_F32 = 0, KVS_DTYPE_BF16 = 1 };
 
 /*
- * Bytes of device workspace kvs_token_confidence needs: fp32 partial results per
- * (row, chunk of 32 768 logits) when vocab > 32 768, else 0.  Returns 0 (and sets
- * kvs_last_error()) on invalid arguments.
+ * Bytes of device workspace kvs_token_confidence needs: (2 + k) fp32 partial
+ * results per (row, chunk of 8 192 logits) when vocab > 8 192, else 0 (sized for
+ * fp32 logits; bf16 rows use chunks of 16 384 and need at most this).  Returns 0
+ * (and sets kvs_last_error()) on invalid arguments.
  */
 size_t kvs_token_confidence_workspace_size(int64_t rows, int64_t vocab, int32_t k);
 

@@ -7,14 +7,17 @@
 //     conf = (1/k) sum_{j in T} -ln p_j = LSE(z) - mean_{j in T} z_j
 //          = ln S + (1/k) sum_{j in T} (M - z_j),   M = max z,  S = sum_j exp(z_j - M).
 //
-// One workgroup takes a chunk of 32 768 logits of one row (64 per thread, held in
-// VGPRs) and produces (M, S) and the chunk's k largest values; a row of a
-// 128 256-token vocabulary is 4 chunks.  The chunk's top k come without a sort:
-//   * the k-th largest of the 512 per-thread maxima, M_k, is found by a radix
-//     search over order-preserving integer keys (4 passes of 8 bits);
+// Rows are cut into chunks of 32 KiB of logits (16 384 bf16 or 8 192 fp32), one per
+// 256-thread workgroup, held in 32 VGPRs per thread; workgroups are small so that
+// six of them share a CU and one's barriers overlap the others' loads.  Per chunk:
+//   * the maximum M and S = sum exp(z - M): per-thread maxima and sums, the sums
+//     rescaled to M and added over the block;
+//   * the k-th largest of the 256 per-thread maxima, M_k: each wave sorts its 64
+//     maxima (bitonic, in registers), and each of the first k of every sorted list is
+//     ranked against the first k of the other lists; the one of rank k is M_k;
 //   * at least k values are >= M_k (one per thread whose maximum is >= M_k), and
 //     values > M_k only occur in the at most k-1 threads whose maximum is > M_k,
-//     so there are at most (k-1)*64 of them: they are compacted into LDS;
+//     so at most (k-1)*64 of them exist: they are appended to an LDS list;
 //   * if there are k or more, each is ranked among them (value, then position);
 //     otherwise the rest of the top k are copies of M_k.
 // A second kernel merges the chunks of a row: M = max M_c, S = sum S_c exp(M_c - M),
@@ -25,27 +28,56 @@
 namespace kvs {
 namespace {
 
-constexpr int kConfThreads = 512;
+constexpr int kConfThreads = 256;
 constexpr int kConfWaves = kConfThreads / 64;
-constexpr int kConfPer = 64;                                 // logits per thread
-constexpr int kConfChunk = kConfThreads * kConfPer;          // logits per workgroup
+constexpr int kConfWords = 32;                               // u32 of logits per thread and buffer
 constexpr int kConfMaxK = 64;
-constexpr int kCandCap = (kConfMaxK - 1) * kConfPer;         // values above M_k, at most
+constexpr int kCandCap = (kConfMaxK - 1) * 64;               // values above M_k, at most
 constexpr int kCombineThreads = 256;
-constexpr int kConfMaxChunks = 32;                           // vocabularies up to 2^20
+constexpr int kConfMaxChunks = 128;                          // vocabularies up to 2^20 (fp32 chunks)
+constexpr int kConfWavesPerSimd = 6;                         // occupancy the kernel is compiled for
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool BF16> constexpr int conf_per() { return BF16 ? 64 : 32; }     // logits per thread
+template <bool BF16> constexpr int conf_chunk() { return kConfThreads * conf_per<BF16>(); }
 
 struct ConfArgs {
   const void *logits;
   int64_t rows;
   int64_t vocab;
   int64_t stride;    // elements between rows
+  int64_t total;     // rows * chunks
   int32_t k;
   int32_t chunks;    // per row
   float *conf;       // [rows], written directly when chunks == 1
   float *part;       // [rows][chunks][2 + k]: M, S, then the chunk's top k values
 };
+
+struct ConfShared {
+  alignas(16) uint32_t sorted[kConfWaves][64];   // each wave's thread maxima (keys), descending
+  alignas(16) uint32_t cand[kCandCap];           // read 4 at a time: capacity a multiple of 4
+  float topv[kConfMaxK];
+  float ws[kConfWaves];                          // each wave's sum of exp(z - M)
+  uint32_t mk;
+  uint32_t ncand;
+};
+static_assert(kCandCap % 4 == 0, "candidate list read 4 at a time");
+
+// Wave sum of a float, result in lane 63 (DPP row shifts and broadcasts, no LDS).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp_f32(float x) {
+  x = dpp_add<kRowShr1, 0xF>(x);
+  x = dpp_add<kRowShr2, 0xF>(x);
+  x = dpp_add<kRowShr4, 0xF>(x);
+  x = dpp_add<kRowShr8, 0xF>(x);
+  x = dpp_add<kRowBcast15, 0xA>(x);
+  x = dpp_add<kRowBcast31, 0xC>(x);
+  return x;
+}
 
 // Order-preserving map of fp32 bit patterns to unsigned keys (NaN excluded).
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -56,16 +88,311 @@ __device__ __forceinline__ float key_f(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ float bf16_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Value of lane (lane ^ MASK).  Masks below 32 use ds_swizzle in bit-mask mode (the
+// pattern is an immediate: no address register); 32 uses ds_bpermute with the
+// partner address recomputed from the lane id.
+template <int MASK>
+__device__ __forceinline__ uint32_t xshfl(uint32_t v) {
+  if constexpr (MASK < 32) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (MASK << 10) | 0x1F);
+  } else {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ MASK) << 2, (int)v);
+  }
+}
+template <int MASK>
+__device__ __forceinline__ float xshfl_f(float v) { return __uint_as_float(xshfl<MASK>(__float_as_uint(v))); }
 
 __device__ __forceinline__ float wave_sum_f32(float x) {
-  x += __shfl_xor(x, 32);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 1);
+  x += xshfl_f<32>(x);
+  x += xshfl_f<16>(x);
+  x += xshfl_f<8>(x);
+  x += xshfl_f<4>(x);
+  x += xshfl_f<2>(x);
+  x += xshfl_f<1>(x);
   return x;
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only: vector loads of
+// the next chunk stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A copy of the thread index the compiler cannot see through: index arithmetic is
+// then recomputed where it is used instead of being hoisted out of the chunk loop
+// and kept live (or spilled) across it.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Logit i of this thread from a buffer of 32 words (bf16 pairs or fp32).
+template <bool BF16>
+__device__ __forceinline__ float logit(const uint32_t (&w)[kConfWords], int i) {
+  const uint32_t x = w[BF16 ? (i >> 1) : i];
+  if (BF16) return __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  return __uint_as_float(x);
+}
+
+// The buffer's words pass through an empty asm (in place, no instructions), so that
+// each pass over the buffer unpacks it again instead of keeping 64 unpacked values
+// (and their keys) live from one pass to the next.
+__device__ __forceinline__ void fence_words(uint32_t (&w)[kConfWords]) {
+#pragma unroll
+  for (int i = 0; i < kConfWords; ++i) asm volatile("" : "+v"(w[i]));
+}
+
+// Number of valid logits in chunk cidx (>= 1; < chunk size only in a row's last chunk).
+template <bool BF16>
+__device__ __forceinline__ int32_t conf_nvalid(const ConfArgs &a, int64_t cidx) {
+  constexpr int CH = conf_chunk<BF16>();
+  const int64_t row = cidx / a.chunks;
+  const int64_t rem = a.vocab - (cidx - row * a.chunks) * CH;
+  return (int32_t)(rem < CH ? rem : CH);
+}
+
+// Issue the loads of chunk `cidx` (row-major over (row, chunk)) into w.  Every load is
+// at an index clamped into the chunk's valid range, so no load depends on a branch and
+// nothing here waits on the data; conf_mask replaces the out-of-range positions.
+// VEC (rows 16-byte aligned and the vocabulary a multiple of the vector width):
+// 16-byte vector u of thread t holds logits (u * 512 + t) * per-vector, and whole
+// vectors are either valid or not.  Otherwise word i holds logits (2i * 512 + t) and
+// (2i+1) * 512 + t (bf16), or logit i * 512 + t (fp32).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint32_t (&w)[kConfWords]) {
+  constexpr int CH = conf_chunk<BF16>();
+  const int t = opaque_tid();
+  const int64_t row = cidx / a.chunks;
+  const int64_t c0 = (cidx - row * a.chunks) * CH;
+  const int32_t nvalid = conf_nvalid<BF16>(a, cidx);
+  if (VEC) {
+    constexpr int EPV = BF16 ? 8 : 4;                           // logits per vector
+    const uint4 *src = (const uint4 *)((const uint8_t *)a.logits + (row * a.stride + c0) * (BF16 ? 2 : 4));
+    const int32_t last = nvalid / EPV - 1;                        // vocab % EPV == 0
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int32_t vi = u * kConfThreads + t;
+      const uint4 v = src[vi < last ? vi : last];
+      w[4 * u] = v.x;
+      w[4 * u + 1] = v.y;
+      w[4 * u + 2] = v.z;
+      w[4 * u + 3] = v.w;
+    }
+  } else if (BF16) {
+    const uint16_t *src = (const uint16_t *)a.logits + row * a.stride + c0;
+#pragma unroll
+    for (int i = 0; i < kConfWords; ++i) {
+      const int32_t e0 = 2 * i * kConfThreads + t, e1 = e0 + kConfThreads;
+      const uint32_t lo = src[e0 < nvalid ? e0 : nvalid - 1], hi = src[e1 < nvalid ? e1 : nvalid - 1];
+      w[i] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t *src = (const uint32_t *)a.logits + row * a.stride + c0;
+#pragma unroll
+    for (int i = 0; i < kConfWords; ++i) {
+      const int32_t e = i * kConfThreads + t;
+      w[i] = src[e < nvalid ? e : nvalid - 1];
+    }
+  }
+}
+
+// Set the positions of a partial chunk that lie past the row end to -inf.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void conf_mask(int32_t nvalid, uint32_t (&w)[kConfWords]) {
+  const int t = opaque_tid();
+#pragma unroll
+  for (int i = 0; i < kConfWords; ++i) {
+    if (VEC) {
+      constexpr int EPV = BF16 ? 8 : 4;
+      const int32_t vi = (i / 4) * kConfThreads + t;
+      if (vi >= nvalid / EPV) w[i] = BF16 ? 0xFF80FF80u : 0xFF800000u;
+    } else if (BF16) {
+      const int32_t e0 = 2 * i * kConfThreads + t, e1 = e0 + kConfThreads;
+      if (e0 >= nvalid) w[i] = (w[i] & 0xFFFF0000u) | 0xFF80u;
+      if (e1 >= nvalid) w[i] = (w[i] & 0x0000FFFFu) | 0xFF800000u;
+    } else {
+      if (i * kConfThreads + t >= nvalid) w[i] = 0xFF800000u;
+    }
+  }
+}
+
+// Reduce one chunk held in w and write its result.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uint32_t (&w)[kConfWords],
+                                            ConfShared &sh) {
+  constexpr int PER = conf_per<BF16>();
+  {
+    const int32_t nvalid = conf_nvalid<BF16>(a, cidx);
+    if (nvalid < conf_chunk<BF16>()) conf_mask<BF16, VEC>(nvalid, w);   // uniform branch
+  }
+  const float NEG = -__builtin_inff();
+  const int t = opaque_tid(), lane = t & 63, wave = t >> 6;
+  const int k = a.k;
+  if (t == 0) sh.ncand = 0;
+
+  // ---- per-thread maximum (three-input max over unpacked pairs) ----
+  fence_words(w);
+  float tmax = NEG;
+#pragma unroll
+  for (int i = 0; i < PER; i += 2) {
+    tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(logit<BF16>(w, i), logit<BF16>(w, i + 1)));
+    if ((i & 7) == 6) __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t tkey = fkey(tmax);
+  // ---- sort the wave's 64 thread maxima, descending (bitonic, in registers) ----
+  uint32_t v = tkey;
+  auto cx = [&](uint32_t o, int size, int j) {
+    const bool desc_block = (lane & size) == 0;     // blocks alternate; the last is whole
+    const bool lower = (lane & j) == 0;
+    v = (desc_block == lower) ? max(v, o) : min(v, o);
+  };
+  cx(xshfl<1>(v), 2, 1);
+  cx(xshfl<2>(v), 4, 2);
+  cx(xshfl<1>(v), 4, 1);
+  cx(xshfl<4>(v), 8, 4);
+  cx(xshfl<2>(v), 8, 2);
+  cx(xshfl<1>(v), 8, 1);
+  cx(xshfl<8>(v), 16, 8);
+  cx(xshfl<4>(v), 16, 4);
+  cx(xshfl<2>(v), 16, 2);
+  cx(xshfl<1>(v), 16, 1);
+  cx(xshfl<16>(v), 32, 16);
+  cx(xshfl<8>(v), 32, 8);
+  cx(xshfl<4>(v), 32, 4);
+  cx(xshfl<2>(v), 32, 2);
+  cx(xshfl<1>(v), 32, 1);
+  cx(xshfl<32>(v), 64, 32);
+  cx(xshfl<16>(v), 64, 16);
+  cx(xshfl<8>(v), 64, 8);
+  cx(xshfl<4>(v), 64, 4);
+  cx(xshfl<2>(v), 64, 2);
+  cx(xshfl<1>(v), 64, 1);
+  sh.sorted[wave][lane] = v;
+  // ---- per-thread sum of exp(z - tmax) (one FMA per logit: c = tmax log2 e is rounded
+  // once, which scales every term of this thread by the same factor, within
+  // 2^-24 |tmax| log2 e of 1), overlapping the barrier wait ----
+  fence_words(w);
+  float tsum = 0.f;
+  if (tmax != NEG) {
+    const float c = tmax * kLog2e;
+    auto term = [&](int i) { return __builtin_amdgcn_exp2f(__builtin_fmaf(logit<BF16>(w, i), kLog2e, -c)); };
+    float t0 = term(0), t1 = term(1), t2 = term(2), t3 = term(3);
+#pragma unroll
+    for (int i = 4; i < PER; i += 4) {
+      t0 += term(i);
+      t1 += term(i + 1);
+      t2 += term(i + 2);
+      t3 += term(i + 3);
+      if ((i & 7) == 4) __builtin_amdgcn_sched_barrier(0);
+    }
+    tsum = (t0 + t1) + (t2 + t3);
+  }
+  lds_barrier();
+
+  // ---- M, each wave's sum rescaled to M; M_k = the key of rank k among the maxima ----
+  uint32_t mkey = 0;
+#pragma unroll
+  for (int q = 0; q < kConfWaves; ++q) mkey = max(mkey, sh.sorted[q][0]);
+  const float M = key_f(mkey);
+  {
+    const float r = tmax != NEG ? tsum * __builtin_amdgcn_exp2f((tmax - M) * kLog2e) : 0.f;
+    const float ws = wave_sum_dpp_f32(r);
+    if (lane == 63) sh.ws[wave] = ws;
+  }
+  if (t < kConfWaves * k) {
+    // order: key descending, then list, then position in the list; only the first k
+    // of a list can rank below k, so only those are compared
+    const int lw = t / k, p = t - lw * k;
+    const uint32_t key = sh.sorted[lw][p];
+    int rank = p;
+    for (int q = 0; q < kConfWaves; ++q) {
+      if (q == lw) continue;
+      const uint32_t *lq = sh.sorted[q];
+      const bool ge = q < lw;
+      for (int j = 0; j < k; j += 4) {
+        const uint4 x4 = *(const uint4 *)(lq + j);
+        const uint32_t xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rank += (j + e < k && (xs[e] > key || (ge && xs[e] == key))) ? 1 : 0;
+      }
+    }
+    if (rank == k - 1) sh.mk = key;
+  }
+  lds_barrier();
+  const uint32_t mk = sh.mk;
+
+  // ---- values above M_k (at most (k-1) * PER of them) appended to the LDS list;
+  // only the at most k-1 threads whose maximum is above M_k hold any ----
+  fence_words(w);
+  if (tkey > mk) {
+    // one pass, one LDS atomic per value appended (a few per such thread)
+    const float fmk = key_f(mk);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float x = logit<BF16>(w, i);
+      if (x > fmk || (x == fmk && fkey(x) > mk)) sh.cand[atomicAdd(&sh.ncand, 1u)] = fkey(x);
+      if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  lds_barrier();
+  // the list's order depends on atomic order; ranks break ties by position, so the
+  // chosen values (and their sum) do not.  Reads take 4 entries at a time (the list
+  // capacity is a multiple of 4; entries past nc are masked).
+  // The chunk's k largest are written in descending order: every candidate is ranked
+  // (ranks below k land in topv[rank]); with fewer than k candidates the rest are
+  // copies of M_k, which is below all of them.
+  const int nc = (int)sh.ncand;
+  {
+    for (int i = t; i < nc; i += kConfThreads) {
+      const uint32_t ki = sh.cand[i];
+      int rank = 0;
+      for (int j = 0; j < nc; j += 4) {
+        const uint4 c4 = *(const uint4 *)(sh.cand + j);
+        const uint32_t cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kj = cs[e];
+          rank += (j + e < nc && (kj > ki || (kj == ki && j + e < i))) ? 1 : 0;
+        }
+      }
+      if (rank < k) sh.topv[rank] = key_f(ki);
+    }
+    if (t >= nc && t < k) sh.topv[t] = key_f(mk);
+  }
+  lds_barrier();
+
+  // ---- result (wave 0) ----
+  if (wave == 0) {
+    float S = 0.f;
+#pragma unroll
+    for (int q = 0; q < kConfWaves; ++q) S += sh.ws[q];
+    const float tv = lane < k ? sh.topv[lane] : 0.f;
+    if (a.chunks == 1) {
+      const float d = wave_sum_f32(lane < k ? M - tv : 0.f);
+      if (lane == 0) a.conf[cidx] = __builtin_amdgcn_logf(S) * kLn2 + d / (float)k;
+    } else {
+      float *p = a.part + cidx * (int64_t)(2 + k);
+      if (lane == 0) {
+        p[0] = M;
+        p[1] = S;
+      }
+      if (lane < k) p[2 + lane] = tv;
+    }
+  }
+}
+
+// One chunk per workgroup.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kConfThreads, kConfWavesPerSimd) void conf_chunk_kernel(ConfArgs a) {
+  __shared__ ConfShared sh;
+  const int64_t c = blockIdx.x;
+  if (c >= a.total) return;
+  uint32_t w[kConfWords];
+  conf_load<BF16, VEC>(a, c, w);
+  conf_reduce<BF16, VEC>(a, c, w, sh);
 }
 
 // Block sum of a float in wave order (deterministic).  scratch: one float per wave.
@@ -80,191 +407,55 @@ __device__ __forceinline__ float block_sum_f32(float x, float *scratch) {
   return t;
 }
 
-// The key of rank `need` (1 = largest) among one key per thread: radix search, 8 bits
-// per pass, over a 256-bin LDS histogram.  Every thread must call it.
-__device__ __forceinline__ uint32_t block_kth_key(uint32_t key, int need, uint32_t *hist, uint32_t *bcast) {
-  uint32_t prefix = 0, mask = 0;
-  const int lane = threadIdx.x & 63;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = threadIdx.x; b < 256; b += blockDim.x) hist[b] = 0;
-    __syncthreads();
-    if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l owns bins 4l .. 4l+3; count strictly above them, from the top
-      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                     c3 = hist[4 * lane + 3];
-      const uint32_t mine = c0 + c1 + c2 + c3;
-      const uint32_t incl = wave_scan_u32(mine);
-      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-      const uint32_t above = total - incl;       // keys in bins above lane l's four
-      if (above < (uint32_t)need && (uint32_t)need <= above + mine) {
-        uint32_t cum = above;
-        int d = 4 * lane + 3;
-        const uint32_t c[4] = {c0, c1, c2, c3};
-        for (int b = 3; b >= 0; --b) {
-          if (cum + c[b] >= (uint32_t)need) { d = 4 * lane + b; break; }
-          cum += c[b];
-        }
-        bcast[0] = (uint32_t)d;
-        bcast[1] = cum;
-      }
-    }
-    __syncthreads();
-    prefix |= bcast[0] << shift;
-    mask |= 255u << shift;
-    need -= (int)bcast[1];
-    __syncthreads();
-  }
-  return prefix;
+// Wave maximum of a u32, uniform result (DPP row shifts and broadcasts).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr2, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr4, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr8, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-// One (row, chunk) per workgroup.  BF16: logits are bf16, else fp32.  VEC: rows are
-// 16-byte aligned, so whole 16-byte vectors are loaded where they lie inside the row.
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kConfThreads) void conf_chunk_kernel(ConfArgs a) {
-  __shared__ float red[kConfWaves];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[2];
-  __shared__ uint32_t ncand;
-  __shared__ uint32_t cand[kCandCap];
-  __shared__ float topv[kConfMaxK];
+constexpr int kMergeChunks = 64;   // chunks per row the one-wave merge takes
 
-  const int64_t blk = blockIdx.x;
-  const int64_t row = blk / a.chunks;
-  const int32_t chunk = (int32_t)(blk - row * a.chunks);
+// Merge the chunks of one row with one wave (rows of at most 64 chunks).  Each chunk's
+// k values are stored in descending order, so the row's k largest are taken by k
+// rounds of "largest current head": lane c holds the head of chunk c's list, the wave
+// maximum picks the next value, and the lowest lane holding it advances.
+__global__ __launch_bounds__(64) void conf_merge_kernel(ConfArgs a) {
+  __shared__ float L[kMergeChunks * (2 + kConfMaxK)];
+  const int64_t row = blockIdx.x;
   if (row >= a.rows) return;
-  const int t = threadIdx.x;
-  const int64_t c0 = (int64_t)chunk * kConfChunk;     // first logit of the chunk
-  const int64_t rem = a.vocab - c0;                     // logits left in the row
-  const int64_t nvalid = rem < kConfChunk ? rem : kConfChunk;
-  const float NEG = -__builtin_inff();
-
-  // ---- load 64 logits per thread; positions past the row end are -inf ----
-  float x[kConfPer];
-  if (BF16) {
-    const uint16_t *src = (const uint16_t *)a.logits + row * a.stride + c0;
-    if (VEC) {
-      // vector u (of 8 logits) of thread t starts at logit (u * 512 + t) * 8
-#pragma unroll
-      for (int u = 0; u < kConfPer / 8; ++u) {
-        const int64_t e = ((int64_t)u * kConfThreads + t) * 8;
-        if (e + 8 <= nvalid) {
-          const uint4 v = *(const uint4 *)(src + e);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            x[u * 8 + 2 * q] = __uint_as_float(w[q] << 16);
-            x[u * 8 + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) x[u * 8 + q] = (e + q < nvalid) ? bf16_f(src[e + q]) : NEG;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kConfPer; ++u) {
-        const int64_t e = (int64_t)u * kConfThreads + t;
-        x[u] = e < nvalid ? bf16_f(src[e]) : NEG;
-      }
-    }
-  } else {
-    const float *src = (const float *)a.logits + row * a.stride + c0;
-    if (VEC) {
-#pragma unroll
-      for (int u = 0; u < kConfPer / 4; ++u) {
-        const int64_t e = ((int64_t)u * kConfThreads + t) * 4;
-        if (e + 4 <= nvalid) {
-          const float4 v = *(const float4 *)(src + e);
-          x[u * 4] = v.x;
-          x[u * 4 + 1] = v.y;
-          x[u * 4 + 2] = v.z;
-          x[u * 4 + 3] = v.w;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) x[u * 4 + q] = (e + q < nvalid) ? src[e + q] : NEG;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kConfPer; ++u) {
-        const int64_t e = (int64_t)u * kConfThreads + t;
-        x[u] = e < nvalid ? src[e] : NEG;
-      }
+  const int lane = threadIdx.x;
+  const int k = a.k, C = a.chunks;
+  const int w = 2 + k;
+  const float *p = a.part + row * (int64_t)C * w;
+  for (int i = lane; i < C * w; i += 64) L[i] = p[i];
+  __builtin_amdgcn_s_waitcnt(0);     // the wave's own LDS writes, before its reads
+  const bool live = lane < C;
+  const float mc = live ? L[lane * w] : -__builtin_inff();
+  const float M = key_f(wave_max_u32(fkey(mc)));
+  const float sc = (live && mc != -__builtin_inff()) ? L[lane * w + 1] * __builtin_amdgcn_exp2f((mc - M) * kLog2e) : 0.f;
+  const float S = wave_sum_f32(sc);
+  int h = 0;
+  uint32_t head = live ? fkey(L[lane * w + 2]) : 0u;
+  float d = 0.f;
+  for (int r = 0; r < k; ++r) {
+    const uint32_t mx = wave_max_u32(head);
+    const uint64_t hit = __ballot(head == mx);
+    const int winner = __ffsll((long long)hit) - 1;
+    d += M - key_f(mx);
+    if (lane == winner) {
+      ++h;
+      head = h < k ? fkey(L[lane * w + 2 + h]) : 0u;
     }
   }
-
-  // ---- maximum and sum of exp(z - M) ----
-  float tmax = NEG;
-#pragma unroll
-  for (int u = 0; u < kConfPer; ++u) tmax = fmaxf(tmax, x[u]);
-  // exp(z - tmax) as 2^((z - tmax) log2 e): the difference first, so that the rounding
-  // of the exponent scales with |z - tmax| and not with |z|
-  float tsum = 0.f;
-  if (tmax != NEG) {
-#pragma unroll
-    for (int u = 0; u < kConfPer; ++u) tsum += __builtin_amdgcn_exp2f((x[u] - tmax) * kLog2e);
-  }
-  const uint32_t tkey = fkey(tmax);
-  const float M = key_f(block_max_u32(tkey, (uint32_t *)red));
-  const float S = block_sum_f32(tmax != NEG ? tsum * __builtin_amdgcn_exp2f((tmax - M) * kLog2e) : 0.f, red);
-
-  // ---- the chunk's k largest values ----
-  const int k = a.k;
-  const uint32_t mk = block_kth_key(tkey, k, hist, bcast);
-  if (t == 0) ncand = 0;
-  __syncthreads();
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int u = 0; u < kConfPer; ++u) cnt += fkey(x[u]) > mk ? 1u : 0u;
-  const uint32_t incl = wave_scan_u32(cnt);
-  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  uint32_t base = 0;
-  if ((t & 63) == 63 && wtot) base = atomicAdd(&ncand, wtot);
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
-  if (cnt) {
-    uint32_t pos = base + incl - cnt;
-#pragma unroll
-    for (int u = 0; u < kConfPer; ++u) {
-      const uint32_t kx = fkey(x[u]);
-      if (kx > mk) cand[pos++] = kx;      // pos < kCandCap: see the bound above
-    }
-  }
-  __syncthreads();
-  const int nc = (int)ncand;
-  if (nc >= k) {
-    // rank each candidate: larger keys first, then lower position
-    for (int i = t; i < nc; i += kConfThreads) {
-      const uint32_t ki = cand[i];
-      int rank = 0;
-      for (int j = 0; j < nc; ++j) {
-        const uint32_t kj = cand[j];
-        rank += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
-      }
-      if (rank < k) topv[rank] = key_f(ki);
-    }
-  } else {
-    for (int i = t; i < k; i += kConfThreads) topv[i] = i < nc ? key_f(cand[i]) : key_f(mk);
-  }
-  __syncthreads();
-
-  if (a.chunks == 1) {
-    if (t < 64) {
-      const float d = wave_sum_f32(t < k ? M - topv[t] : 0.f);
-      if (t == 0) a.conf[row] = __builtin_amdgcn_logf(S) * kLn2 + d / (float)k;
-    }
-  } else {
-    float *p = a.part + (row * a.chunks + chunk) * (int64_t)(2 + k);
-    if (t == 0) {
-      p[0] = M;
-      p[1] = S;
-    }
-    if (t < k) p[2 + t] = topv[t];
-  }
+  if (lane == 0) a.conf[row] = __builtin_amdgcn_logf(S) * kLn2 + d / (float)k;
 }
 
-// Merge the chunks of one row (one workgroup per row).
+// Merge the chunks of one row (one workgroup per row; rows of more than 64 chunks).
 __global__ __launch_bounds__(kCombineThreads) void conf_combine_kernel(ConfArgs a) {
   __shared__ float red[kCombineThreads / 64];
   __shared__ float topv[kConfMaxK];
@@ -308,13 +499,17 @@ __global__ __launch_bounds__(kCombineThreads) void conf_combine_kernel(ConfArgs 
 
 }  // namespace
 
-int64_t conf_max_vocab() { return (int64_t)kConfMaxChunks * kConfChunk; }
+int64_t conf_max_vocab() { return (int64_t)1 << 20; }
 int32_t conf_max_k() { return kConfMaxK; }
 
-int32_t conf_chunks(int64_t vocab) { return (int32_t)((vocab + kConfChunk - 1) / kConfChunk); }
+int32_t conf_chunks(int64_t vocab, bool bf16) {
+  const int64_t ch = bf16 ? conf_chunk<true>() : conf_chunk<false>();
+  return (int32_t)((vocab + ch - 1) / ch);
+}
 
+// The workspace is sized for fp32 rows (the smaller chunk), which covers bf16 too.
 size_t conf_workspace_bytes(int64_t rows, int64_t vocab, int32_t k) {
-  const int32_t C = conf_chunks(vocab);
+  const int32_t C = conf_chunks(vocab, false);
   if (C <= 1) return 0;
   return (size_t)rows * C * (2 + k) * sizeof(float);
 }
@@ -327,20 +522,23 @@ hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_
   a.vocab = vocab;
   a.stride = stride;
   a.k = k;
-  a.chunks = conf_chunks(vocab);
+  a.chunks = conf_chunks(vocab, bf16);
+  a.total = rows * a.chunks;
   a.conf = conf;
   a.part = (float *)ws;
   const size_t es = bf16 ? 2 : 4;
-  const bool vec = ((uintptr_t)logits % 16 == 0) && ((size_t)stride * es) % 16 == 0;
-  const unsigned blocks = (unsigned)(rows * a.chunks);
+  const bool vec = ((uintptr_t)logits % 16 == 0) && ((size_t)stride * es) % 16 == 0 &&
+                   ((size_t)vocab * es) % 16 == 0;
+  const unsigned grid = (unsigned)a.total;
   if (bf16) {
-    if (vec) conf_chunk_kernel<true, true><<<blocks, kConfThreads, 0, st>>>(a);
-    else conf_chunk_kernel<true, false><<<blocks, kConfThreads, 0, st>>>(a);
+    if (vec) conf_chunk_kernel<true, true><<<grid, kConfThreads, 0, st>>>(a);
+    else conf_chunk_kernel<true, false><<<grid, kConfThreads, 0, st>>>(a);
   } else {
-    if (vec) conf_chunk_kernel<false, true><<<blocks, kConfThreads, 0, st>>>(a);
-    else conf_chunk_kernel<false, false><<<blocks, kConfThreads, 0, st>>>(a);
+    if (vec) conf_chunk_kernel<false, true><<<grid, kConfThreads, 0, st>>>(a);
+    else conf_chunk_kernel<false, false><<<grid, kConfThreads, 0, st>>>(a);
   }
-  if (a.chunks > 1) conf_combine_kernel<<<(unsigned)rows, kCombineThreads, 0, st>>>(a);
+  if (a.chunks > kMergeChunks) conf_combine_kernel<<<(unsigned)rows, kCombineThreads, 0, st>>>(a);
+  else if (a.chunks > 1) conf_merge_kernel<<<(unsigned)rows, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

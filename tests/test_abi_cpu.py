@@ -206,10 +206,11 @@ def test_token_confidence_validation():
     assert call(logits=None) == 1 and call(conf=None) == 1
     assert call(ws=None) == 4 and call(ws_bytes=16) == 4
     assert call(rows=0) == 0                         # nothing to do: no launch
+    # sized for fp32 rows: chunks of 8 192 logits, (2 + k) floats per (row, chunk)
     need = L.kvs_token_confidence_workspace_size(4, 128256, 20)
-    assert need == 4 * 4 * (2 + 20) * 4              # 4 chunks of 32 768 logits per row
-    assert L.kvs_token_confidence_workspace_size(4, 32768, 20) == 0
-    assert L.kvs_token_confidence_workspace_size(4, 32769, 64) == 4 * 2 * 66 * 4
+    assert need == 4 * 16 * (2 + 20) * 4
+    assert L.kvs_token_confidence_workspace_size(4, 8192, 20) == 0
+    assert L.kvs_token_confidence_workspace_size(4, 8193, 64) == 4 * 2 * 66 * 4
 
 
 @pytest.mark.parametrize("n", [0, 1, 63, 64, 71, 72, 200, 4096])

@@ -85,11 +85,13 @@ def test_confidence_strided_and_unaligned(dtype):
     _ = torch
 
 
-def test_confidence_largest_vocabulary():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_confidence_largest_vocabulary(dtype):
+    # 2^20 logits: 64 bf16 chunks (one-wave merge) or 128 fp32 chunks (ranked merge)
     V = 1 << 20
-    z = np.concatenate([LG.lm_rows(11, 2, V), LG.special_rows(12, V)[[0, 3, 4]]])
-    print("confidence V=2^20", flush=True)
-    x, exact = device_rows(z, "bf16")
+    z = np.concatenate([LG.lm_rows(11, 2, V), LG.special_rows(12, V)[[0, 1, 3, 4]]])
+    print(f"confidence V=2^20 {dtype}", flush=True)
+    x, exact = device_rows(z, dtype)
     check(gpu_conf(x, 64), exact, 64, "2^20")
     check(gpu_conf(x, 20), exact, 20, "2^20")
 
