@@ -292,9 +292,10 @@ enum { KVS_DTYPE_F32 = 0, KVS_DTYPE_BF16 = 1 };
 
 /*
  * Bytes of device workspace kvs_token_confidence needs: (2 + k) fp32 partial
- * results per (row, chunk of 8 192 logits) when vocab > 8 192, else 0 (sized for
- * fp32 logits; bf16 rows use chunks of 16 384 and need at most this).  Returns 0
- * (and sets kvs_last_error()) on invalid arguments.
+ * results per (row, chunk), chunks of 16 384 logits for k <= 32 and of 8 192 above;
+ * 0 when a row is one chunk.  Sized for fp32 logits (bf16 chunks are twice as long,
+ * so bf16 rows need at most this).  Returns 0 (and sets kvs_last_error()) on invalid
+ * arguments.
  */
 size_t kvs_token_confidence_workspace_size(int64_t rows, int64_t vocab, int32_t k);
 

@@ -395,7 +395,7 @@ kvs_status check_confidence(int32_t dtype, int64_t rows, int64_t vocab, int64_t 
   if (k < 1 || k > kvs::conf_max_k()) return fail(KVS_ERR_UNSUPPORTED, "k %d not in [1, %d]", k, kvs::conf_max_k());
   if (k > vocab) return fail(KVS_ERR_SHAPE, "k %d > vocab %lld", k, (long long)vocab);
   if (row_stride < vocab) return fail(KVS_ERR_SHAPE, "row_stride %lld < vocab", (long long)row_stride);
-  if (rows * (int64_t)kvs::conf_chunks(vocab, false) > ((int64_t)1 << 40))
+  if (rows * (int64_t)kvs::conf_chunks(vocab, false, k) > ((int64_t)1 << 40))
     return fail(KVS_ERR_UNSUPPORTED, "rows x chunks exceeds the grid limit");
   return KVS_OK;
 }

@@ -7,9 +7,10 @@
 //     conf = (1/k) sum_{j in T} -ln p_j = LSE(z) - mean_{j in T} z_j
 //          = ln S + (1/k) sum_{j in T} (M - z_j),   M = max z,  S = sum_j exp(z_j - M).
 //
-// Rows are cut into chunks of 32 KiB of logits (16 384 bf16 or 8 192 fp32), one per
-// 256-thread workgroup, held in 32 VGPRs per thread; workgroups are small so that
-// six of them share a CU and one's barriers overlap the others' loads.  Per chunk:
+// Rows are cut into chunks of 64 KiB of logits (32 768 bf16 or 16 384 fp32) when
+// k <= 32, else 32 KiB, one per 256-thread workgroup, held in 64 (32) VGPRs per
+// thread; workgroups are small so that several share a CU and one's barriers overlap
+// the others' loads.  Per chunk:
 //   * the maximum M and S = sum exp(z - M): per-thread maxima and sums, the sums
 //     rescaled to M and added over the block;
 //   * the k-th largest of the 256 per-thread maxima, M_k: each wave sorts its 64
@@ -17,7 +18,8 @@
 //     ranked against the first k of the other lists; the one of rank k is M_k;
 //   * at least k values are >= M_k (one per thread whose maximum is >= M_k), and
 //     values > M_k only occur in the at most k-1 threads whose maximum is > M_k,
-//     so at most (k-1)*64 of them exist: they are appended to an LDS list;
+//     so at most (k-1) x (logits per thread) <= 4 032 of them exist: they are
+//     appended to an LDS list;
 //   * if there are k or more, each is ranked among them (value, then position);
 //     otherwise the rest of the top k are copies of M_k.
 // A second kernel merges the chunks of a row: M = max M_c, S = sum S_c exp(M_c - M),
@@ -30,7 +32,9 @@ namespace {
 
 constexpr int kConfThreads = 256;
 constexpr int kConfWaves = kConfThreads / 64;
-constexpr int kConfWords = 32;                               // u32 of logits per thread and buffer
+// Words (u32) of logits per thread: 64 while k <= 32, else 32 (the candidate list of a
+// chunk, at most (k-1) x logits per thread, then still fits its 4 032 entries).
+constexpr int kConfWordsSmallK = 64, kConfWordsLargeK = 32, kConfSmallK = 32;
 constexpr int kConfMaxK = 64;
 constexpr int kCandCap = (kConfMaxK - 1) * 64;               // values above M_k, at most
 constexpr int kCombineThreads = 256;
@@ -39,8 +43,8 @@ constexpr int kConfWavesPerSimd = 6;                         // occupancy the ke
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool BF16> constexpr int conf_per() { return BF16 ? 64 : 32; }     // logits per thread
-template <bool BF16> constexpr int conf_chunk() { return kConfThreads * conf_per<BF16>(); }
+template <bool BF16, int W> constexpr int conf_per() { return BF16 ? 2 * W : W; }   // logits per thread
+template <bool BF16, int W> constexpr int conf_chunk() { return kConfThreads * conf_per<BF16, W>(); }
 
 struct ConfArgs {
   const void *logits;
@@ -129,8 +133,8 @@ __device__ __forceinline__ int opaque_tid() {
 }
 
 // Logit i of this thread from a buffer of 32 words (bf16 pairs or fp32).
-template <bool BF16>
-__device__ __forceinline__ float logit(const uint32_t (&w)[kConfWords], int i) {
+template <bool BF16, int W>
+__device__ __forceinline__ float logit(const uint32_t (&w)[W], int i) {
   const uint32_t x = w[BF16 ? (i >> 1) : i];
   if (BF16) return __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
   return __uint_as_float(x);
@@ -139,15 +143,16 @@ __device__ __forceinline__ float logit(const uint32_t (&w)[kConfWords], int i) {
 // The buffer's words pass through an empty asm (in place, no instructions), so that
 // each pass over the buffer unpacks it again instead of keeping 64 unpacked values
 // (and their keys) live from one pass to the next.
-__device__ __forceinline__ void fence_words(uint32_t (&w)[kConfWords]) {
+template <int W>
+__device__ __forceinline__ void fence_words(uint32_t (&w)[W]) {
 #pragma unroll
-  for (int i = 0; i < kConfWords; ++i) asm volatile("" : "+v"(w[i]));
+  for (int i = 0; i < W; ++i) asm volatile("" : "+v"(w[i]));
 }
 
 // Number of valid logits in chunk cidx (>= 1; < chunk size only in a row's last chunk).
-template <bool BF16>
+template <bool BF16, int W>
 __device__ __forceinline__ int32_t conf_nvalid(const ConfArgs &a, int64_t cidx) {
-  constexpr int CH = conf_chunk<BF16>();
+  constexpr int CH = conf_chunk<BF16, W>();
   const int64_t row = cidx / a.chunks;
   const int64_t rem = a.vocab - (cidx - row * a.chunks) * CH;
   return (int32_t)(rem < CH ? rem : CH);
@@ -157,22 +162,22 @@ __device__ __forceinline__ int32_t conf_nvalid(const ConfArgs &a, int64_t cidx) 
 // at an index clamped into the chunk's valid range, so no load depends on a branch and
 // nothing here waits on the data; conf_mask replaces the out-of-range positions.
 // VEC (rows 16-byte aligned and the vocabulary a multiple of the vector width):
-// 16-byte vector u of thread t holds logits (u * 512 + t) * per-vector, and whole
-// vectors are either valid or not.  Otherwise word i holds logits (2i * 512 + t) and
-// (2i+1) * 512 + t (bf16), or logit i * 512 + t (fp32).
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint32_t (&w)[kConfWords]) {
-  constexpr int CH = conf_chunk<BF16>();
+// 16-byte vector u of thread t holds logits (u * T + t) * per-vector, T the workgroup
+// size, and whole vectors are either valid or not.  Otherwise word i holds logits
+// 2i * T + t and (2i+1) * T + t (bf16), or logit i * T + t (fp32).
+template <bool BF16, bool VEC, int W>
+__device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint32_t (&w)[W]) {
+  constexpr int CH = conf_chunk<BF16, W>();
   const int t = opaque_tid();
   const int64_t row = cidx / a.chunks;
   const int64_t c0 = (cidx - row * a.chunks) * CH;
-  const int32_t nvalid = conf_nvalid<BF16>(a, cidx);
+  const int32_t nvalid = conf_nvalid<BF16, W>(a, cidx);
   if (VEC) {
     constexpr int EPV = BF16 ? 8 : 4;                           // logits per vector
     const uint4 *src = (const uint4 *)((const uint8_t *)a.logits + (row * a.stride + c0) * (BF16 ? 2 : 4));
     const int32_t last = nvalid / EPV - 1;                        // vocab % EPV == 0
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < W / 4; ++u) {
       const int32_t vi = u * kConfThreads + t;
       const uint4 v = src[vi < last ? vi : last];
       w[4 * u] = v.x;
@@ -183,7 +188,7 @@ __device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint3
   } else if (BF16) {
     const uint16_t *src = (const uint16_t *)a.logits + row * a.stride + c0;
 #pragma unroll
-    for (int i = 0; i < kConfWords; ++i) {
+    for (int i = 0; i < W; ++i) {
       const int32_t e0 = 2 * i * kConfThreads + t, e1 = e0 + kConfThreads;
       const uint32_t lo = src[e0 < nvalid ? e0 : nvalid - 1], hi = src[e1 < nvalid ? e1 : nvalid - 1];
       w[i] = lo | (hi << 16);
@@ -191,7 +196,7 @@ __device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint3
   } else {
     const uint32_t *src = (const uint32_t *)a.logits + row * a.stride + c0;
 #pragma unroll
-    for (int i = 0; i < kConfWords; ++i) {
+    for (int i = 0; i < W; ++i) {
       const int32_t e = i * kConfThreads + t;
       w[i] = src[e < nvalid ? e : nvalid - 1];
     }
@@ -199,11 +204,11 @@ __device__ __forceinline__ void conf_load(const ConfArgs &a, int64_t cidx, uint3
 }
 
 // Set the positions of a partial chunk that lie past the row end to -inf.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void conf_mask(int32_t nvalid, uint32_t (&w)[kConfWords]) {
+template <bool BF16, bool VEC, int W>
+__device__ __forceinline__ void conf_mask(int32_t nvalid, uint32_t (&w)[W]) {
   const int t = opaque_tid();
 #pragma unroll
-  for (int i = 0; i < kConfWords; ++i) {
+  for (int i = 0; i < W; ++i) {
     if (VEC) {
       constexpr int EPV = BF16 ? 8 : 4;
       const int32_t vi = (i / 4) * kConfThreads + t;
@@ -219,13 +224,13 @@ __device__ __forceinline__ void conf_mask(int32_t nvalid, uint32_t (&w)[kConfWor
 }
 
 // Reduce one chunk held in w and write its result.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uint32_t (&w)[kConfWords],
+template <bool BF16, bool VEC, int W>
+__device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uint32_t (&w)[W],
                                             ConfShared &sh) {
-  constexpr int PER = conf_per<BF16>();
+  constexpr int PER = conf_per<BF16, W>();
   {
-    const int32_t nvalid = conf_nvalid<BF16>(a, cidx);
-    if (nvalid < conf_chunk<BF16>()) conf_mask<BF16, VEC>(nvalid, w);   // uniform branch
+    const int32_t nvalid = conf_nvalid<BF16, W>(a, cidx);
+    if (nvalid < conf_chunk<BF16, W>()) conf_mask<BF16, VEC, W>(nvalid, w);   // uniform branch
   }
   const float NEG = -__builtin_inff();
   const int t = opaque_tid(), lane = t & 63, wave = t >> 6;
@@ -237,7 +242,7 @@ __device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uin
   float tmax = NEG;
 #pragma unroll
   for (int i = 0; i < PER; i += 2) {
-    tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(logit<BF16>(w, i), logit<BF16>(w, i + 1)));
+    tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(logit<BF16, W>(w, i), logit<BF16, W>(w, i + 1)));
     if ((i & 7) == 6) __builtin_amdgcn_sched_barrier(0);
   }
   const uint32_t tkey = fkey(tmax);
@@ -277,7 +282,7 @@ __device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uin
   float tsum = 0.f;
   if (tmax != NEG) {
     const float c = tmax * kLog2e;
-    auto term = [&](int i) { return __builtin_amdgcn_exp2f(__builtin_fmaf(logit<BF16>(w, i), kLog2e, -c)); };
+    auto term = [&](int i) { return __builtin_amdgcn_exp2f(__builtin_fmaf(logit<BF16, W>(w, i), kLog2e, -c)); };
     float t0 = term(0), t1 = term(1), t2 = term(2), t3 = term(3);
 #pragma unroll
     for (int i = 4; i < PER; i += 4) {
@@ -332,7 +337,7 @@ __device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uin
     const float fmk = key_f(mk);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const float x = logit<BF16>(w, i);
+      const float x = logit<BF16, W>(w, i);
       if (x > fmk || (x == fmk && fkey(x) > mk)) sh.cand[atomicAdd(&sh.ncand, 1u)] = fkey(x);
       if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -385,14 +390,14 @@ __device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uin
 }
 
 // One chunk per workgroup.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int W>
 __global__ __launch_bounds__(kConfThreads, kConfWavesPerSimd) void conf_chunk_kernel(ConfArgs a) {
   __shared__ ConfShared sh;
   const int64_t c = blockIdx.x;
   if (c >= a.total) return;
-  uint32_t w[kConfWords];
-  conf_load<BF16, VEC>(a, c, w);
-  conf_reduce<BF16, VEC>(a, c, w, sh);
+  uint32_t w[W];
+  conf_load<BF16, VEC, W>(a, c, w);
+  conf_reduce<BF16, VEC, W>(a, c, w, sh);
 }
 
 // Block sum of a float in wave order (deterministic).  scratch: one float per wave.
@@ -502,14 +507,16 @@ __global__ __launch_bounds__(kCombineThreads) void conf_combine_kernel(ConfArgs 
 int64_t conf_max_vocab() { return (int64_t)1 << 20; }
 int32_t conf_max_k() { return kConfMaxK; }
 
-int32_t conf_chunks(int64_t vocab, bool bf16) {
-  const int64_t ch = bf16 ? conf_chunk<true>() : conf_chunk<false>();
+int32_t conf_chunks(int64_t vocab, bool bf16, int32_t k) {
+  const bool small = k <= kConfSmallK;
+  const int64_t ch = bf16 ? (small ? conf_chunk<true, kConfWordsSmallK>() : conf_chunk<true, kConfWordsLargeK>())
+                          : (small ? conf_chunk<false, kConfWordsSmallK>() : conf_chunk<false, kConfWordsLargeK>());
   return (int32_t)((vocab + ch - 1) / ch);
 }
 
 // The workspace is sized for fp32 rows (the smaller chunk), which covers bf16 too.
 size_t conf_workspace_bytes(int64_t rows, int64_t vocab, int32_t k) {
-  const int32_t C = conf_chunks(vocab, false);
+  const int32_t C = conf_chunks(vocab, false, k);
   if (C <= 1) return 0;
   return (size_t)rows * C * (2 + k) * sizeof(float);
 }
@@ -522,7 +529,7 @@ hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_
   a.vocab = vocab;
   a.stride = stride;
   a.k = k;
-  a.chunks = conf_chunks(vocab, bf16);
+  a.chunks = conf_chunks(vocab, bf16, k);
   a.total = rows * a.chunks;
   a.conf = conf;
   a.part = (float *)ws;
@@ -530,12 +537,24 @@ hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_
   const bool vec = ((uintptr_t)logits % 16 == 0) && ((size_t)stride * es) % 16 == 0 &&
                    ((size_t)vocab * es) % 16 == 0;
   const unsigned grid = (unsigned)a.total;
+  const bool small = k <= kConfSmallK;
+  constexpr int WS = kConfWordsSmallK, WL = kConfWordsLargeK;
   if (bf16) {
-    if (vec) conf_chunk_kernel<true, true><<<grid, kConfThreads, 0, st>>>(a);
-    else conf_chunk_kernel<true, false><<<grid, kConfThreads, 0, st>>>(a);
+    if (vec) {
+      if (small) conf_chunk_kernel<true, true, WS><<<grid, kConfThreads, 0, st>>>(a);
+      else conf_chunk_kernel<true, true, WL><<<grid, kConfThreads, 0, st>>>(a);
+    } else {
+      if (small) conf_chunk_kernel<true, false, WS><<<grid, kConfThreads, 0, st>>>(a);
+      else conf_chunk_kernel<true, false, WL><<<grid, kConfThreads, 0, st>>>(a);
+    }
   } else {
-    if (vec) conf_chunk_kernel<false, true><<<grid, kConfThreads, 0, st>>>(a);
-    else conf_chunk_kernel<false, false><<<grid, kConfThreads, 0, st>>>(a);
+    if (vec) {
+      if (small) conf_chunk_kernel<false, true, WS><<<grid, kConfThreads, 0, st>>>(a);
+      else conf_chunk_kernel<false, true, WL><<<grid, kConfThreads, 0, st>>>(a);
+    } else {
+      if (small) conf_chunk_kernel<false, false, WS><<<grid, kConfThreads, 0, st>>>(a);
+      else conf_chunk_kernel<false, false, WL><<<grid, kConfThreads, 0, st>>>(a);
+    }
   }
   if (a.chunks > kMergeChunks) conf_combine_kernel<<<(unsigned)rows, kCombineThreads, 0, st>>>(a);
   else if (a.chunks > 1) conf_merge_kernel<<<(unsigned)rows, 64, 0, st>>>(a);

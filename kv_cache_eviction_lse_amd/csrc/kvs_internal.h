@@ -69,7 +69,7 @@ hipError_t launch_compact(const kvs_cache &c, const Batch &b, const int32_t *pai
 // Token confidence (mean NLL of the k most probable tokens per logits row).
 int64_t conf_max_vocab();
 int32_t conf_max_k();
-int32_t conf_chunks(int64_t vocab, bool bf16);
+int32_t conf_chunks(int64_t vocab, bool bf16, int32_t k);
 size_t conf_workspace_bytes(int64_t rows, int64_t vocab, int32_t k);
 hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_t vocab, int64_t stride,
                              int32_t k, float *conf, void *ws, hipStream_t st);

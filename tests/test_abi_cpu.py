@@ -206,10 +206,13 @@ def test_token_confidence_validation():
     assert call(logits=None) == 1 and call(conf=None) == 1
     assert call(ws=None) == 4 and call(ws_bytes=16) == 4
     assert call(rows=0) == 0                         # nothing to do: no launch
-    # sized for fp32 rows: chunks of 8 192 logits, (2 + k) floats per (row, chunk)
+    # sized for fp32 rows: chunks of 16 384 logits for k <= 32, else 8 192; (2 + k)
+    # floats per (row, chunk)
     need = L.kvs_token_confidence_workspace_size(4, 128256, 20)
-    assert need == 4 * 16 * (2 + 20) * 4
-    assert L.kvs_token_confidence_workspace_size(4, 8192, 20) == 0
+    assert need == 4 * 8 * (2 + 20) * 4
+    assert L.kvs_token_confidence_workspace_size(4, 16384, 20) == 0
+    assert L.kvs_token_confidence_workspace_size(4, 16385, 32) == 4 * 2 * 34 * 4
+    assert L.kvs_token_confidence_workspace_size(4, 8192, 33) == 0
     assert L.kvs_token_confidence_workspace_size(4, 8193, 64) == 4 * 2 * 66 * 4
 
 
