@@ -39,7 +39,6 @@ METRIC = "KV entries scored+compacted/sec; achieved HBM GB/s vs peak (8B shape, 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 D = 128
-TRAFFIC_WORKLOAD = "llama3_8b_32k"
 
 
 def _stream_job(args):
@@ -66,17 +65,16 @@ def host_samples(wname, streams, workers):
         return list(ex.map(_stream_job, jobs))
 
 
-def load_traffic(workload):
-    """HBM bytes per scorer launch from the committed rocprofv3 counter summary, if it
-    was taken on this workload and the current scorer source; else None."""
-    from kv_cache_eviction_lse_amd.profiling import score_source_sha
-    if workload != TRAFFIC_WORKLOAD:
-        return None
-    p = os.path.join(ROOT, "profiles", f"score_mfma_{workload}_traffic.json")
+def load_traffic(workload, name="score_mfma", source="score.hip"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
+    profiles/<name>_<workload>_traffic.json, if it was taken on the current source of
+    that kernel; else None."""
+    from kv_cache_eviction_lse_amd.profiling import source_sha
+    p = os.path.join(ROOT, "profiles", f"{name}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("score_source_sha") != score_source_sha():
+    if t.get("source_sha", t.get("score_source_sha")) != source_sha(source):
         return None
     return float(t["hbm_bytes_per_launch"])
 
@@ -125,8 +123,9 @@ def bench_confidence(args) -> None:
         "config": {"workload": "token_confidence", "rows": rows, "vocab": V, "k": k, "logits": "bf16",
                    "rows_are": "64 sequences x 64 decode steps"},
         "hbm_gbps": byts / (ms / 1000.0) / 1e9, "hbm_frac": byts / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS,
-        "roofline": {"kernel": "conf_chunk_kernel (+ conf_combine_kernel)", "bound": "hbm", "achieved": gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+        "roofline": {"kernel": "conf_chunk_kernel (+ conf_merge_kernel)", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("token_confidence", "conf_chunk", "confidence.hip"),
                      "ms": ev_ms, "bytes_per_launch": byts},
     }
     if not args.no_cpu_baseline:
@@ -147,6 +146,13 @@ def bench_confidence(args) -> None:
                                "sample": f"{n_done} of {rows} rows of the same batch, {t_cpu:.1f} s of fp64 "
                                          f"numpy oracle time (one thread)"}
         out["parity"] = {"rows": n_done, "max_abs_conf_err": worst}
+    if args.calibration_copy:
+        src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     out["setup_s"] = {"settle_s": round(t_settle, 2)}
     print(json.dumps(out), flush=True)
 

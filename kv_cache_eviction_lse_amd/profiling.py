@@ -45,16 +45,20 @@ def _short(name: str) -> str:
     return name.split("(")[0][:60]
 
 
-def score_source_sha() -> str:
-    p = os.path.join(HERE, "csrc", "score.hip")
+def source_sha(name: str = "score.hip") -> str:
+    p = os.path.join(HERE, "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def score_source_sha() -> str:
+    return source_sha("score.hip")
 
 
 def stats(args) -> None:
     rows = _rows(args.dir, "kernel_stats.csv")
     if not rows:
         sys.exit(f"no kernel_stats.csv under {args.dir}")
-    print("# Kernel time per launch, one eviction round = one call of each kvs kernel\n")
+    print("# Kernel time per launch (rocprofv3 kernel trace; kvs kernels only)\n")
     print(f"Command: `{args.command}`\n")
     print("| kernel | calls | average us | min us | max us | share of all GPU time |")
     print("|---|---|---|---|---|---|")
@@ -78,8 +82,10 @@ def _counter(directory: str, counter: str) -> dict[str, list[float]]:
 
 
 def traffic(args) -> None:
+    kernel = args.kernel
     copy_bytes = args.copy_mib * 2**20
-    out = {"score_source_sha": score_source_sha(), "copy_bytes": copy_bytes}
+    out = {"kernel": kernel, "source_sha": source_sha(args.source), "source": args.source,
+           "copy_bytes": copy_bytes}
     factors = {}
     for counter, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
         per = _counter(d, counter)
@@ -89,9 +95,9 @@ def traffic(args) -> None:
             sys.exit(f"no copy kernel in the {counter} run")
         c_kib = max(copies)
         factor = copy_bytes / (c_kib * 1024.0)
-        sc = [v for k, vs in per.items() if SCORER in k for v in vs]
+        sc = [v for k, vs in per.items() if kernel in k for v in vs]
         if not sc:
-            sys.exit(f"no {SCORER} dispatch in the {counter} run")
+            sys.exit(f"no {kernel} dispatch in the {counter} run")
         s_kib = sum(sc) / len(sc)
         key = counter.lower()
         out[f"{key}_kib_per_dispatch"] = s_kib
@@ -106,10 +112,10 @@ def traffic(args) -> None:
     out["commands"] = args.command
     with open(args.json, "w") as f:
         json.dump(out, f, indent=1)
-    print(f"# {SCORER}: HBM traffic per launch (llama3_8b_32k)\n")
+    print(f"# {kernel}: HBM traffic per launch ({args.workload})\n")
     for c in args.command:
         print(f"Command: `{c}`\n")
-    print("| counter | scorer KiB/dispatch | copy KiB ({} MiB copy) | bytes per counted byte | scorer bytes/launch |".format(args.copy_mib))
+    print("| counter | kernel KiB/dispatch | copy KiB ({} MiB copy) | bytes per counted byte | kernel bytes/launch |".format(args.copy_mib))
     print("|---|---|---|---|---|")
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         k = counter.lower()
@@ -121,7 +127,7 @@ def traffic(args) -> None:
               f"{args.algorithmic_bytes:.4e})")
     else:
         print()
-    print(f"\nscore.hip sha256[:16] = {out['score_source_sha']}")
+    print(f"\n{args.source} sha256[:16] = {out['source_sha']}")
 
 
 def _smi_sample() -> tuple[float, float] | None:
@@ -191,6 +197,9 @@ def main() -> None:
     t.add_argument("--json", required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
     t.add_argument("--command", action="append", default=[])
+    t.add_argument("--kernel", default=SCORER, help="kernel name substring")
+    t.add_argument("--source", default="score.hip", help="csrc file the counters are tied to")
+    t.add_argument("--workload", default="llama3_8b_32k")
     pw = sub.add_parser("power")
     pw.add_argument("--interval", type=float, default=0.5)
     pw.add_argument("cmd_args", nargs=argparse.REMAINDER)
