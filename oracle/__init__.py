@@ -10,3 +10,4 @@ from .kvs_oracle import (  # noqa: F401
     plan_stream, plan_sequence, compact_stream, eviction_round, round_fraction_to_f32,
 )
 from . import confidence_oracle as confidence  # noqa: F401
+from . import decode_oracle as decode  # noqa: F401
