@@ -16,6 +16,10 @@
  *   kvs_compact      one in-place pass that moves K row, V row and CRF per pair
  *   kvs_plan_compact the two calls above fused (same results)
  *
+ * kvs_decode_attention is the decode step itself with the same tally folded in:
+ * paged attention that emits the LSE and adds the action tokens' attention to the
+ * scores (ActKV, Component 3).
+ *
  * and, for the budget that the rounds use (ActKV, Component 2):
  *
  *   kvs_token_confidence  per decode step, the mean negative log-probability of
@@ -284,6 +288,39 @@ kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const 
  */
 kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs,
                               int32_t num, int32_t den, int32_t cap);
+
+/*
+ * Bytes of device workspace kvs_decode_attention needs (tally != 0: with the
+ * per-entry logits kept for the score tally, 4 x rows bytes per entry).  Returns 0
+ * (and sets kvs_last_error()) on invalid arguments.
+ */
+size_t kvs_decode_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs,
+                                 const kvs_observers *queries, int32_t tally);
+
+/*
+ * kvs_decode_attention -- ActKV, Component 3 (the log-sum-exp is a byproduct of
+ * paged attention, and each block's attention is recovered from it without
+ * gathering or recomputing the attention matrix) and Component 1 (an entry's signal
+ * is the attention it receives from the action tokens).  For every sequence i, KV
+ * head g and query row r = (query head h of g's group, token t of the call):
+ *     logit_rj = scale * <q_r, k_j> over the n_i live entries j (no mask),
+ *     lse_r    = ln sum_j exp(logit_rj),
+ *     out_r    = sum_j exp(logit_rj - lse_r) v_j,
+ * and, when scores is not NULL (the call's tokens are action tokens),
+ *     scores_j += sum over the rows of g of exp(logit_rj - lse_r)
+ * -- the quantity kvs_score computes for observers given their LSE.
+ * queries: the observer structure holding the call's decode tokens: q bf16
+ *   [L][Hq][T_tot][128], obs_off = token offsets [num_seqs + 1] (with host mirror),
+ *   num_q_heads, obs_total = T_tot; its lse field is not read.  At most 16 rows per
+ *   (sequence, KV head): Hq / Hkv x tokens <= 16 (else KVS_ERR_UNSUPPORTED).
+ * out: fp32 [L][Hq][T_tot][128]; lse: fp32 [L][Hq][T_tot] (sequences with no live
+ *   entries get out = 0 and lse = -inf).  scores: fp32 [L][Hkv][E] or NULL.
+ * workspace: device, >= kvs_decode_workspace_size(..., scores != NULL), 256-byte
+ *   aligned; scratch.  fp32 arithmetic with bf16 inputs.
+ */
+kvs_status kvs_decode_attention(const kvs_cache *cache, const kvs_seqs *seqs,
+                                const kvs_observers *queries, float scale, float *out, float *lse,
+                                float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Logit element types for kvs_token_confidence.

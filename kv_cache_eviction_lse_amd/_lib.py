@@ -24,7 +24,8 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_score", "kvs_lrfu_update", "kvs_lrfu_decay", "kvs_select", "kvs_lrfu_select",
            "kvs_pair_capacity",
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
-           "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend")
+           "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
+           "kvs_decode_workspace_size", "kvs_decode_attention")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -95,6 +96,10 @@ def lib() -> C.CDLL:
         L.kvs_plan_compact.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.c_int64, P, P]
         L.kvs_budget_ratchet.restype = C.c_int
         L.kvs_budget_ratchet.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+        L.kvs_decode_workspace_size.restype = C.c_size_t
+        L.kvs_decode_workspace_size.argtypes = [P, P, P, C.c_int32]
+        L.kvs_decode_attention.restype = C.c_int
+        L.kvs_decode_attention.argtypes = [P, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
         L.kvs_token_confidence_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int32]
         L.kvs_token_confidence.restype = C.c_int
@@ -298,6 +303,30 @@ def kvs_budget_ratchet(budget_h: np.ndarray, flags: np.ndarray, num: int = 7, de
     f = np.ascontiguousarray(flags, np.uint8)
     _check(lib().kvs_budget_ratchet(_ptr(b), _ptr(f), b.shape[0], num, den, cap))
     return b
+
+
+class DecodeQueries(ObserverSet):
+    """Decode tokens bf16 [L][Hq][T_tot][128] with per-sequence token offsets (the
+    observer structure; no LSE input)."""
+
+    def __init__(self, q, tok_off_h: np.ndarray, device="cuda"):
+        import torch
+        self.q, self.lse = q, None
+        self.obs_off_h = np.ascontiguousarray(tok_off_h, np.int64)
+        self.obs_off = torch.from_numpy(self.obs_off_h).to(device)
+        self.o = Observers(_ptr(q), None, _ptr(self.obs_off), _ptr(self.obs_off_h),
+                           int(q.shape[1]), int(q.shape[2]))
+
+
+def kvs_decode_workspace_size(cache: PagedCache, seqs: SeqBatch, queries: ObserverSet, tally: bool) -> int:
+    return int(lib().kvs_decode_workspace_size(cache.ref, seqs.ref, queries.ref, 1 if tally else 0))
+
+
+def kvs_decode_attention(cache: PagedCache, seqs: SeqBatch, queries: ObserverSet, scale: float, out, lse,
+                         scores=None, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvs_decode_attention(cache.ref, seqs.ref, queries.ref, C.c_float(scale), _ptr(out), _ptr(lse),
+                                      _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kvs_token_confidence_workspace_size(rows: int, vocab: int, k: int = 20) -> int:

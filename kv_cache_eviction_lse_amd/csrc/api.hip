@@ -382,6 +382,70 @@ kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t 
 
 }  // extern "C"
 
+// ---- decode attention ----
+
+namespace {
+
+// Decode queries reuse the observer structure (q, obs_off as token offsets,
+// num_q_heads, obs_total); its lse field is not read.
+kvs_status check_decode(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *o) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, false)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, false)) != KVS_OK) return st;
+  if (!o) return fail(KVS_ERR_NULL, "queries is NULL");
+  const int32_t Hkv = cache->num_kv_heads;
+  if (o->num_q_heads <= 0 || o->num_q_heads % Hkv != 0)
+    return fail(KVS_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", o->num_q_heads, Hkv);
+  const int32_t G = o->num_q_heads / Hkv;
+  if (o->obs_total < 0) return fail(KVS_ERR_SHAPE, "token total < 0");
+  if (seqs->num_seqs == 0) return KVS_OK;
+  if (!o->obs_off || !o->obs_off_h) return fail(KVS_ERR_NULL, "token offsets are NULL");
+  if (o->obs_off_h[0] < 0) return fail(KVS_ERR_SHAPE, "token offset[0] < 0");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
+    const int64_t T = o->obs_off_h[i + 1] - o->obs_off_h[i];
+    if (T < 0) return fail(KVS_ERR_SHAPE, "token offsets not monotone at %d", i);
+    if ((int64_t)G * T > kvs::decode_max_rows())
+      return fail(KVS_ERR_UNSUPPORTED, "sequence %d has %lld query rows per KV head (max %d)", i,
+                  (long long)(G * T), kvs::decode_max_rows());
+  }
+  if (o->obs_off_h[seqs->num_seqs] > o->obs_total) return fail(KVS_ERR_SHAPE, "token offsets exceed the total");
+  if (o->obs_off_h[seqs->num_seqs] > o->obs_off_h[0] && !o->q) return fail(KVS_ERR_NULL, "q is NULL");
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvs_decode_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *queries,
+                                 int32_t tally) {
+  if (check_decode(cache, seqs, queries) != KVS_OK) return 0;
+  if (seqs->num_seqs == 0) return 0;
+  const kvs::Batch b = make_batch(cache, seqs);
+  return kvs::decode_workspace_bytes(b, queries->num_q_heads / cache->num_kv_heads, queries->obs_off_h,
+                                     seqs->len_h, seqs->start_h, tally != 0, nullptr);
+}
+
+kvs_status kvs_decode_attention(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *queries,
+                                float scale, float *out, float *lse, float *scores, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  kvs_status st;
+  if ((st = check_decode(cache, seqs, queries)) != KVS_OK) return st;
+  if (!std::isfinite(scale)) return fail(KVS_ERR_SHAPE, "scale is not finite");
+  if (seqs->num_seqs == 0 || queries->obs_off_h[seqs->num_seqs] == queries->obs_off_h[0]) return ok();
+  if (!out || !lse) return fail(KVS_ERR_NULL, "out/lse is NULL");
+  const kvs::Batch b = make_batch(cache, seqs);
+  const size_t need = kvs::decode_workspace_bytes(b, queries->num_q_heads / cache->num_kv_heads,
+                                                  queries->obs_off_h, seqs->len_h, seqs->start_h,
+                                                  scores != nullptr, nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  return hip_status(kvs::launch_decode(*cache, b, *queries, scale, out, lse, scores, workspace,
+                                       queries->obs_off_h, seqs->len_h, seqs->start_h, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
 // ---- confidence monitor ----
 
 namespace {

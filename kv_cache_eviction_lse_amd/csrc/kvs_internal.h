@@ -66,6 +66,14 @@ hipError_t launch_plan_move(const kvs_cache &c, const Batch &b, const uint8_t *k
 hipError_t launch_compact(const kvs_cache &c, const Batch &b, const int32_t *pairs,
                           const int32_t *pair_count, int64_t pair_cap, hipStream_t st);
 
+// Paged decode attention with LSE and an optional attention tally.
+int32_t decode_max_rows();
+size_t decode_workspace_bytes(const Batch &b, int32_t G, const int64_t *tok_off_h, const int32_t *len_h,
+                              const int32_t *start_h, bool tally, int32_t *rmax_out);
+hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale, float *out,
+                         float *lse, float *scores, void *ws, const int64_t *tok_off_h, const int32_t *len_h,
+                         const int32_t *start_h, hipStream_t st);
+
 // Token confidence (mean NLL of the k most probable tokens per logits row).
 int64_t conf_max_vocab();
 int32_t conf_max_k();

@@ -250,3 +250,27 @@ def test_confidence_trend_validation_and_ratchet():
     t = K.kvs_confidence_trend(down)
     assert t.flag and t.slope < 0
     assert K.kvs_budget_ratchet(np.array([512], np.int32), np.array([t.flag], np.uint8))[0] == 896
+
+
+def test_decode_attention_validation():
+    L = K.lib()
+    hs = HostSeqs([[0, 1]], [0], [20])
+    c = _cache(P=2)
+    off = np.array([0, 5], np.int64)           # 5 tokens x G = 4 rows = 20 > 16
+    q = K.Observers(FAKE, None, FAKE, off.ctypes.data, 4, 5)
+    st = L.kvs_decode_attention(C.byref(c), C.byref(hs.s), C.byref(q), C.c_float(0.1), FAKE, FAKE, None,
+                                FAKE, 1 << 30, None)
+    assert st == 3
+    off2 = np.array([0, 4], np.int64)          # 16 rows: allowed
+    q2 = K.Observers(FAKE, None, FAKE, off2.ctypes.data, 4, 4)
+    assert L.kvs_decode_workspace_size(C.byref(c), C.byref(hs.s), C.byref(q2), 1) > 0
+    need = L.kvs_decode_workspace_size(C.byref(c), C.byref(hs.s), C.byref(q2), 0)
+    assert 0 < need < L.kvs_decode_workspace_size(C.byref(c), C.byref(hs.s), C.byref(q2), 1)
+    assert L.kvs_decode_attention(C.byref(c), C.byref(hs.s), C.byref(q2), C.c_float(0.1), None, FAKE, None,
+                                  FAKE, 1 << 30, None) == 1
+    assert L.kvs_decode_attention(C.byref(c), C.byref(hs.s), C.byref(q2), C.c_float(0.1), FAKE, FAKE, None,
+                                  FAKE, 16, None) == 4
+    q3 = K.Observers(FAKE, None, FAKE, off2.ctypes.data, 6, 4)   # 6 heads over 4 KV heads? not a multiple
+    c4 = _cache(Hkv=4, P=2)
+    assert L.kvs_decode_attention(C.byref(c4), C.byref(hs.s), C.byref(q3), C.c_float(0.1), FAKE, FAKE, None,
+                                  FAKE, 1 << 30, None) == 2
