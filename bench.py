@@ -14,7 +14,9 @@ tokens), so the work per step is constant.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-`--workload token_confidence` instead times the confidence monitor that drives the
+`--workload decode_llama3_8b_32k` times paged decode attention with the LSE and the
+attention tally (one decode token over the 8B-shaped cache), and `--workload
+token_confidence` times the confidence monitor that drives the
 budget ratchet: kvs_token_confidence over one round's decode steps (64 sequences x
 64 steps = 4 096 rows of bf16 logits over the Llama-3 vocabulary, 128 256 tokens),
 and prints its own JSON line.
@@ -30,6 +32,7 @@ import sys
 import time
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -157,6 +160,127 @@ def bench_confidence(args) -> None:
     print(json.dumps(out), flush=True)
 
 
+DEC_METRIC = ("KV entries attended by paged decode attention with LSE and attention tally/sec; achieved HBM "
+              "GB/s vs peak (8B shape, 32K ctx)")
+
+
+def bench_decode(args) -> None:
+    """kvs_decode_attention for one decode token over the 8B-shaped cache, with the
+    attention tally into the scores (the token is an action token); one JSON line."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import ALL
+    from workloads.host import make_layout, observers
+    from workloads import device as DV
+    import oracle as O
+
+    w = ALL["llama3_8b_32k"]
+    lay = make_layout(w)
+    L, Hkv, Hq = w.num_layers, w.num_kv_heads, w.num_q_heads
+    dev = torch.device("cuda", 0)
+    q_obs = observers(w, lay, heads=set(), only_heads=True)
+    d = DV.fill(w, lay, q_obs, dev)
+    T = 1                                                    # one decode token per sequence
+    g = torch.Generator(device=dev).manual_seed(5)
+    q = torch.randn((L, Hq, T * w.num_seqs, D), generator=g, device=dev).to(torch.bfloat16)
+    tok_off = np.arange(w.num_seqs + 1, dtype=np.int64) * T
+    cache = K.PagedCache(d.k, d.v, d.crf)
+    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
+    qs = K.DecodeQueries(q, tok_off, device=dev)
+    out = torch.empty((L, Hq, T * w.num_seqs, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((L, Hq, T * w.num_seqs), dtype=torch.float32, device=dev)
+    E = int(lay.entry_off[-1])
+    scores = torch.zeros((L, Hkv, E), dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvs_decode_workspace_size(cache, seqs, qs, True), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    run = lambda: K.kvs_decode_attention(cache, seqs, qs, w.scale, out, lse, scores, ws)  # noqa: E731
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+    t_settle = time.perf_counter() - t_settle
+    for _ in range(args.warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(st)
+        run()
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    entries = E * L * Hkv
+    R = Hq // Hkv * T
+    # K and V rows read once, the tally's logits written and read (4 B per row), scores
+    # read and written, queries read and outputs written
+    byts = entries * (2 * 2 * D + 2 * 4 * R + 8) + L * Hq * T * (2 * D + 4 * D + 4)
+    gbps = byts / (ev_ms / 1000.0) / 1e9
+    res = {
+        "metric": DEC_METRIC, "value": entries / (ms / 1000.0), "unit": "entries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_llama3_8b_32k", "layers": L, "kv_heads": Hkv, "q_heads": Hq,
+                   "head_dim": D, "context": int(lay.length[0]), "decode_tokens": T, "tally": True,
+                   "entries_per_step": entries},
+        "hbm_gbps": byts / (ms / 1000.0) / 1e9, "hbm_frac": byts / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "decode_split_kernel (+ combine, tally)", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("decode_llama3_8b_32k", "decode_split", "decode.hip"),
+                     "ms": ev_ms, "bytes_per_launch": byts},
+    }
+    if not args.no_cpu_baseline:
+        # parity and the oracle's rate on sampled streams (one call, tally from zero)
+        scores.zero_()
+        run()
+        torch.cuda.synchronize()
+        o_gpu, l_gpu, s_gpu = out.cpu().numpy(), lse.cpu().numpy(), scores.cpu().numpy()
+        rng = np.random.default_rng(0)
+        t_cpu, n_done, worst_o, worst_t = 0.0, 0, 0.0, 0.0
+        G = Hq // Hkv
+        n = int(lay.length[0])
+        pos = int(lay.start[0]) + np.arange(n)
+        pg = torch.from_numpy(lay.block_table[0][pos // 16].astype(np.int64)).to(dev)
+        rw = torch.from_numpy((pos % 16).astype(np.int64)).to(dev)
+        # up to 16 distinct streams are gathered to the host once and checked against the
+        # oracle; the oracle then runs over them in turn (one BLAS thread) until it has
+        # spent --cpu-seconds
+        host = []
+        for (l, gg) in {(int(rng.integers(L)), int(rng.integers(Hkv))) for _ in range(16)}:
+            # the pools hold bf16 bit patterns in int16 storage
+            kk = d.k[l][pg, gg, rw].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+            vv = d.v[l][pg, gg, rw].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+            qq = q[l, gg * G:(gg + 1) * G, 0].float().cpu().numpy().astype(np.float64)
+            host.append((l, gg, qq, kk, vv))
+        with threadpool_limits(1):
+            while t_cpu < args.cpu_seconds:
+                for (l, gg, qq, kk, vv) in host:
+                    ta = time.perf_counter()
+                    o_ref, l_ref, p_ref = O.decode.attend_stream(qq, kk, vv, w.scale)
+                    t_cpu += time.perf_counter() - ta
+                    if n_done < len(host) * n:
+                        worst_o = max(worst_o, float(np.max(np.abs(o_gpu[l, gg * G:(gg + 1) * G, 0] - o_ref))))
+                        tref = p_ref.sum(0)
+                        worst_t = max(worst_t, float(np.max(np.abs(s_gpu[l, gg] - tref) / np.maximum(tref, 1e-6))))
+                    n_done += n
+        res["cpu_baseline"] = {"value": n_done / t_cpu, "unit": "entries/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{len(host)} of {L * Hkv} streams (layer, KV head), each "
+                                         f"{n} entries, evaluated {n_done // n} times in {t_cpu:.1f} s of fp64 "
+                                         f"numpy oracle time (one BLAS thread)"}
+        res["parity"] = {"streams": len(host), "max_abs_out_err": worst_o, "max_rel_tally_err": worst_t}
+    if args.calibration_copy:
+        src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    res["setup_s"] = {"settle_s": round(t_settle, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +309,9 @@ def main():
 
     if args.workload == "token_confidence":
         bench_confidence(args)
+        return
+    if args.workload == "decode_llama3_8b_32k":
+        bench_decode(args)
         return
     from workloads import ALL
     from workloads.host import make_layout, observers

@@ -312,7 +312,8 @@ size_t kvs_decode_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs,
  * queries: the observer structure holding the call's decode tokens: q bf16
  *   [L][Hq][T_tot][128], obs_off = token offsets [num_seqs + 1] (with host mirror),
  *   num_q_heads, obs_total = T_tot; its lse field is not read.  At most 16 rows per
- *   (sequence, KV head): Hq / Hkv x tokens <= 16 (else KVS_ERR_UNSUPPORTED).
+ *   (sequence, KV head): Hq / Hkv x tokens <= 16, and start + length of every
+ *   sequence <= 4 194 304 positions (else KVS_ERR_UNSUPPORTED).
  * out: fp32 [L][Hq][T_tot][128]; lse: fp32 [L][Hq][T_tot] (sequences with no live
  *   entries get out = 0 and lse = -inf).  scores: fp32 [L][Hkv][E] or NULL.
  * workspace: device, >= kvs_decode_workspace_size(..., scores != NULL), 256-byte

@@ -407,6 +407,9 @@ kvs_status check_decode(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_
     if ((int64_t)G * T > kvs::decode_max_rows())
       return fail(KVS_ERR_UNSUPPORTED, "sequence %d has %lld query rows per KV head (max %d)", i,
                   (long long)(G * T), kvs::decode_max_rows());
+    if ((int64_t)seqs->start_h[i] + seqs->len_h[i] > kvs::decode_max_positions())
+      return fail(KVS_ERR_UNSUPPORTED, "sequence %d ends at position %lld (max %lld)", i,
+                  (long long)seqs->start_h[i] + seqs->len_h[i], (long long)kvs::decode_max_positions());
   }
   if (o->obs_off_h[seqs->num_seqs] > o->obs_total) return fail(KVS_ERR_SHAPE, "token offsets exceed the total");
   if (o->obs_off_h[seqs->num_seqs] > o->obs_off_h[0] && !o->q) return fail(KVS_ERR_NULL, "q is NULL");

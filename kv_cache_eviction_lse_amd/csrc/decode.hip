@@ -10,9 +10,8 @@
 // tally reads 4R bytes per entry instead of the 256-byte K row that kvs_score reads.
 //
 // Three kernels per call:
-//   decode_split_kernel  one wave per (stream, split of 256 positions).  Per 64-key
-//       tile: lane = key for the logits (its K row in VGPRs, v_dot2 with the query
-//       rows, which are wave-uniform and come through scalar loads); online softmax
+//   decode_split_kernel  one wave per (stream, split of 1 024 positions).  Per 64-key
+//       tile: QK^T on 16x16x32 bf16 MFMAs (query rows on M, keys on N); online softmax
 //       per row; then lane = pair of dimensions for P.V (each V row is one coalesced
 //       256-byte load, the tile's probabilities are read from LDS).  Writes the split's
 //       (max, sum, accumulator) per row, and the logits when a tally is requested.
@@ -24,7 +23,7 @@
 namespace kvs {
 namespace {
 
-constexpr int kSplit = 256;                     // key positions per split (16 pages)
+constexpr int kSplit = 1024;                    // key positions per split (64 pages)
 constexpr int kTile = 64;
 constexpr int kPartFloats = 2 + kHeadDim;       // max, sum, accumulator
 constexpr float kLog2e = 1.4426950408889634f;
@@ -98,81 +97,145 @@ __device__ __forceinline__ int64_t row_elem(const DecodeArgs &a, const int32_t *
   return ((((int64_t)l * a.b.num_pages + page) * a.b.Hkv + g) * kPage + (pos & 15)) * kHeadDim;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+// LDS written by some lanes of a wave and then read by others: the wave's LDS
+// operations complete in order, this keeps the compiler from reordering them.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Maximum / sum over the 16 lanes of each 16-lane block (xor swizzles stay in the block).
+__device__ __forceinline__ float block16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (8 << 10) | 0x1F)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1F)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (2 << 10) | 0x1F)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (1 << 10) | 0x1F)));
+  return x;
+}
+__device__ __forceinline__ float block16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (8 << 10) | 0x1F));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1F));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (2 << 10) | 0x1F));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (1 << 10) | 0x1F));
+  return x;
+}
+
+// One wave per (split, sequence, layer x KV head).  QK^T on v_mfma_f32_16x16x32_bf16
+// with the query rows on M (padded to 16 with zero rows) and 16 keys on N: lane l
+// loads 16 bytes of key l % 16 (dims 8 (l / 16) .. + 8 of each 32-dim slice), so one
+// load instruction covers 64 contiguous bytes of 16 key rows, and ends up holding
+// rows 4 (l / 16) .. + 4 of key l % 16.  The softmax state of those 4 rows is kept in
+// each lane of the 16-lane block (identical across the block).  P.V runs with lane =
+// pair of dimensions over the tile's V rows (coalesced 256-byte loads).
 template <int RMAX>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  __shared__ float plds[RMAX][kTile];
+  __shared__ float plds[16][kTile];
+  __shared__ float corr_lds[16];
   const int32_t s = blockIdx.x, i = blockIdx.y, lg = blockIdx.z;
   if (s >= seq_splits(a, i)) return;
   const int32_t l = lg / a.b.Hkv, g = lg - l * a.b.Hkv;
   const int lane = threadIdx.x;
-  const int32_t start = a.b.start[i], n = a.b.len[i];
+  const int blk = lane >> 4, n = lane & 15;
+  const int32_t start = a.b.start[i], len = a.b.len[i];
   const int64_t t0 = a.tok_off[i];
   const int32_t T = (int32_t)(a.tok_off[i + 1] - t0);
-  const int32_t R = a.G * T;                   // <= RMAX (host checked)
+  const int32_t R = a.G * T;                   // <= RMAX <= 16 (host checked)
   const int32_t *bt_row = a.b.bt + (int64_t)i * a.b.max_pages;
-  const int32_t p0 = s * kSplit, p1 = min(p0 + kSplit, start + n);
+  const int32_t p0 = s * kSplit, p1 = min(p0 + kSplit, start + len);
   const float NEG = -__builtin_inff();
 
-  float m[RMAX], lsum[RMAX], acc0[RMAX], acc1[RMAX];
+  // query rows as MFMA A operands: lane (m = lane % 16, 8-dim block lane / 16)
+  bf16x8 qa[4];
+  {
+    const int m = n;
+    const bool ok = m < R;
+    const int32_t mc = ok ? m : 0;
+    const int32_t h = g * a.G + mc / T, t = mc - (mc / T) * T;
+    const uint16_t *qp = a.q + (((int64_t)l * a.Hq + h) * a.t_total + t0 + t) * kHeadDim + 8 * blk;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) { m[r] = NEG; lsum[r] = 0.f; acc0[r] = 0.f; acc1[r] = 0.f; }
+    for (int sl = 0; sl < 4; ++sl) {
+      const bf16x8 v = *(const bf16x8 *)(qp + 32 * sl);
+      const bf16x8 z = {};
+      qa[sl] = ok ? v : z;
+    }
+  }
+  float mrun[4], lrun[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { mrun[e] = NEG; lrun[e] = 0.f; }
+  float acc0[RMAX], acc1[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; }
 
-  for (int32_t tp = p0; tp < p1; tp += kTile) {
-    // ---- logits: lane = key ----
-    const int32_t pos = tp + lane;
-    const bool valid = pos >= start && pos < p1;
-    const int32_t pc = valid ? pos : max(start, tp);      // clamped to a live position
-    const uint4 *kr = (const uint4 *)(a.k + row_elem(a, bt_row, l, g, pc));
-    bf16x2 kv[64];
+  // tiles that lie wholly before the first live position are skipped, so every tile
+  // visited holds a live key
+  const int32_t tbeg = p0 + ((max(start, p0) - p0) / kTile) * kTile;
+  for (int32_t tp = tbeg; tp < p1; tp += kTile) {
+    // ---- logits of the tile's 64 keys (4 groups of 16) ----
+    floatx4 d[4];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint4 x = kr[c];
-      const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+    for (int kg = 0; kg < 4; ++kg) {
+      const int32_t pos = min(max(tp + 16 * kg + n, start), p1 - 1);
+      const uint16_t *kr = a.k + row_elem(a, bt_row, l, g, pos) + 8 * blk;
+      d[kg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kv[c * 4 + e] = __builtin_bit_cast(bf16x2, w4[e]);
+      for (int sl = 0; sl < 4; ++sl)
+        d[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[sl], *(const bf16x8 *)(kr + 32 * sl), d[kg], 0, 0, 0);
     }
-    float lg2[RMAX];
+    // ---- online softmax of rows 4 blk + e (state replicated over the 16 lanes) ----
+    float x[4][4];
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      lg2[r] = NEG;
-      if (r < R) {
-        const int32_t h = g * a.G + r / T, t = r - (r / T) * T;
-        const bf16x2 *qp = (const bf16x2 *)(a.q + (((int64_t)l * a.Hq + h) * a.t_total + t0 + t) * kHeadDim);
-        float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+    for (int kg = 0; kg < 4; ++kg) {
+      const int32_t pos = tp + 16 * kg + n;
+      const bool valid = pos >= start && pos < p1;
 #pragma unroll
-        for (int e = 0; e < 64; e += 4) {
-          d0 = __builtin_amdgcn_fdot2_f32_bf16(qp[e], kv[e], d0, false);
-          d1 = __builtin_amdgcn_fdot2_f32_bf16(qp[e + 1], kv[e + 1], d1, false);
-          d2 = __builtin_amdgcn_fdot2_f32_bf16(qp[e + 2], kv[e + 2], d2, false);
-          d3 = __builtin_amdgcn_fdot2_f32_bf16(qp[e + 3], kv[e + 3], d3, false);
+      for (int e = 0; e < 4; ++e) x[kg][e] = valid ? d[kg][e] * a.alpha : NEG;
+      if (a.logits && valid) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * blk + e;
+          if (r < R) a.logits[((int64_t)lg * a.b.E + a.b.entry_off[i] + (pos - start)) * a.rmax + r] = x[kg][e];
         }
-        lg2[r] = valid ? ((d0 + d1) + (d2 + d3)) * a.alpha : NEG;
-        if (a.logits && valid)
-          a.logits[((int64_t)lg * a.b.E + a.b.entry_off[i] + (pos - start)) * a.rmax + r] = lg2[r];
       }
     }
-    // ---- online softmax per row; tile probabilities to LDS ----
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mt = block16_max(fmaxf(fmaxf(x[0][e], x[1][e]), fmaxf(x[2][e], x[3][e])));
+      const float mn = fmaxf(mrun[e], mt);              // finite: the tile has a live key
+      const float corr = mrun[e] == NEG ? 0.f : __builtin_amdgcn_exp2f(mrun[e] - mn);
+      const float mref = mn == NEG ? 0.f : mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const float p = __builtin_amdgcn_exp2f(x[kg][e] - mref);  // 0 for dead keys
+        ps += p;
+        plds[4 * blk + e][16 * kg + n] = p;
+      }
+      lrun[e] = lrun[e] * corr + block16_sum(ps);
+      mrun[e] = mn;
+      if (n == 0) corr_lds[4 * blk + e] = corr;
+    }
+    wave_lds_order();
+    // ---- P.V: lane = dimensions 2 lane, 2 lane + 1 (same wave: LDS in order) ----
+    uint32_t vw[kTile];
+#pragma unroll
+    for (int q = 0; q < kTile; ++q) {
+      const int32_t kp = min(max(tp + q, start), p1 - 1);
+      vw[q] = ((const uint32_t *)(a.v + row_elem(a, bt_row, l, g, kp)))[lane];
+    }
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r < R) {
-        const float mt = wave_max_f32(lg2[r]);
-        const float mn = fmaxf(m[r], mt);                 // finite: the tile has a live key
-        const float corr = m[r] == NEG ? 0.f : __builtin_amdgcn_exp2f(m[r] - mn);
-        const float p = valid ? __builtin_amdgcn_exp2f(lg2[r] - mn) : 0.f;
-        lsum[r] = lsum[r] * corr + wave_sum_f32(p);
-        acc0[r] *= corr;
-        acc1[r] *= corr;
-        m[r] = mn;
-        plds[r][lane] = p;
+        const float c = corr_lds[r];
+        acc0[r] *= c;
+        acc1[r] *= c;
       }
     }
-    // ---- P.V: lane = dimensions 2 lane, 2 lane + 1 ----
-    const int32_t nk = min(kTile, p1 - tp);
-    for (int32_t q = 0; q < nk; ++q) {
-      const int32_t kp = tp + q;
-      if (kp < start) continue;                           // wave-uniform
-      const uint32_t vw = ((const uint32_t *)(a.v + row_elem(a, bt_row, l, g, kp)))[lane];
-      const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xFFFF0000u);
+#pragma unroll
+    for (int q = 0; q < kTile; ++q) {
+      const float v0 = __uint_as_float(vw[q] << 16), v1 = __uint_as_float(vw[q] & 0xFFFF0000u);
 #pragma unroll
       for (int r = 0; r < RMAX; ++r) {
         if (r < R) {
@@ -182,17 +245,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
+    wave_lds_order();
   }
   // ---- the split's partials ----
   const int64_t base = (int64_t)lg * a.part_off[a.b.S] + a.part_off[i] + (int64_t)s * R;
+  if (n == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * blk + e;
+      if (r < R) {
+        float *pp = a.part + (base + r) * kPartFloats;
+        pp[0] = mrun[e];
+        pp[1] = lrun[e];
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
     if (r < R) {
       float *pp = a.part + (base + r) * kPartFloats;
-      if (lane == 0) {
-        pp[0] = m[r];
-        pp[1] = lsum[r];
-      }
       pp[2 + 2 * lane] = acc0[r];
       pp[3 + 2 * lane] = acc1[r];
     }
@@ -200,36 +271,58 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge the splits of one (stream, row): output = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
-// LSE = (M + log2 sum) ln 2.  One wave per (sequence, layer x KV head), rows in turn.
+// LSE = (M + log2 sum) ln 2.  One wave per (sequence, layer x KV head, row): lanes take
+// the splits for M and the sum (their weights go to LDS), then lane = pair of dimensions
+// for the accumulators, 8 splits in flight.
+constexpr int kMaxSplits = 4096;
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  const int32_t i = blockIdx.x, lg = blockIdx.y;
-  const int32_t ns = seq_splits(a, i);
+  __shared__ float f_lds[kMaxSplits];
+  const int32_t i = blockIdx.x, lg = blockIdx.y, r = blockIdx.z;
   const int64_t t0 = a.tok_off[i];
   const int32_t T = (int32_t)(a.tok_off[i + 1] - t0);
   const int32_t R = a.G * T;
+  if (r >= R) return;
+  const int32_t ns = seq_splits(a, i);
   const int32_t l = lg / a.b.Hkv, g = lg - l * a.b.Hkv;
   const int lane = threadIdx.x;
   const float NEG = -__builtin_inff();
-  for (int32_t r = 0; r < R; ++r) {
-    const int32_t h = g * a.G + r / T, t = r - (r / T) * T;
-    const int64_t orow = ((int64_t)l * a.Hq + h) * a.t_total + t0 + t;
-    float M = NEG;
-    for (int32_t s = 0; s < ns; ++s)
-      M = fmaxf(M, a.part[((int64_t)lg * a.part_off[a.b.S] + a.part_off[i] + (int64_t)s * R + r) * kPartFloats]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int32_t s = 0; s < ns; ++s) {
-      const float *pp = a.part + ((int64_t)lg * a.part_off[a.b.S] + a.part_off[i] + (int64_t)s * R + r) * kPartFloats;
-      const float ms = pp[0];
-      const float f = ms == NEG ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      L = __builtin_fmaf(pp[1], f, L);
-      o0 = __builtin_fmaf(pp[2 + 2 * lane], f, o0);
-      o1 = __builtin_fmaf(pp[3 + 2 * lane], f, o1);
-    }
-    const bool any = ns > 0 && M != NEG;
-    a.out[orow * kHeadDim + 2 * lane] = any ? o0 / L : 0.f;
-    a.out[orow * kHeadDim + 2 * lane + 1] = any ? o1 / L : 0.f;
-    if (lane == 0) a.lse[orow] = any ? (M + __builtin_amdgcn_logf(L)) * kLn2 : NEG;
+  const int32_t h = g * a.G + r / T, t = r - (r / T) * T;
+  const int64_t orow = ((int64_t)l * a.Hq + h) * a.t_total + t0 + t;
+  const float *pb = a.part + ((int64_t)lg * a.part_off[a.b.S] + a.part_off[i] + r) * kPartFloats;
+  const int64_t sstride = (int64_t)R * kPartFloats;        // from split s to s + 1
+  float M = NEG;
+  for (int32_t s = lane; s < ns; s += 64) M = fmaxf(M, pb[s * sstride]);
+  M = wave_max_f32(M);
+  float Ls = 0.f;
+  for (int32_t s = lane; s < ns; s += 64) {
+    const float ms = pb[s * sstride];
+    const float f = ms == NEG ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    f_lds[s] = f;
+    Ls = __builtin_fmaf(pb[s * sstride + 1], f, Ls);
   }
+  const float L = wave_sum_f32(Ls);
+  float o0 = 0.f, o1 = 0.f;
+  int32_t s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const float2 *)(pb + (s + u) * sstride + 2 + 2 * lane);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = f_lds[s + u];
+      o0 = __builtin_fmaf(v[u].x, f, o0);
+      o1 = __builtin_fmaf(v[u].y, f, o1);
+    }
+  }
+  for (; s < ns; ++s) {
+    const float2 v = *(const float2 *)(pb + s * sstride + 2 + 2 * lane);
+    const float f = f_lds[s];
+    o0 = __builtin_fmaf(v.x, f, o0);
+    o1 = __builtin_fmaf(v.y, f, o1);
+  }
+  const bool any = ns > 0 && M != NEG;
+  *(float2 *)(a.out + orow * kHeadDim + 2 * lane) = any ? float2{o0 / L, o1 / L} : float2{0.f, 0.f};
+  if (lane == 0) a.lse[orow] = any ? (M + __builtin_amdgcn_logf(L)) * kLn2 : NEG;
 }
 
 // s_j += sum_r 2^(logit2_rj - LSE_r log2 e) over the stream's rows.
@@ -274,6 +367,7 @@ size_t decode_workspace_bytes(const Batch &b, int32_t G, const int64_t *tok_off_
 }
 
 int32_t decode_max_rows() { return 16; }
+int64_t decode_max_positions() { return (int64_t)kMaxSplits * kSplit; }
 
 hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale, float *out,
                          float *lse, float *scores, void *ws, const int64_t *tok_off_h, const int32_t *len_h,
@@ -321,7 +415,7 @@ hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers
     else if (rmax <= 8) decode_split_kernel<8><<<grid, 64, 0, st>>>(a);
     else decode_split_kernel<16><<<grid, 64, 0, st>>>(a);
   }
-  decode_combine_kernel<<<dim3((unsigned)b.S, (unsigned)LH), 64, 0, st>>>(a);
+  decode_combine_kernel<<<dim3((unsigned)b.S, (unsigned)LH, (unsigned)(rmax > 0 ? rmax : 1)), 64, 0, st>>>(a);
   int32_t max_len = 0;
   for (int32_t i = 0; i < b.S; ++i) max_len = len_h[i] > max_len ? len_h[i] : max_len;
   if (scores && max_len > 0)

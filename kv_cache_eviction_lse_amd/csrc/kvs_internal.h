@@ -68,6 +68,7 @@ hipError_t launch_compact(const kvs_cache &c, const Batch &b, const int32_t *pai
 
 // Paged decode attention with LSE and an optional attention tally.
 int32_t decode_max_rows();
+int64_t decode_max_positions();   // start + length of a sequence, at most
 size_t decode_workspace_bytes(const Batch &b, int32_t G, const int64_t *tok_off_h, const int32_t *len_h,
                               const int32_t *start_h, bool tally, int32_t *rmax_out);
 hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale, float *out,

@@ -69,7 +69,7 @@ def _check(lay, inp, Hq, res, tally=True):
             assert err.max() <= 1e-3, (i, l, g, float(err.max()))
 
 
-@pytest.mark.parametrize("case", ["ragged", "gqa8_two_tokens", "long"])
+@pytest.mark.parametrize("case", ["ragged", "gqa8_two_tokens", "long", "split_edges"])
 def test_decode_attention_parity(case):
     if case == "ragged":
         # G = 4; lengths with partial first pages, an empty sequence, one entry, and
@@ -80,9 +80,15 @@ def test_decode_attention_parity(case):
     elif case == "gqa8_two_tokens":
         lay, inp = random_batch(32, 1, 2, 16, [1029, 4100], [3, 0], [2, 1], prior_crf=False)
         Hq = 16
-    else:
+    elif case == "long":
         lay, inp = random_batch(33, 1, 1, 4, [40000], [11], [1], prior_crf=False, planted=0.02)
         Hq = 4
+    else:
+        # live ranges that end exactly on a split boundary (1 024 positions), one past
+        # it (a split with one key), on the second boundary, and within the first tile
+        lay, inp = random_batch(35, 1, 2, 8, [1009, 1010, 2033, 49], [15, 15, 15, 15], [1, 2, 1, 4],
+                                prior_crf=False)
+        Hq = 8
     print(f"decode parity {case}", flush=True)
     res, _ = _run(lay, inp, Hq)
     _check(lay, inp, Hq, res)
