@@ -229,6 +229,7 @@ def bench_decode(args) -> None:
         "roofline": {"kernel": "decode_split_kernel (+ combine, tally)", "bound": "hbm", "achieved": gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                      "traffic": load_traffic("decode_llama3_8b_32k", "decode_split", "decode.hip"),
+                     "traffic_of": "decode_split_kernel",
                      "ms": ev_ms, "bytes_per_launch": byts},
     }
     if not args.no_cpu_baseline:

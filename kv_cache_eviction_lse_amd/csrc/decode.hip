@@ -10,7 +10,7 @@
 // tally reads 4R bytes per entry instead of the 256-byte K row that kvs_score reads.
 //
 // Three kernels per call:
-//   decode_split_kernel  one wave per (stream, split of 1 024 positions).  Per 64-key
+//   decode_split_kernel  one wave per (stream, split of 512 positions).  Per 64-key
 //       tile: QK^T on 16x16x32 bf16 MFMAs (query rows on M, keys on N); online softmax
 //       per row; then lane = pair of dimensions for P.V (each V row is one coalesced
 //       256-byte load, the tile's probabilities are read from LDS).  Writes the split's
@@ -23,7 +23,7 @@
 namespace kvs {
 namespace {
 
-constexpr int kSplit = 1024;                    // key positions per split (64 pages)
+constexpr int kSplit = 512;                     // key positions per split (32 pages)
 constexpr int kTile = 64;
 constexpr int kPartFloats = 2 + kHeadDim;       // max, sum, accumulator
 constexpr float kLog2e = 1.4426950408889634f;
@@ -130,8 +130,9 @@ __device__ __forceinline__ float block16_sum(float x) {
 // rows 4 (l / 16) .. + 4 of key l % 16.  The softmax state of those 4 rows is kept in
 // each lane of the 16-lane block (identical across the block).  P.V runs with lane =
 // pair of dimensions over the tile's V rows (coalesced 256-byte loads).
+// Occupancy: 4 waves per SIMD for up to 4 rows (115 VGPRs), 2 for 8, 1 for 16.
 template <int RMAX>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, RMAX <= 4 ? 4 : (RMAX <= 8 ? 2 : 1)) void decode_split_kernel(DecodeArgs a) {
   __shared__ float plds[16][kTile];
   __shared__ float corr_lds[16];
   const int32_t s = blockIdx.x, i = blockIdx.y, lg = blockIdx.z;
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // LSE = (M + log2 sum) ln 2.  One wave per (sequence, layer x KV head, row): lanes take
 // the splits for M and the sum (their weights go to LDS), then lane = pair of dimensions
 // for the accumulators, 8 splits in flight.
-constexpr int kMaxSplits = 4096;
+constexpr int kMaxSplits = 8192;
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float f_lds[kMaxSplits];
   const int32_t i = blockIdx.x, lg = blockIdx.y, r = blockIdx.z;
@@ -325,25 +326,60 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[orow] = any ? (M + __builtin_amdgcn_logf(L)) * kLn2 : NEG;
 }
 
-// s_j += sum_r 2^(logit2_rj - LSE_r log2 e) over the stream's rows.
+// s_j += sum_r 2^(logit2_rj - LSE_r log2 e) over the stream's rows.  256 threads, four
+// entries per thread (256 apart); the rows' LSEs are loaded once per block, the logits
+// of an entry as float4s when the row count per entry is a multiple of 4.
+constexpr int kTallyPer = 4;
+template <int RMAX>
 __global__ __launch_bounds__(256) void decode_tally_kernel(DecodeArgs a) {
   const int32_t i = blockIdx.y, lg = blockIdx.z;
   const int32_t n = a.b.len[i];
-  const int32_t j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= n) return;
+  const int32_t j0 = blockIdx.x * (256 * kTallyPer) + threadIdx.x;
+  if (blockIdx.x * (256 * kTallyPer) >= n) return;
   const int64_t t0 = a.tok_off[i];
   const int32_t T = (int32_t)(a.tok_off[i + 1] - t0);
-  const int32_t R = a.G * T;
+  const int32_t R = a.G * T;                   // <= RMAX (host checked)
   if (R == 0) return;
   const int32_t l = lg / a.b.Hkv, g = lg - l * a.b.Hkv;
-  const int64_t e = (int64_t)lg * a.b.E + a.b.entry_off[i] + j;
-  float s = 0.f;
-  for (int32_t r = 0; r < R; ++r) {
-    const int32_t h = g * a.G + r / T, t = r - (r / T) * T;
-    const float lse2 = a.lse[((int64_t)l * a.Hq + h) * a.t_total + t0 + t] * kLog2e;
-    s += __builtin_amdgcn_exp2f(a.logits[e * a.rmax + r] - lse2);
+  float lse2[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    lse2[r] = __builtin_inff();                  // rows beyond R contribute 2^(-inf) = 0
+    if (r < R) {
+      const int32_t h = g * a.G + r / T, t = r - (r / T) * T;
+      lse2[r] = a.lse[((int64_t)l * a.Hq + h) * a.t_total + t0 + t] * kLog2e;
+    }
   }
-  a.scores[e] += s;
+  const int64_t ebase = (int64_t)lg * a.b.E + a.b.entry_off[i];
+  float x[kTallyPer][RMAX];
+#pragma unroll
+  for (int u = 0; u < kTallyPer; ++u) {
+    const int32_t j = min(j0 + 256 * u, n - 1);
+    const float *lp = a.logits + (ebase + j) * a.rmax;
+    if (a.rmax % 4 == 0) {
+#pragma unroll
+      for (int r4 = 0; r4 < RMAX; r4 += 4) {
+        float4 v = {0.f, 0.f, 0.f, 0.f};
+        if (r4 < R) v = *(const float4 *)(lp + r4);
+        // logits of rows beyond this sequence's R were never written
+        x[u][r4] = v.x;
+        x[u][r4 + 1] = r4 + 1 < R ? v.y : 0.f;
+        x[u][r4 + 2] = r4 + 2 < R ? v.z : 0.f;
+        x[u][r4 + 3] = r4 + 3 < R ? v.w : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) x[u][r] = r < R ? lp[r] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kTallyPer; ++u) {
+    const int32_t j = j0 + 256 * u;
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) sum += __builtin_amdgcn_exp2f(x[u][r] - lse2[r]);
+    if (j < n) a.scores[ebase + j] += sum;
+  }
 }
 
 }  // namespace
@@ -418,8 +454,12 @@ hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers
   decode_combine_kernel<<<dim3((unsigned)b.S, (unsigned)LH, (unsigned)(rmax > 0 ? rmax : 1)), 64, 0, st>>>(a);
   int32_t max_len = 0;
   for (int32_t i = 0; i < b.S; ++i) max_len = len_h[i] > max_len ? len_h[i] : max_len;
-  if (scores && max_len > 0)
-    decode_tally_kernel<<<dim3((unsigned)((max_len + 255) / 256), (unsigned)b.S, (unsigned)LH), 256, 0, st>>>(a);
+  if (scores && max_len > 0) {
+    const dim3 tg((unsigned)((max_len + 256 * kTallyPer - 1) / (256 * kTallyPer)), (unsigned)b.S, (unsigned)LH);
+    if (rmax <= 4) decode_tally_kernel<4><<<tg, 256, 0, st>>>(a);
+    else if (rmax <= 8) decode_tally_kernel<8><<<tg, 256, 0, st>>>(a);
+    else decode_tally_kernel<16><<<tg, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
