@@ -208,6 +208,46 @@ kvs_status kvs_lrfu_select(const kvs_cache *cache, const kvs_seqs *seqs, const f
                            const int32_t *budget_h, uint8_t *keep, void *stream);
 
 /*
+ * Reasoning steps of each sequence (StepKV, Abstract: cache entries are associated
+ * with the step that generated them).  Sequence i's steps are the global step ids
+ * step_off[i] .. step_off[i+1]-1; step k covers live slots first[k] .. (first of the
+ * next step of the sequence, or len[i]) - 1.  Requirements (checked on the host
+ * mirrors): step_off[0] = 0, non-decreasing; within a sequence first[] starts at 0,
+ * never decreases and stays <= len[i] (empty steps are allowed); a sequence with live
+ * entries has at least one step.  At most 2^31 steps.  The same steps hold for every
+ * layer and KV head.
+ */
+typedef struct kvs_steps {
+  const int64_t *step_off;      /* [num_seqs + 1] */
+  const int64_t *step_off_h;
+  const int32_t *first;         /* [step_off[num_seqs]] */
+  const int32_t *first_h;
+} kvs_steps;
+
+/* Bytes of workspace kvs_step_select needs: fp32 keys [L][Hkv][E]. */
+size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs);
+
+/*
+ * kvs_step_select -- StepKV, Abstract: step utility combined with token saliency
+ * ranks the prunable entries, and the top ones are kept under the budget.  Per
+ * stream (sequence, layer, KV head), with a_j = floor(s_j * 2^32):
+ *   U_k = fp32(floor(sum_{j in step k} a_j / |k|) * 2^-32)   (0 for an empty step),
+ *   c_j = fma(beta, U_k(j), fp32(fp32(1 - beta) * s_j)),
+ *   keep = the first K = min(budget[i], len[i]) entries of (c desc, s desc, slot asc).
+ * Every live entry is prunable.  scores: fp32 [L][Hkv][E], finite, >= 0, with the
+ * scores of any one step summing to less than 2^32.  beta in [0, 1].
+ * keep: uint8 [L][Hkv][E].  utility: fp32 [L][Hkv][num_steps] (U of every step) or
+ * NULL.  budget: int32 [num_seqs] device with its host mirror budget_h (>= 0).
+ * workspace: device, >= kvs_step_select_workspace_size(), 256-byte aligned; scratch.
+ * Exact: the keep set and the utilities are defined to the bit.  cache supplies the
+ * shape only (k, v and crf are not read).
+ */
+kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_steps *steps,
+                           const float *scores, float beta, const int32_t *budget,
+                           const int32_t *budget_h, uint8_t *keep, float *utility,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Per-stream capacity of the move-pair buffer for this batch and budget:
  *   P = max over sequences of min(len_i - K_i, K_i),  K_i = min(budget_h[i], len_i).
  * pairs must hold int32 [num_layers][num_kv_heads][num_seqs][P][2] and pair_count

@@ -25,7 +25,8 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_pair_capacity",
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
-           "kvs_decode_workspace_size", "kvs_decode_attention")
+           "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
+           "kvs_step_select")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -48,6 +49,11 @@ class Seqs(C.Structure):
                 ("start", C.c_void_p), ("start_h", C.c_void_p),
                 ("len", C.c_void_p), ("len_h", C.c_void_p),
                 ("entry_off", C.c_void_p), ("entry_off_h", C.c_void_p)]
+
+
+class Steps(C.Structure):
+    _fields_ = [("step_off", C.c_void_p), ("step_off_h", C.c_void_p), ("first", C.c_void_p),
+                ("first_h", C.c_void_p)]
 
 
 class Observers(C.Structure):
@@ -100,6 +106,10 @@ def lib() -> C.CDLL:
         L.kvs_decode_workspace_size.argtypes = [P, P, P, C.c_int32]
         L.kvs_decode_attention.restype = C.c_int
         L.kvs_decode_attention.argtypes = [P, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
+        L.kvs_step_select_workspace_size.restype = C.c_size_t
+        L.kvs_step_select_workspace_size.argtypes = [P, P]
+        L.kvs_step_select.restype = C.c_int
+        L.kvs_step_select.argtypes = [P, P, P, P, C.c_float, P, P, P, P, P, C.c_size_t, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
         L.kvs_token_confidence_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int32]
         L.kvs_token_confidence.restype = C.c_int
@@ -327,6 +337,42 @@ def kvs_decode_attention(cache: PagedCache, seqs: SeqBatch, queries: ObserverSet
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kvs_decode_attention(cache.ref, seqs.ref, queries.ref, C.c_float(scale), _ptr(out), _ptr(lse),
                                       _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+class StepSet:
+    """Reasoning steps per sequence: step_off int64 [S+1] (global step ids of sequence i
+    are step_off[i] .. step_off[i+1]-1) and first int32 [M] (first live slot of each
+    step), on the device with host mirrors."""
+
+    def __init__(self, step_off_h: np.ndarray, first_h: np.ndarray, device="cuda"):
+        import torch
+        self.step_off_h = np.ascontiguousarray(step_off_h, np.int64)
+        self.first_h = np.ascontiguousarray(first_h, np.int32)
+        self.step_off = torch.from_numpy(self.step_off_h).to(device)
+        self.first = torch.from_numpy(self.first_h).to(device) if self.first_h.size else None
+        self.t = Steps(_ptr(self.step_off), _ptr(self.step_off_h), _ptr(self.first),
+                       _ptr(self.first_h) if self.first_h.size else None)
+
+    @property
+    def num_steps(self) -> int:
+        return int(self.step_off_h[-1])
+
+    @property
+    def ref(self):
+        return C.byref(self.t)
+
+
+def kvs_step_select_workspace_size(cache: PagedCache, seqs: SeqBatch) -> int:
+    return int(lib().kvs_step_select_workspace_size(cache.ref, seqs.ref))
+
+
+def kvs_step_select(cache: PagedCache, seqs: SeqBatch, steps: StepSet, scores, beta: float, budget,
+                    budget_h: np.ndarray, keep, utility=None, workspace=None, stream=None) -> None:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvs_step_select(cache.ref, seqs.ref, steps.ref, _ptr(scores), C.c_float(beta), _ptr(budget),
+                                 _ptr(budget_h), _ptr(keep), _ptr(utility), _ptr(workspace), ws_bytes,
+                                 _stream(stream)))
 
 
 def kvs_token_confidence_workspace_size(rows: int, vocab: int, k: int = 20) -> int:

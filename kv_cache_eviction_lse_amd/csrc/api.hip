@@ -221,6 +221,79 @@ kvs_status kvs_select(const kvs_cache *cache, const kvs_seqs *seqs, const float 
   return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, (hipStream_t)stream));
 }
 
+namespace {
+
+// Step boundaries: step_off[0] = 0, non-decreasing; per sequence with steps,
+// first[step_off[i]] = 0 <= first[...] non-decreasing <= len[i]; a sequence with live
+// entries has at least one step.
+kvs_status check_steps(const kvs_steps *t, const kvs_seqs *s) {
+  if (!t) return fail(KVS_ERR_NULL, "steps is NULL");
+  if (!t->step_off || !t->step_off_h) return fail(KVS_ERR_NULL, "step_off is NULL");
+  if (t->step_off_h[0] != 0) return fail(KVS_ERR_SHAPE, "step_off[0] != 0");
+  const int64_t M = t->step_off_h[s->num_seqs];
+  if (M > (int64_t(1) << 31)) return fail(KVS_ERR_UNSUPPORTED, "%lld steps (max 2^31)", (long long)M);
+  if (M > 0 && (!t->first || !t->first_h)) return fail(KVS_ERR_NULL, "first is NULL");
+  for (int32_t i = 0; i < s->num_seqs; ++i) {
+    const int64_t k0 = t->step_off_h[i], k1 = t->step_off_h[i + 1];
+    if (k1 < k0) return fail(KVS_ERR_SHAPE, "step_off not monotone at %d", i);
+    const int32_t n = s->len_h[i];
+    if (k1 == k0) {
+      if (n > 0) return fail(KVS_ERR_SHAPE, "sequence %d has live entries but no step", i);
+      continue;
+    }
+    if (t->first_h[k0] != 0) return fail(KVS_ERR_SHAPE, "the first step of sequence %d does not start at slot 0", i);
+    for (int64_t k = k0 + 1; k < k1; ++k)
+      if (t->first_h[k] < t->first_h[k - 1] || t->first_h[k] > n)
+        return fail(KVS_ERR_SHAPE, "step %lld of sequence %d starts at %d: not in [%d, %d]", (long long)(k - k0), i,
+                    t->first_h[k], t->first_h[k - 1], n);
+  }
+  return KVS_OK;
+}
+
+}  // namespace
+
+size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs) {
+  if (check_cache(cache, false, false) != KVS_OK) return 0;
+  if (check_seqs(seqs, cache->num_pages, false) != KVS_OK) return 0;
+  if (seqs->num_seqs == 0) return 0;
+  const kvs::Batch b = make_batch(cache, seqs);
+  ok();
+  return (size_t)b.L * b.Hkv * (size_t)b.E * sizeof(float);
+}
+
+kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_steps *steps,
+                           const float *scores, float beta, const int32_t *budget, const int32_t *budget_h,
+                           uint8_t *keep, float *utility, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, false, false)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, false)) != KVS_OK) return st;
+  if (!(beta >= 0.f && beta <= 1.f)) return fail(KVS_ERR_SHAPE, "beta = %g not in [0, 1]", (double)beta);
+  if ((int64_t)cache->num_layers * cache->num_kv_heads > 65535)
+    return fail(KVS_ERR_UNSUPPORTED, "num_layers x num_kv_heads exceeds 65535");
+  if (seqs->num_seqs == 0) return ok();
+  if ((st = check_steps(steps, seqs)) != KVS_OK) return st;
+  if (!budget || !budget_h) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  if (!scores || !keep) return fail(KVS_ERR_NULL, "scores/keep is NULL");
+  const size_t need = (size_t)b.L * b.Hkv * (size_t)b.E * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float *keys = (float *)workspace;
+  const hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = kvs::launch_step_keys(b, scores, steps->step_off, steps->first, steps->step_off_h[seqs->num_seqs],
+                                       beta, keys, utility, hs);
+  if (e != hipSuccess) return hip_status(e);
+  const int32_t max_len = max_len_of(seqs);
+  if (kvs::stream_reg_fits(max_len, cache->num_pages, cache->num_kv_heads))
+    return hip_status(kvs::launch_stream_reg(*cache, b, scores, false, true, 0, 1, nullptr, nullptr, nullptr,
+                                             budget, keep, hs, keys));
+  return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, hs, keys));
+}
+
 kvs_status kvs_lrfu_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, uint32_t mass_num,
                            uint32_t mass_den, const float *decay, const int32_t *n_prev, uint8_t *hit,
                            const int32_t *budget, const int32_t *budget_h, uint8_t *keep, void *stream) {

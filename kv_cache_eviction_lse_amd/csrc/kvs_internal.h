@@ -45,14 +45,17 @@ hipError_t launch_lrfu(const kvs_cache &c, const Batch &b, const float *scores, 
                        uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
                        int32_t max_len, hipStream_t st);
 
+// keys (nullable): per-entry fp32 keys [L*Hkv][E] that take the CRF's place in the order.
 hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores,
-                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st);
+                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st,
+                         const float *keys = nullptr);
 
 // Register-resident cut + LRFU and/or top-B for streams of at most 32768 entries.
 bool stream_reg_fits(int32_t max_len, int64_t num_pages, int32_t Hkv);
 hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *scores, bool lrfu, bool select,
                              uint32_t num, uint32_t den, const float *decay, const int32_t *n_prev,
-                             uint8_t *hit, const int32_t *budget, uint8_t *keep, hipStream_t st);
+                             uint8_t *hit, const int32_t *budget, uint8_t *keep, hipStream_t st,
+                             const float *keys = nullptr);
 
 hipError_t launch_plan(const Batch &b, const uint8_t *keep, const int32_t *budget, int32_t *pairs,
                        int32_t *pair_count, int64_t pair_cap, hipStream_t st);
@@ -74,6 +77,10 @@ size_t decode_workspace_bytes(const Batch &b, int32_t G, const int64_t *tok_off_
 hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers &o, float scale, float *out,
                          float *lse, float *scores, void *ws, const int64_t *tok_off_h, const int32_t *len_h,
                          const int32_t *start_h, hipStream_t st);
+
+// Step-aware ranking keys (StepKV): c_j = beta U_step(j) + (1 - beta) s_j into keys.
+hipError_t launch_step_keys(const Batch &b, const float *scores, const int64_t *step_off, const int32_t *first,
+                            int64_t num_steps, float beta, float *keys, float *utility, hipStream_t st);
 
 // Token confidence (mean NLL of the k most probable tokens per logits row).
 int64_t conf_max_vocab();

@@ -2,7 +2,8 @@
 //
 // ActKV Dissected, Summary / Results: eviction keeps an entry budget.  Exactly
 // K = min(B, n) entries are kept per stream: the first K of the order
-// (CRF desc, s desc, slot asc) on fp32 bit patterns.  Selection runs in up to three
+// (CRF desc, s desc, slot asc) on fp32 bit patterns (step-aware ranking passes keys per
+// entry in place of the CRF).  Selection runs in up to three
 // levels, each only over the entries still tied:
 //   1. radix-select the K-th largest CRF value c* (CRF cached in LDS when it fits);
 //   2. among CRF == c*, radix-select s* so that the remaining count is met;
@@ -18,6 +19,7 @@ struct SelectArgs {
   const float *crf;
   const int32_t *budget;
   uint8_t *keep;
+  const float *keys;      // nullable: keys per entry [L*Hkv][E] in place of the CRF
   Batch b;
   int32_t cache_cap;
   int32_t bt_cap;
@@ -62,7 +64,9 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
   const int32_t *bt_use = bt_cached ? bt_lds : bt_row;
   const uint32_t *crf_base = (const uint32_t *)a.crf + (((int64_t)l * a.b.num_pages) * a.b.Hkv + g) * kPage;
   const int64_t page_stride = (int64_t)a.b.Hkv * kPage;
+  const uint32_t *kflat = a.keys ? (const uint32_t *)(a.keys + (int64_t)lg * a.b.E + e0) : nullptr;
   auto crf_addr = [&](int32_t j) -> const uint32_t * {
+    if (kflat) return kflat + j;
     const int32_t pos = start + j;
     return crf_base + (int64_t)bt_use[pos >> 4] * page_stride + (pos & 15);
   };
@@ -160,7 +164,8 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
 }  // namespace
 
 hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores,
-                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st) {
+                         const int32_t *budget, uint8_t *keep, int32_t max_len, hipStream_t st,
+                         const float *keys) {
   static bool attr_set = false;
   const int32_t cache = max_len <= kCacheCap ? max_len : 0;
   const size_t dyn = ((size_t)cache + kBtCap) * sizeof(uint32_t);
@@ -175,6 +180,7 @@ hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores
   a.crf = c.crf;
   a.budget = budget;
   a.keep = keep;
+  a.keys = keys;
   a.b = b;
   a.cache_cap = cache;
   a.bt_cap = kBtCap;

@@ -10,7 +10,8 @@
 // m = floor(s * 2^32); LRFU with lambda = 0.5 gives CRF <- fma(d, CRF, hit), the prior
 // taken as 0 for entries appended since the previous round.  Summary / Results: a
 // fixed entry budget per head keeps the first K = min(B, n) entries of
-// (CRF desc, s desc, slot asc).  Both orders compare fp32 bit patterns (values >= 0)
+// (CRF desc, s desc, slot asc) -- or, for step-aware ranking, of (key desc, s desc,
+// slot asc) with caller keys in place of the CRF.  Both orders compare fp32 bit patterns (values >= 0)
 // and ties at a threshold go to the lowest slots, so the results are exact.
 //
 // Selection: radix search on the key bits below the candidates' common prefix (from
@@ -41,6 +42,7 @@ struct StreamArgs {
   const int32_t *n_prev;
   const int32_t *budget;
   uint8_t *keep;
+  const float *keys;     // nullable: top-B keys per entry [L*Hkv][E] in place of the CRF
   Batch b;
   uint32_t num, den;
 };
@@ -364,7 +366,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       return;
     }
   } else {
-    gather_crf();
+    if (a.keys) {
+      const uint32_t *kf = (const uint32_t *)(a.keys + (int64_t)lg * a.b.E + e0);
+#pragma unroll
+      for (int u0 = 0; u0 < kRegU; u0 += 8) {
+        const int t = opaque(tid);
+#pragma unroll
+        for (int u = u0; u < u0 + 8; ++u) c[u] = kf[slot(u, t)];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      gather_crf();
+    }
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) c[u] = u < cnt ? c[u] : 0u;
   }
@@ -493,8 +506,10 @@ bool stream_reg_fits(int32_t max_len, int64_t num_pages, int32_t Hkv) {
 
 hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *scores, bool lrfu, bool select,
                              uint32_t num, uint32_t den, const float *decay, const int32_t *n_prev,
-                             uint8_t *hit, const int32_t *budget, uint8_t *keep, hipStream_t st) {
+                             uint8_t *hit, const int32_t *budget, uint8_t *keep, hipStream_t st,
+                             const float *keys) {
   StreamArgs a{};
+  a.keys = keys;
   a.scores = scores;
   a.crf = c.crf;
   a.hit = hit;

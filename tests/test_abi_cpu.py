@@ -274,3 +274,33 @@ def test_decode_attention_validation():
     c4 = _cache(Hkv=4, P=2)
     assert L.kvs_decode_attention(C.byref(c4), C.byref(hs.s), C.byref(q3), C.c_float(0.1), FAKE, FAKE, None,
                                   FAKE, 1 << 30, None) == 2
+
+
+def test_step_select_validation():
+    # every bad argument is refused on the host (status codes), before any HIP call
+    L = K.lib()
+    hs = HostSeqs([[0, 1], [2, 3]], [0, 3], [20, 9])
+    c = _cache(L=2, Hkv=2, P=4)
+    assert L.kvs_step_select_workspace_size(C.byref(c), C.byref(hs.s)) == 2 * 2 * 29 * 4
+    bud = np.array([5, 5], np.int32)
+
+    def run(off, first, beta=0.5, budget=bud, ws_bytes=1 << 20, steps=True):
+        off = np.ascontiguousarray(off, np.int64)
+        first = np.ascontiguousarray(first, np.int32)
+        t = K.Steps(FAKE, off.ctypes.data, FAKE, first.ctypes.data)
+        return L.kvs_step_select(C.byref(c), C.byref(hs.s), C.byref(t) if steps else None, FAKE,
+                                 C.c_float(beta), FAKE, budget.ctypes.data, FAKE, None, FAKE, ws_bytes, None)
+
+    good_off, good_first = [0, 3, 5], [0, 4, 11, 0, 9]       # the last step of sequence 1 is empty
+    for beta in (-0.1, 1.5, float("nan")):
+        assert run(good_off, good_first, beta=beta) == 2
+    assert run(good_off, good_first, steps=False) == 1
+    assert run([1, 3, 5], good_first) == 2                     # step_off[0] != 0
+    assert run([0, 3, 2], good_first) == 2                     # not monotone
+    assert run([0, 0, 2], [0, 3]) == 2                         # live entries without a step
+    assert run(good_off, [1, 4, 11, 0, 9]) == 2                # a sequence's steps start at slot 0
+    assert run(good_off, [0, 11, 4, 0, 9]) == 2                # boundaries decrease
+    assert run(good_off, [0, 4, 21, 0, 9]) == 2                # past the sequence end
+    assert run(good_off, good_first, budget=np.array([5, -1], np.int32)) == 2
+    assert run(good_off, good_first, ws_bytes=100) == 4
+    assert L.kvs_last_error().decode().startswith("workspace")

@@ -1,0 +1,143 @@
+"""GPU parity of step-aware ranking (kvs_step_select through the C ABI) against the
+oracle on the same scores and steps.  Keys are integer sums, one rounding of the step
+mean and one fused multiply-add, and the keep set is a selection on their bit
+patterns: the keep set and the step utilities must match bit for bit."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from oracle import stepkv_oracle as SO
+from workloads import steps as WS
+
+pytestmark = pytest.mark.gpu
+
+
+class ShapeCache:
+    """The cache structure with the shape only (kvs_step_select reads no pool)."""
+
+    def __init__(self, L, Hkv, P):
+        from kv_cache_eviction_lse_amd import _lib
+        self.c = _lib.Cache(None, None, None, L, Hkv, 128, 16, P)
+
+    @property
+    def ref(self):
+        return C.byref(self.c)
+
+
+def make_batch(seed, lengths, starts, L=2, Hkv=2, empty=0.1, quantum=None, zero=0.1):
+    rng = np.random.default_rng(seed)
+    S = len(lengths)
+    npg = [(int(st) + int(n) + 15) // 16 if n else 0 for n, st in zip(lengths, starts)]
+    P = max(sum(npg), 1)
+    perm = rng.permutation(P)
+    bt = np.zeros((S, max(max(npg), 1)), np.int32)
+    o = 0
+    for i in range(S):
+        bt[i, :npg[i]] = perm[o:o + npg[i]]
+        o += npg[i]
+    step_off, first, bounds = WS.batch_steps(rng, lengths, empty)
+    E = int(sum(lengths))
+    eo = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    s = np.zeros((L, Hkv, E), np.float32)
+    for i in range(S):
+        for l in range(L):
+            for g in range(Hkv):
+                if lengths[i]:
+                    s[l, g, eo[i]:eo[i + 1]] = WS.step_scores(rng, bounds[i], quantum=quantum, zero=zero)
+    return dict(L=L, Hkv=Hkv, P=P, bt=bt, start=np.asarray(starts, np.int32),
+                length=np.asarray(lengths, np.int32), step_off=step_off, first=first, bounds=bounds,
+                s=s, eo=eo)
+
+
+def gpu_step_select(d, beta, budget):
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    dev = torch.device("cuda", 0)
+    cache = ShapeCache(d["L"], d["Hkv"], d["P"])
+    seqs = K.SeqBatch(d["bt"], d["start"], d["length"], device=dev)
+    steps = K.StepSet(d["step_off"], d["first"], device=dev)
+    scores = torch.from_numpy(d["s"]).to(dev)
+    E = d["s"].shape[2]
+    keep = torch.full((d["L"], d["Hkv"], max(E, 1)), 7, dtype=torch.uint8, device=dev)
+    M = steps.num_steps
+    util = torch.full((d["L"], d["Hkv"], max(M, 1)), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kvs_step_select_workspace_size(cache, seqs), 256), dtype=torch.uint8, device=dev)
+    budget_h = np.asarray(budget, np.int32)
+    K.kvs_step_select(cache, seqs, steps, scores, beta, torch.from_numpy(budget_h).to(dev), budget_h, keep,
+                      utility=util, workspace=ws)
+    torch.cuda.synchronize()
+    raw = keep.cpu().numpy()[:, :, :E]
+    assert np.isin(raw, (0, 1)).all()            # every entry written (the buffer started at 7)
+    return raw.astype(bool), util.cpu().numpy()[:, :, :M]
+
+
+def check(d, beta, budget, keep, util):
+    so = d["step_off"]
+    for i in range(len(d["length"])):
+        n = int(d["length"][i])
+        if n == 0:
+            continue
+        e0, e1 = int(d["eo"][i]), int(d["eo"][i + 1])
+        for l in range(d["L"]):
+            for g in range(d["Hkv"]):
+                want_keep, _, want_u = SO.step_select(d["s"][l, g, e0:e1], d["bounds"][i], beta, int(budget[i]))
+                np.testing.assert_array_equal(util[l, g, so[i]:so[i + 1]], want_u, err_msg=f"U {i} {l} {g}")
+                got = keep[l, g, e0:e1]
+                assert got.sum() == min(int(budget[i]), n), (i, l, g)
+                np.testing.assert_array_equal(got, want_keep, err_msg=f"keep {i} {l} {g}")
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.3, 0.5, 1.0])
+def test_step_select_parity_ragged(beta):
+    # lengths with an empty sequence, one entry, partial first pages; budgets 0, < n, >= n
+    lengths = [700, 333, 0, 1, 16, 5000, 2049]
+    d = make_batch(41, lengths, [0, 9, 3, 15, 0, 7, 2])
+    budget = [256, 400, 5, 0, 8, 1000, 1]
+    print(f"step select ragged beta={beta}", flush=True)
+    keep, util = gpu_step_select(d, beta, budget)
+    check(d, beta, budget, keep, util)
+
+
+@pytest.mark.parametrize("quantum", [None, 1.0 / 64])
+def test_step_select_ties(quantum):
+    # quantised scores (many exact ties in s and in the keys) and many empty steps: the
+    # tie-breaking levels (s, then the slot) decide
+    lengths = [4000, 1500, 32768]
+    d = make_batch(42, lengths, [0, 5, 0], empty=0.3, quantum=quantum, zero=0.4)
+    budget = [1000, 700, 2048]
+    print(f"step select ties quantum={quantum}", flush=True)
+    for beta in (0.25, 1.0):
+        keep, util = gpu_step_select(d, beta, budget)
+        check(d, beta, budget, keep, util)
+
+
+def test_step_select_long_stream():
+    # a stream longer than 32 768 entries takes the LDS/global selection kernel
+    lengths = [40000, 300]
+    d = make_batch(43, lengths, [3, 0], L=1, Hkv=2)
+    budget = [4096, 100]
+    print("step select long", flush=True)
+    keep, util = gpu_step_select(d, 0.6, budget)
+    check(d, 0.6, budget, keep, util)
+
+
+def test_step_select_single_step_and_one_entry_steps():
+    # one step per sequence (every key is beta U + (1 - beta) s with the same U) and
+    # steps of one entry each (U = the entry's own grid value)
+    import torch  # noqa: F401
+    rng = np.random.default_rng(44)
+    lengths = [900, 257]
+    d = make_batch(44, lengths, [0, 0], L=1, Hkv=1)
+    for case in ("single", "unit"):
+        if case == "single":
+            d["bounds"] = [np.array([0, n], np.int64) for n in lengths]
+        else:
+            d["bounds"] = [np.arange(n + 1, dtype=np.int64) for n in lengths]
+        counts = [len(b) - 1 for b in d["bounds"]]
+        d["step_off"] = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+        d["first"] = np.concatenate([b[:-1] for b in d["bounds"]]).astype(np.int32)
+        budget = [int(rng.integers(1, 900)), 128]
+        print(f"step select {case}", flush=True)
+        keep, util = gpu_step_select(d, 0.5, budget)
+        check(d, 0.5, budget, keep, util)
