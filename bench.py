@@ -282,6 +282,116 @@ def bench_decode(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+SK_METRIC = ("KV entries ranked by step-aware selection (step utility + token saliency -> top-B keep "
+             "set)/sec; achieved HBM GB/s vs peak (8B shape, 32K ctx)")
+
+
+def bench_stepkv(args) -> None:
+    """kvs_step_select over the 8B-shaped batch (32 layers x 8 KV heads x 32 768 entries)
+    with an agent-trajectory step structure; one JSON line."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import ALL
+    from workloads import steps as WS
+    from workloads.host import make_layout
+    import oracle as O
+
+    w = ALL["llama3_8b_32k"]
+    lay = make_layout(w)
+    L, Hkv = w.num_layers, w.num_kv_heads
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(7)
+    step_off, first, bounds = WS.batch_steps(rng, lay.length)
+    E = int(lay.entry_off[-1])
+    s_h = np.empty((L, Hkv, E), np.float32)
+    for i in range(w.num_seqs):
+        e0, e1 = int(lay.entry_off[i]), int(lay.entry_off[i + 1])
+        for l in range(L):
+            for g in range(Hkv):
+                s_h[l, g, e0:e1] = WS.step_scores(rng, bounds[i])
+    beta = 0.5
+    cache = K.CacheShape(L, Hkv, lay.num_pages)
+    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
+    steps = K.StepSet(step_off, first, device=dev)
+    scores = torch.from_numpy(s_h).to(dev)
+    budget_h = np.full(w.num_seqs, w.budget, np.int32)
+    budget = torch.from_numpy(budget_h).to(dev)
+    keep = torch.empty((L, Hkv, E), dtype=torch.uint8, device=dev)
+    M = steps.num_steps
+    util = torch.empty((L, Hkv, M), dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvs_step_select_workspace_size(cache, seqs), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    run = lambda: K.kvs_step_select(cache, seqs, steps, scores, beta, budget, budget_h, keep, util, ws)  # noqa: E731
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+    t_settle = time.perf_counter() - t_settle
+    for _ in range(args.warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0_, e1_ in evs:
+        e0_.record(st)
+        run()
+        e1_.record(st)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    entries = E * L * Hkv
+    # scores read and keep bits written once per entry; per step its first slot and its
+    # utility per stream
+    byts = entries * (4 + 1) + M * (4 + 4 * L * Hkv) + 8 * (w.num_seqs + 1)
+    gbps = byts / (ev_ms / 1000.0) / 1e9
+    res = {
+        "metric": SK_METRIC, "value": entries / (ms / 1000.0), "unit": "entries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "stepkv_llama3_8b_32k", "layers": L, "kv_heads": Hkv, "context": int(lay.length[0]),
+                   "reasoning_steps": M, "budget": int(w.budget), "beta": beta,
+                   "entries_per_step": entries},
+        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "step_key_kernel + stream_reg_kernel (keys from the step utilities)",
+                     "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "ms": ev_ms, "bytes_per_launch": byts},
+        "setup_s": {"settle_s": round(t_settle, 2)},
+    }
+    if not args.no_cpu_baseline:
+        keep_g, util_g = keep.cpu().numpy(), util.cpu().numpy()
+        pick = np.random.default_rng(1).permutation(L * Hkv)
+        t_cpu, n_done, streams, mism = 0.0, 0, 0, 0
+        while t_cpu < args.cpu_seconds:
+            for p in pick:
+                l, g = divmod(int(p), Hkv)
+                for i in range(w.num_seqs):
+                    e0, e1 = int(lay.entry_off[i]), int(lay.entry_off[i + 1])
+                    ta = time.perf_counter()
+                    kw, _, uw = O.stepkv.step_select(s_h[l, g, e0:e1], bounds[i], beta, int(budget_h[i]))
+                    t_cpu += time.perf_counter() - ta
+                    n_done += e1 - e0
+                    if streams < L * Hkv:
+                        mism += int(np.sum(kw != keep_g[l, g, e0:e1].astype(bool)))
+                        mism += int(np.sum(uw != util_g[l, g, step_off[i]:step_off[i + 1]]))
+                if streams < L * Hkv:
+                    streams += 1
+                if t_cpu >= args.cpu_seconds:
+                    break
+        res["cpu_baseline"] = {"value": n_done / t_cpu, "unit": "entries/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n_done} entries ({streams} distinct streams of {L * Hkv}) in "
+                                         f"{t_cpu:.1f} s of oracle time (numpy and exact integer sums)"}
+        res["parity"] = {"streams": streams, "mismatches": mism}
+    if args.calibration_copy:
+        src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +423,9 @@ def main():
         return
     if args.workload == "decode_llama3_8b_32k":
         bench_decode(args)
+        return
+    if args.workload == "stepkv_llama3_8b_32k":
+        bench_stepkv(args)
         return
     from workloads import ALL
     from workloads.host import make_layout, observers

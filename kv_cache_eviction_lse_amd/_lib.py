@@ -163,6 +163,18 @@ class PagedCache:
         return C.byref(self.c)
 
 
+class CacheShape:
+    """The cache structure with its shape only, for calls that read no pool
+    (kvs_step_select)."""
+
+    def __init__(self, num_layers: int, num_kv_heads: int, num_pages: int):
+        self.c = Cache(None, None, None, num_layers, num_kv_heads, 128, 16, num_pages)
+
+    @property
+    def ref(self):
+        return C.byref(self.c)
+
+
 class SeqBatch:
     """Device arrays plus their host mirrors (numpy) for a batch of sequences."""
 

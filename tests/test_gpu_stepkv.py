@@ -2,8 +2,6 @@
 oracle on the same scores and steps.  Keys are integer sums, one rounding of the step
 mean and one fused multiply-add, and the keep set is a selection on their bit
 patterns: the keep set and the step utilities must match bit for bit."""
-import ctypes as C
-
 import numpy as np
 import pytest
 
@@ -11,18 +9,6 @@ from oracle import stepkv_oracle as SO
 from workloads import steps as WS
 
 pytestmark = pytest.mark.gpu
-
-
-class ShapeCache:
-    """The cache structure with the shape only (kvs_step_select reads no pool)."""
-
-    def __init__(self, L, Hkv, P):
-        from kv_cache_eviction_lse_amd import _lib
-        self.c = _lib.Cache(None, None, None, L, Hkv, 128, 16, P)
-
-    @property
-    def ref(self):
-        return C.byref(self.c)
 
 
 def make_batch(seed, lengths, starts, L=2, Hkv=2, empty=0.1, quantum=None, zero=0.1):
@@ -54,7 +40,7 @@ def gpu_step_select(d, beta, budget):
     import torch
     import kv_cache_eviction_lse_amd as K
     dev = torch.device("cuda", 0)
-    cache = ShapeCache(d["L"], d["Hkv"], d["P"])
+    cache = K.CacheShape(d["L"], d["Hkv"], d["P"])
     seqs = K.SeqBatch(d["bt"], d["start"], d["length"], device=dev)
     steps = K.StepSet(d["step_off"], d["first"], device=dev)
     scores = torch.from_numpy(d["s"]).to(dev)
