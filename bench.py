@@ -319,7 +319,8 @@ def bench_stepkv(args) -> None:
     keep = torch.empty((L, Hkv, E), dtype=torch.uint8, device=dev)
     M = steps.num_steps
     util = torch.empty((L, Hkv, M), dtype=torch.float32, device=dev)
-    ws = torch.empty(K.kvs_step_select_workspace_size(cache, seqs), dtype=torch.uint8, device=dev)
+    need = K.kvs_step_select_workspace_size(cache, seqs, steps)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()
     run = lambda: K.kvs_step_select(cache, seqs, steps, scores, beta, budget, budget_h, keep, util, ws)  # noqa: E731
     t_settle = time.perf_counter()
@@ -355,7 +356,9 @@ def bench_stepkv(args) -> None:
         "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
         "roofline": {"kernel": "step_key_kernel + stream_reg_kernel (keys from the step utilities)",
                      "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "ms": ev_ms, "bytes_per_launch": byts},
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("stepkv_llama3_8b_32k", "stream_reg", "stream.hip"),
+                     "traffic_of": "stream_reg_kernel", "ms": ev_ms, "bytes_per_launch": byts},
         "setup_s": {"settle_s": round(t_settle, 2)},
     }
     if not args.no_cpu_baseline:

@@ -224,8 +224,10 @@ typedef struct kvs_steps {
   const int32_t *first_h;
 } kvs_steps;
 
-/* Bytes of workspace kvs_step_select needs: fp32 keys [L][Hkv][E]. */
-size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs);
+/* Bytes of workspace kvs_step_select needs (the combined keys, fp32 [L][Hkv][E]); 0 on
+ * invalid arguments (kvs_last_error() says which). */
+size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs,
+                                      const kvs_steps *steps);
 
 /*
  * kvs_step_select -- StepKV, Abstract: step utility combined with token saliency

@@ -107,7 +107,7 @@ def lib() -> C.CDLL:
         L.kvs_decode_attention.restype = C.c_int
         L.kvs_decode_attention.argtypes = [P, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
         L.kvs_step_select_workspace_size.restype = C.c_size_t
-        L.kvs_step_select_workspace_size.argtypes = [P, P]
+        L.kvs_step_select_workspace_size.argtypes = [P, P, P]
         L.kvs_step_select.restype = C.c_int
         L.kvs_step_select.argtypes = [P, P, P, P, C.c_float, P, P, P, P, P, C.c_size_t, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
@@ -374,8 +374,8 @@ class StepSet:
         return C.byref(self.t)
 
 
-def kvs_step_select_workspace_size(cache: PagedCache, seqs: SeqBatch) -> int:
-    return int(lib().kvs_step_select_workspace_size(cache.ref, seqs.ref))
+def kvs_step_select_workspace_size(cache: PagedCache, seqs: SeqBatch, steps: StepSet) -> int:
+    return int(lib().kvs_step_select_workspace_size(cache.ref, seqs.ref, steps.ref))
 
 
 def kvs_step_select(cache: PagedCache, seqs: SeqBatch, steps: StepSet, scores, beta: float, budget,

@@ -252,13 +252,21 @@ kvs_status check_steps(const kvs_steps *t, const kvs_seqs *s) {
 
 }  // namespace
 
-size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs) {
+namespace {
+
+// The combined keys of every entry, fp32 [L][Hkv][E].
+size_t step_ws_bytes(const kvs::Batch &b) { return (size_t)b.L * b.Hkv * (size_t)b.E * sizeof(float); }
+
+}  // namespace
+
+size_t kvs_step_select_workspace_size(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_steps *steps) {
   if (check_cache(cache, false, false) != KVS_OK) return 0;
   if (check_seqs(seqs, cache->num_pages, false) != KVS_OK) return 0;
   if (seqs->num_seqs == 0) return 0;
+  if (check_steps(steps, seqs) != KVS_OK) return 0;
   const kvs::Batch b = make_batch(cache, seqs);
   ok();
-  return (size_t)b.L * b.Hkv * (size_t)b.E * sizeof(float);
+  return step_ws_bytes(b);
 }
 
 kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_steps *steps,
@@ -279,11 +287,11 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
   const kvs::Batch b = make_batch(cache, seqs);
   if (b.E == 0) return ok();
   if (!scores || !keep) return fail(KVS_ERR_NULL, "scores/keep is NULL");
-  const size_t need = (size_t)b.L * b.Hkv * (size_t)b.E * sizeof(float);
+  const size_t need = step_ws_bytes(b);
   if (!workspace || workspace_bytes < need)
     return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  float *keys = (float *)workspace;
   const hipStream_t hs = (hipStream_t)stream;
+  float *keys = (float *)workspace;
   hipError_t e = kvs::launch_step_keys(b, scores, steps->step_off, steps->first, steps->step_off_h[seqs->num_seqs],
                                        beta, keys, utility, hs);
   if (e != hipSuccess) return hip_status(e);

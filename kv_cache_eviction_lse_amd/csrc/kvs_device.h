@@ -184,6 +184,18 @@ __device__ __forceinline__ uint64_t fixed_mass(uint32_t bits) {
   return bits < 0x7F800000u ? m : 0ull;
 }
 
+// Nearest fp32 (ties to even) to an unsigned 64-bit integer, by integer steps.
+__device__ __forceinline__ float u64_to_f32_rn(uint64_t x) {
+  if (x < (1ull << 24)) return (float)(uint32_t)x;             // exact
+  const int e = 63 - __clzll((long long)x);                     // 2^e <= x < 2^(e+1), e >= 24
+  const int sh = e - 23;
+  uint64_t m = x >> sh;                                         // the 24 leading bits
+  const uint64_t rem = x & ((1ull << sh) - 1ull);
+  const uint64_t half = 1ull << (sh - 1);
+  m += (rem > half || (rem == half && (m & 1ull))) ? 1ull : 0ull;   // 2^24 at most: exact below
+  return __builtin_ldexpf((float)(uint32_t)m, sh);
+}
+
 // Address of the CRF of live slot j of a stream.
 __device__ __forceinline__ float *crf_slot(float *crf, const int32_t *bt_row, int32_t start, int32_t j,
                                            int32_t l, int32_t g, int64_t num_pages, int32_t Hkv) {

@@ -31,18 +31,6 @@ struct StepArgs {
   float w;                    // fp32(1 - beta)
 };
 
-// Nearest fp32 (ties to even) to an unsigned 64-bit integer, by integer steps.
-__device__ __forceinline__ float u64_to_f32_rn(uint64_t x) {
-  if (x < (1ull << 24)) return (float)(uint32_t)x;             // exact
-  const int e = 63 - __clzll((long long)x);                     // 2^e <= x < 2^(e+1), e >= 24
-  const int sh = e - 23;
-  uint64_t m = x >> sh;                                         // the 24 leading bits
-  const uint64_t rem = x & ((1ull << sh) - 1ull);
-  const uint64_t half = 1ull << (sh - 1);
-  m += (rem > half || (rem == half && (m & 1ull))) ? 1ull : 0ull;   // 2^24 at most: exact below
-  return __builtin_ldexpf((float)(uint32_t)m, sh);
-}
-
 constexpr int kStepWaves = 4;
 
 __global__ __launch_bounds__(64 * kStepWaves) void step_key_kernel(StepArgs a) {
@@ -64,15 +52,29 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_key_kernel(StepArgs a) {
   const int32_t last = gk + 1 < a.step_off[i + 1] ? a.first[gk + 1] : n;     // one past the step
   const int64_t e0 = a.b.entry_off[i];
   const uint32_t *sp = (const uint32_t *)(a.scores + (int64_t)lg * a.b.E + e0);
+  // four loads in flight per lane, then the tail
   uint64_t sum = 0;
-  for (int32_t j = first + lane; j < last; j += 64) sum += fixed_mass(sp[j]);
+  int32_t j = first + lane;
+  for (; j + 192 < last; j += 256) {
+    const uint32_t x0 = sp[j], x1 = sp[j + 64], x2 = sp[j + 128], x3 = sp[j + 192];
+    sum += (fixed_mass(x0) + fixed_mass(x1)) + (fixed_mass(x2) + fixed_mass(x3));
+  }
+  for (; j < last; j += 64) sum += fixed_mass(sp[j]);
   sum = wave_sum_u64(sum);
   const int32_t len = last - first;
   const float U = len > 0 ? u64_to_f32_rn(sum / (uint64_t)len) * 0x1p-32f : 0.f;   // scaling is exact
   if (a.utility && lane == 0) a.utility[(int64_t)lg * a.M + gk] = U;
   float *kp = a.keys + (int64_t)lg * a.b.E + e0;
-  for (int32_t j = first + lane; j < last; j += 64)
-    kp[j] = __builtin_fmaf(a.beta, U, a.w * __uint_as_float(sp[j]));
+  auto key = [&](uint32_t x) { return __builtin_fmaf(a.beta, U, a.w * __uint_as_float(x)); };
+  j = first + lane;
+  for (; j + 192 < last; j += 256) {
+    const uint32_t x0 = sp[j], x1 = sp[j + 64], x2 = sp[j + 128], x3 = sp[j + 192];
+    kp[j] = key(x0);
+    kp[j + 64] = key(x1);
+    kp[j + 128] = key(x2);
+    kp[j + 192] = key(x3);
+  }
+  for (; j < last; j += 64) kp[j] = key(sp[j]);
 }
 
 }  // namespace

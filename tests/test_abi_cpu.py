@@ -281,7 +281,6 @@ def test_step_select_validation():
     L = K.lib()
     hs = HostSeqs([[0, 1], [2, 3]], [0, 3], [20, 9])
     c = _cache(L=2, Hkv=2, P=4)
-    assert L.kvs_step_select_workspace_size(C.byref(c), C.byref(hs.s)) == 2 * 2 * 29 * 4
     bud = np.array([5, 5], np.int32)
 
     def run(off, first, beta=0.5, budget=bud, ws_bytes=1 << 20, steps=True):
@@ -302,5 +301,10 @@ def test_step_select_validation():
     assert run(good_off, [0, 11, 4, 0, 9]) == 2                # boundaries decrease
     assert run(good_off, [0, 4, 21, 0, 9]) == 2                # past the sequence end
     assert run(good_off, good_first, budget=np.array([5, -1], np.int32)) == 2
-    assert run(good_off, good_first, ws_bytes=100) == 4
-    assert L.kvs_last_error().decode().startswith("workspace")
+    off = np.array([0, 3, 5], np.int64)
+    first = np.array([0, 4, 11, 0, 9], np.int32)
+    t = K.Steps(FAKE, off.ctypes.data, FAKE, first.ctypes.data)
+    assert L.kvs_step_select_workspace_size(C.byref(c), C.byref(hs.s), C.byref(t)) == 2 * 2 * 29 * 4
+    st = L.kvs_step_select(C.byref(c), C.byref(hs.s), C.byref(t), FAKE, C.c_float(0.5), FAKE,
+                           bud.ctypes.data, FAKE, None, FAKE, 100, None)
+    assert st == 4 and L.kvs_last_error().decode().startswith("workspace")

@@ -48,7 +48,8 @@ def gpu_step_select(d, beta, budget):
     keep = torch.full((d["L"], d["Hkv"], max(E, 1)), 7, dtype=torch.uint8, device=dev)
     M = steps.num_steps
     util = torch.full((d["L"], d["Hkv"], max(M, 1)), float("nan"), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(K.kvs_step_select_workspace_size(cache, seqs), 256), dtype=torch.uint8, device=dev)
+    need = K.kvs_step_select_workspace_size(cache, seqs, steps)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     budget_h = np.asarray(budget, np.int32)
     K.kvs_step_select(cache, seqs, steps, scores, beta, torch.from_numpy(budget_h).to(dev), budget_h, keep,
                       utility=util, workspace=ws)
@@ -63,6 +64,7 @@ def check(d, beta, budget, keep, util):
     for i in range(len(d["length"])):
         n = int(d["length"][i])
         if n == 0:
+            assert np.all(util[:, :, so[i]:so[i + 1]] == 0.0)     # empty steps have U = 0
             continue
         e0, e1 = int(d["eo"][i]), int(d["eo"][i + 1])
         for l in range(d["L"]):
@@ -110,20 +112,22 @@ def test_step_select_long_stream():
 
 def test_step_select_single_step_and_one_entry_steps():
     # one step per sequence (every key is beta U + (1 - beta) s with the same U) and
-    # steps of one entry each (U = the entry's own grid value)
-    import torch  # noqa: F401
+    # steps of one entry each (U = the entry's own grid value; 2 500 steps in one
+    # sequence)
+    # (and a sequence with no entries but two empty steps)
     rng = np.random.default_rng(44)
-    lengths = [900, 257]
-    d = make_batch(44, lengths, [0, 0], L=1, Hkv=1)
+    lengths = [2500, 257, 0]
+    d = make_batch(44, lengths, [0, 0, 0], L=1, Hkv=1)
     for case in ("single", "unit"):
         if case == "single":
-            d["bounds"] = [np.array([0, n], np.int64) for n in lengths]
+            d["bounds"] = [np.array([0, n], np.int64) for n in lengths[:2]]
         else:
-            d["bounds"] = [np.arange(n + 1, dtype=np.int64) for n in lengths]
+            d["bounds"] = [np.arange(n + 1, dtype=np.int64) for n in lengths[:2]]
+        d["bounds"].append(np.zeros(3, np.int64))
         counts = [len(b) - 1 for b in d["bounds"]]
         d["step_off"] = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
         d["first"] = np.concatenate([b[:-1] for b in d["bounds"]]).astype(np.int32)
-        budget = [int(rng.integers(1, 900)), 128]
+        budget = [int(rng.integers(1, 2500)), 128, 4]
         print(f"step select {case}", flush=True)
         keep, util = gpu_step_select(d, 0.5, budget)
         check(d, 0.5, budget, keep, util)
