@@ -1,0 +1,116 @@
+"""Pins of the beacon k-means oracle (oracle/kmeans_oracle.py): a hand-worked example,
+scikit-learn's Lloyd k-means on separated groups, the one-group mean, tie and
+empty-group rules, exact invariances, the non-increasing objective, and the bf16
+rounding against torch."""
+import numpy as np
+import pytest
+
+from oracle import kmeans_oracle as KO
+
+rng = np.random.default_rng(77)
+D = 128
+
+
+def line_points(vals):
+    x = np.zeros((len(vals), D))
+    x[:, 0] = vals
+    return x
+
+
+def test_hand_worked_example():
+    # points 0, 1, 10, 11 on the first axis; centroids 0 and 10: one iteration assigns
+    # {0, 1} and {10, 11} and moves the centroids to 0.5 and 10.5; a second changes nothing
+    x = line_points([0.0, 1.0, 10.0, 11.0])
+    c0 = np.zeros((2, D), np.float32)
+    c0[1, 0] = 10.0
+    c, a = KO.lloyd(x, c0, 1)
+    np.testing.assert_array_equal(a, [0, 0, 1, 1])
+    assert c[0, 0] == 0.5 and c[1, 0] == 10.5 and np.all(c[:, 1:] == 0)
+    c2, a2 = KO.lloyd(x, c0, 2)
+    np.testing.assert_array_equal(c2, c)
+    np.testing.assert_array_equal(a2, a)
+    # on the 2^-16 grid a coordinate is truncated toward zero before the mean:
+    # 3 2^-17 -> 2^-16 and -3 2^-17 -> -2^-16
+    y = line_points([3 * 2.0 ** -17, -3 * 2.0 ** -17])
+    c1 = KO.update(y, np.array([0, 1]), np.zeros((2, D), np.float32))
+    assert c1[0, 0] == np.float32(2.0 ** -16) and c1[1, 0] == np.float32(-(2.0 ** -16))
+
+
+def test_matches_scikit_learn_on_separated_groups():
+    # 8 well separated groups: labels match scikit-learn's Lloyd k-means exactly and the
+    # centroids to the grid spacing (scikit-learn takes the mean in fp64 without the grid)
+    from sklearn.cluster import KMeans
+    K, n = 8, 600
+    centers = rng.normal(0.0, 4.0, (K, D))
+    lab = rng.integers(0, K, n)
+    x = centers[lab] + rng.normal(0.0, 0.3, (n, D))
+    x = x.astype(np.float32).astype(np.float64)
+    c0 = x[[int(np.nonzero(lab == k)[0][0]) for k in range(K)]].astype(np.float32)
+    c, a = KO.lloyd(x, c0, 10)
+    km = KMeans(n_clusters=K, init=c0.astype(np.float64), n_init=1, max_iter=10, algorithm="lloyd", tol=0.0)
+    km.fit(x)
+    np.testing.assert_array_equal(a, km.labels_)
+    np.testing.assert_allclose(c, km.cluster_centers_, atol=2.0 ** -16 * 1.01, rtol=1e-6)
+    # initial centroid k is a member of planted group k, and the groups are far apart
+    np.testing.assert_array_equal(a, lab)
+
+
+def test_one_group_is_the_mean():
+    # K = 1: the centroid is the mean of all points; small integers with a power-of-two
+    # count give an exact mean
+    x = rng.integers(-50, 50, (64, D)).astype(np.float64)
+    c, a = KO.lloyd(x, np.zeros((1, D), np.float32), 1)
+    np.testing.assert_array_equal(c[0], x.mean(axis=0).astype(np.float32))
+    assert np.all(a == 0)
+
+
+def test_ties_and_empty_groups():
+    x = rng.normal(size=(50, D))
+    c0 = np.zeros((3, D), np.float32)
+    c0[0] = c0[1] = x[0].astype(np.float32)          # two equal centroids: the lower one wins
+    c0[2] = 1000.0                                   # far away: stays empty, keeps its centroid
+    c, a = KO.lloyd(x, c0, 1)
+    assert np.all(a == 0)
+    np.testing.assert_array_equal(c[1], c0[1])
+    np.testing.assert_array_equal(c[2], c0[2])
+
+
+def test_invariances():
+    x = rng.normal(size=(300, D)).astype(np.float32).astype(np.float64)
+    c0 = x[:6].astype(np.float32)
+    c, a = KO.lloyd(x, c0, 4)
+    # the order of the points changes nothing (integer sums)
+    perm = rng.permutation(300)
+    cp, ap = KO.lloyd(x[perm], c0, 4)
+    np.testing.assert_array_equal(cp, c)
+    np.testing.assert_array_equal(ap, a[perm])
+    # a translation by an integer vector translates the centroids exactly (on the grid)
+    shift = rng.integers(-3, 4, D).astype(np.float64)
+    ct, at = KO.lloyd(x + shift, (c0 + shift).astype(np.float32), 4)
+    np.testing.assert_array_equal(at, a)
+    np.testing.assert_allclose(ct, c + shift, atol=2.0 ** -16 * 4)
+
+
+def test_objective_does_not_increase():
+    x = rng.normal(size=(800, D))
+    c = x[:16].astype(np.float32)
+    prev = np.inf
+    for _ in range(8):
+        a, sc = KO.assign(x, c)
+        obj = float(np.sum(sc[np.arange(len(a)), a]) + np.sum(x * x))
+        assert obj <= prev * (1 + 1e-9) + 1e-6
+        prev = obj
+        c = KO.update(x, a, c)
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    v = np.concatenate([rng.normal(size=1000) * 10.0 ** rng.integers(-5, 5, 1000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(KO.to_bf16_bits(v), want)
+
+
+def test_bad_points():
+    with pytest.raises(ValueError):
+        KO.lloyd(line_points([2.0 ** 15]), np.zeros((1, D), np.float32), 1)
