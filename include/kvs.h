@@ -250,6 +250,27 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kvs_beacon_kmeans -- BeaconKV, Key ideas: queries that revisit distant context form
+ * a few similarity groups, and one representative per group (a beacon query) joins the
+ * recent queries as an observer.  Lloyd's k-means for num_problems independent
+ * problems (one per layer and query head, say), each over num_points history queries
+ * of 128 bf16 values, from given initial centroids, for iters iterations:
+ *   assignment  a_i = the k minimising ||c_k||^2 - 2 <x_i, c_k> (ties to the lower k),
+ *               taken in fp32 (products carry the full fp32 centroid);
+ *   update      c_kd = fp32(fp64(sum over members of trunc(x_id * 2^16)) / n_k * 2^-16),
+ *               exact integer sums; a group without members keeps its centroid.
+ * points: bf16 [num_problems][num_points][128], finite with |x| < 2^15.
+ * centroids: fp32 [num_problems][k][128], the initial centroids in, the final out.
+ * assign: int32 [num_problems][num_points] (the last iteration's assignments; not
+ * written when iters = 0) or NULL.  beacons: bf16 [num_problems][k][128] (the final
+ * centroids rounded to nearest, ties to even) or NULL.  1 <= k <= 16, num_points >= 1,
+ * iters >= 0.  One workgroup per problem; no workspace.
+ */
+kvs_status kvs_beacon_kmeans(const void *points, int64_t num_problems, int32_t num_points, int32_t k,
+                             int32_t iters, float *centroids, int32_t *assign, void *beacons,
+                             void *stream);
+
+/*
  * Per-stream capacity of the move-pair buffer for this batch and budget:
  *   P = max over sequences of min(len_i - K_i, K_i),  K_i = min(budget_h[i], len_i).
  * pairs must hold int32 [num_layers][num_kv_heads][num_seqs][P][2] and pair_count

@@ -26,7 +26,7 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
            "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
-           "kvs_step_select")
+           "kvs_step_select", "kvs_beacon_kmeans")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -110,6 +110,8 @@ def lib() -> C.CDLL:
         L.kvs_step_select_workspace_size.argtypes = [P, P, P]
         L.kvs_step_select.restype = C.c_int
         L.kvs_step_select.argtypes = [P, P, P, P, C.c_float, P, P, P, P, P, C.c_size_t, P]
+        L.kvs_beacon_kmeans.restype = C.c_int
+        L.kvs_beacon_kmeans.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
         L.kvs_token_confidence_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_int32]
         L.kvs_token_confidence.restype = C.c_int
@@ -385,6 +387,14 @@ def kvs_step_select(cache: PagedCache, seqs: SeqBatch, steps: StepSet, scores, b
     _check(lib().kvs_step_select(cache.ref, seqs.ref, steps.ref, _ptr(scores), C.c_float(beta), _ptr(budget),
                                  _ptr(budget_h), _ptr(keep), _ptr(utility), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+
+
+def kvs_beacon_kmeans(points, centroids, iters: int, assign=None, beacons=None, stream=None) -> None:
+    """points bf16 [P][N][128]; centroids fp32 [P][K][128] (initial in, final out)."""
+    P, N, D = points.shape
+    assert D == 128 and centroids.shape[0] == P and centroids.shape[2] == 128
+    _check(lib().kvs_beacon_kmeans(_ptr(points), P, N, int(centroids.shape[1]), int(iters), _ptr(centroids),
+                                   _ptr(assign), _ptr(beacons), _stream(stream)))
 
 
 def kvs_token_confidence_workspace_size(rows: int, vocab: int, k: int = 20) -> int:

@@ -1,6 +1,7 @@
 // libkvs C ABI: host-side validation, launch planning and the host-only outputs.
 // Every entry point checks its arguments before any HIP call; on error it enqueues
 // nothing and returns a status (detail in kvs_last_error()).
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -300,6 +301,20 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
     return hip_status(kvs::launch_stream_reg(*cache, b, scores, false, true, 0, 1, nullptr, nullptr, nullptr,
                                              budget, keep, hs, keys));
   return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, hs, keys));
+}
+
+kvs_status kvs_beacon_kmeans(const void *points, int64_t num_problems, int32_t num_points, int32_t k, int32_t iters,
+                             float *centroids, int32_t *assign, void *beacons, void *stream) {
+  if (num_problems < 0 || num_problems > INT32_MAX)
+    return fail(KVS_ERR_SHAPE, "num_problems = %lld not in [0, 2^31)", (long long)num_problems);
+  if (num_points < 1) return fail(KVS_ERR_SHAPE, "num_points = %d < 1", num_points);
+  if (k < 1 || k > kvs::kmeans_max_k())
+    return fail(KVS_ERR_UNSUPPORTED, "k = %d not in [1, %d]", k, kvs::kmeans_max_k());
+  if (iters < 0) return fail(KVS_ERR_SHAPE, "iters = %d < 0", iters);
+  if (num_problems == 0) return ok();
+  if (!points || !centroids) return fail(KVS_ERR_NULL, "points/centroids is NULL");
+  return hip_status(kvs::launch_kmeans((const uint16_t *)points, num_problems, num_points, k, iters, centroids,
+                                       assign, (uint16_t *)beacons, (hipStream_t)stream));
 }
 
 kvs_status kvs_lrfu_select(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores, uint32_t mass_num,

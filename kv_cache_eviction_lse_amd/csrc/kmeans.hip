@@ -1,0 +1,197 @@
+// kvs_beacon_kmeans: Lloyd k-means over each (layer, query head)'s history queries,
+// for beacon queries.
+//
+// BeaconKV Compresses KV Cache for Long-Reasoning Models with Beacon Queries, Key
+// ideas: queries that revisit distant context fall into a few similarity groups, and
+// one representative per group (a beacon) is kept beside the recent queries.  The
+// groups are found here by Lloyd's k-means from given initial centroids:
+//   assignment  a_i = argmin_k ||c_k||^2 - 2 <x_i, c_k>   (ties to the lower k);
+//   update      c_kd = fp32(fp64(sum_i trunc(x_id 2^16)) / n_k * 2^-16) over the members,
+//               integer sums so the result does not depend on their order; an empty
+//               group keeps its centroid.
+//
+// One 256-thread workgroup per problem keeps the centroids in LDS for all iterations.
+// Per 16-point tile a wave computes the 16 x 16 block of <c_k, x_i> on
+// v_mfma_f32_16x16x32_bf16 with the centroids on M (each fp32 centroid split into three
+// bf16 parts, so the products carry its full precision) and the points on N (each lane
+// loads 16 bytes of one point row per slice), takes the argmin, then adds the tile's
+// points to their groups' integer sums with LDS 64-bit atomics (lane = two dimensions;
+// the rows come back from the cache that just served the MFMA operands).
+#include "kvs_device.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kKmMaxK = 16;
+constexpr int kKmThreads = 256;
+constexpr int kKmWaves = kKmThreads / 64;
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float kfloatx4;
+
+struct KmArgs {
+  const uint16_t *x;       // bf16 [P][N][128]
+  float *cent;             // fp32 [P][K][128]: initial in, final out
+  int32_t *assign;         // int32 [P][N] or null
+  uint16_t *beacons;       // bf16 [P][K][128] or null
+  int32_t N, K, T;
+};
+
+__device__ __forceinline__ uint16_t bf16_rn(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float km_wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
+  __shared__ float c_lds[kKmMaxK][kHeadDim];
+  __shared__ float cn_lds[kKmMaxK];
+  __shared__ unsigned long long sum_lds[kKmMaxK][kHeadDim];
+  __shared__ uint32_t cnt_lds[kKmMaxK];
+
+  const int64_t p = blockIdx.x;
+  const int32_t N = a.N, K = a.K;
+  const uint16_t *xp = a.x + p * (int64_t)N * kHeadDim;
+  float *cp = a.cent + p * (int64_t)K * kHeadDim;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int blk = lane >> 4, n16 = lane & 15;
+  for (int e = tid; e < kKmMaxK * kHeadDim; e += kKmThreads) {
+    const int k = e / kHeadDim, d = e % kHeadDim;
+    c_lds[k][d] = k < K ? cp[k * kHeadDim + d] : 0.f;
+  }
+  const int32_t ntiles = (N + 15) / 16;
+
+  for (int32_t t = 0; t < a.T; ++t) {
+    for (int e = tid; e < kKmMaxK * kHeadDim; e += kKmThreads) sum_lds[e / kHeadDim][e % kHeadDim] = 0ull;
+    if (tid < kKmMaxK) cnt_lds[tid] = 0u;
+    __syncthreads();                                   // c_lds (initial or updated) visible
+    // ||c_k||^2: wave w takes groups 4w .. 4w+3 (groups beyond K score +inf)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 4 * wave + q;
+      const float v0 = c_lds[k][2 * lane], v1 = c_lds[k][2 * lane + 1];
+      const float s = km_wave_sum(__builtin_fmaf(v1, v1, v0 * v0));
+      if (lane == 0) cn_lds[k] = k < K ? s : __builtin_inff();
+    }
+    // MFMA A operands: lane (group n16, block blk) holds dims 32 sl + 8 blk .. + 7 of its
+    // group's centroid as hi + mid + lo bf16 parts
+    bf16x8 ah[4], am[4], al[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = c_lds[n16][32 * sl + 8 * blk + e];
+        const uint16_t h = bf16_rn(c);
+        const float r1 = c - bf16_f(h);
+        const uint16_t m = bf16_rn(r1);
+        const uint16_t lo = bf16_rn(r1 - bf16_f(m));
+        ah[sl][e] = __builtin_bit_cast(__bf16, h);
+        am[sl][e] = __builtin_bit_cast(__bf16, m);
+        al[sl][e] = __builtin_bit_cast(__bf16, lo);
+      }
+    }
+    __syncthreads();                                   // cn_lds visible
+    float cn4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cn4[i] = cn_lds[4 * blk + i];
+
+    for (int32_t tile = wave; tile < ntiles; tile += kKmWaves) {
+      const int32_t base = tile * 16;
+      // B operands: lane (point n16, block blk) loads dims 32 sl + 8 blk .. + 7
+      const int32_t pc = min(base + n16, N - 1);
+      const uint16_t *xr = xp + (int64_t)pc * kHeadDim + 8 * blk;
+      bf16x8 b[4];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) b[sl] = *(const bf16x8 *)(xr + 32 * sl);
+      // the tile's rows again, lane = dims 2 lane, 2 lane + 1 (for the update)
+      uint32_t rw[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int32_t pq = min(base + q, N - 1);
+        rw[q] = ((const uint32_t *)(xp + (int64_t)pq * kHeadDim))[lane];
+      }
+      kfloatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[sl], b[sl], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[sl], b[sl], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[sl], b[sl], d, 0, 0, 0);
+      }
+      // lane (point n16, blk) holds <c_k, x> for k = 4 blk + i: argmin, then across the
+      // four blocks (lanes n16 + 16 j); ties to the lower group
+      float best = cn4[0] - 2.f * d[0];
+      int bi = 4 * blk;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        const float sc = cn4[i] - 2.f * d[i];
+        if (sc < best) {
+          best = sc;
+          bi = 4 * blk + i;
+        }
+      }
+#pragma unroll
+      for (int msk = 16; msk <= 32; msk <<= 1) {
+        const float ob = __shfl_xor(best, msk);
+        const int oi = __shfl_xor(bi, msk);
+        if (ob < best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
+      }
+      if (t == a.T - 1 && a.assign && blk == 0 && base + n16 < N) a.assign[p * N + base + n16] = bi;
+      // integer sums of the members (trunc(x 2^16), exact below 2^31 for |x| < 2^15)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (base + q < N) {
+          const int aq = __builtin_amdgcn_readlane(bi, q);
+          const int32_t v0 = __float2int_rz(__uint_as_float(rw[q] << 16) * 65536.0f);
+          const int32_t v1 = __float2int_rz(__uint_as_float(rw[q] & 0xFFFF0000u) * 65536.0f);
+          atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)(long long)v0);
+          atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)(long long)v1);
+          if (lane == 0) atomicAdd(&cnt_lds[aq], 1u);
+        }
+      }
+    }
+    __syncthreads();                                   // every sum and count in
+    for (int e = tid; e < K * kHeadDim; e += kKmThreads) {
+      const int k = e / kHeadDim, d = e % kHeadDim;
+      const uint32_t cnt = cnt_lds[k];
+      if (cnt) {
+        const double mean = (double)(long long)sum_lds[k][d] / (double)cnt;
+        c_lds[k][d] = (float)(mean * 0x1p-16);
+      }
+    }
+    __syncthreads();                                   // sums read before the next iteration clears them
+  }
+  for (int e = tid; e < K * kHeadDim; e += kKmThreads) {
+    const float c = c_lds[e / kHeadDim][e % kHeadDim];
+    cp[e] = c;
+    if (a.beacons) a.beacons[p * (int64_t)K * kHeadDim + e] = bf16_rn(c);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K, int32_t T, float *centroids,
+                         int32_t *assign, uint16_t *beacons, hipStream_t st) {
+  if (P == 0) return hipSuccess;
+  KmArgs a{};
+  a.x = points;
+  a.cent = centroids;
+  a.assign = assign;
+  a.beacons = beacons;
+  a.N = N;
+  a.K = K;
+  a.T = T;
+  kmeans_kernel<<<dim3((unsigned)P), kKmThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+int32_t kmeans_max_k() { return kKmMaxK; }
+
+}  // namespace kvs

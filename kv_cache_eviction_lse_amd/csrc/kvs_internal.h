@@ -82,6 +82,11 @@ hipError_t launch_decode(const kvs_cache &c, const Batch &b, const kvs_observers
 hipError_t launch_step_keys(const Batch &b, const float *scores, const int64_t *step_off, const int32_t *first,
                             int64_t num_steps, float beta, float *keys, float *utility, hipStream_t st);
 
+// Beacon k-means: Lloyd iterations over P problems of N bf16 points (128 dims), K <= 16.
+int32_t kmeans_max_k();
+hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K, int32_t T, float *centroids,
+                         int32_t *assign, uint16_t *beacons, hipStream_t st);
+
 // Token confidence (mean NLL of the k most probable tokens per logits row).
 int64_t conf_max_vocab();
 int32_t conf_max_k();

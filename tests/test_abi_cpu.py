@@ -308,3 +308,19 @@ def test_step_select_validation():
     st = L.kvs_step_select(C.byref(c), C.byref(hs.s), C.byref(t), FAKE, C.c_float(0.5), FAKE,
                            bud.ctypes.data, FAKE, None, FAKE, 100, None)
     assert st == 4 and L.kvs_last_error().decode().startswith("workspace")
+
+
+def test_beacon_kmeans_validation():
+    L = K.lib()
+    ok_args = dict(P=4, N=100, k=16, T=5)
+
+    def run(P=4, N=100, k=16, T=5, pts=FAKE, cent=FAKE):
+        return L.kvs_beacon_kmeans(pts, P, N, k, T, cent, None, None, None)
+
+    assert run(P=-1) == 2
+    assert run(N=0) == 2
+    assert run(k=0) == 3 and run(k=17) == 3
+    assert run(T=-1) == 2
+    assert run(pts=None) == 1 and run(cent=None) == 1
+    assert run(P=0, pts=None, cent=None) == 0          # nothing to do
+    _ = ok_args
