@@ -395,6 +395,123 @@ def bench_stepkv(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+KM_METRIC = ("history-query point-iterations of beacon k-means (Lloyd, assignment + exact update)/sec; "
+             "achieved HBM GB/s vs peak (70B shape: 80 layers x 64 query heads, 4096 queries, k = 16, "
+             "25 iterations)")
+
+
+def bench_kmeans(args) -> None:
+    """kvs_beacon_kmeans for every (layer, query head) of the 70B shape; one JSON line."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import ALL
+    from workloads import beacons as WB
+    from workloads.logits import bf16_bits_to_f64
+    import oracle as O
+
+    w = ALL["llama3_70b_128k"]
+    L, Hq, N, Kc, T = w.num_layers, w.num_q_heads, w.beacon_history, w.beacons, w.kmeans_iters
+    P = L * Hq
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(11)
+    pts = torch.randn((P, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    # initial centroids: K distinct history rows per problem
+    rows = torch.rand((P, N), generator=g, device=dev).argsort(dim=1)[:, :Kc]
+    c0 = torch.gather(pts, 1, rows[:, :, None].expand(P, Kc, 128)).float()
+    cent = c0.clone()
+    asg = torch.empty((P, N), dtype=torch.int32, device=dev)
+    bcn = torch.empty((P, Kc, 128), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+
+    def run():
+        cent.copy_(c0)
+        K.kvs_beacon_kmeans(pts, cent, T, assign=asg, beacons=bcn)
+
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        run()
+        torch.cuda.synchronize()
+    t_settle = time.perf_counter() - t_settle
+    for _ in range(args.warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0_, e1_ in evs:
+        cent.copy_(c0)
+        e0_.record(st)
+        K.kvs_beacon_kmeans(pts, cent, T, assign=asg, beacons=bcn)
+        e1_.record(st)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pit = P * N * T
+    # every iteration reads each history row once; centroids in and out, beacons and
+    # the assignments written once
+    byts = P * N * 128 * 2 * T + P * Kc * 128 * (4 + 4 + 2) + P * N * 4
+    gbps = byts / (ev_ms / 1000.0) / 1e9
+    flops = 2.0 * 2 * 128 * 16 * P * N * T          # two bf16 centroid parts x 16 groups (MFMA)
+    res = {
+        "metric": KM_METRIC, "value": pit / (ev_ms / 1000.0), "unit": "point-iterations/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "beacon_kmeans_llama3_70b", "layers": L, "q_heads": Hq, "problems": P,
+                   "history": N, "k": Kc, "iters": T, "init": "k distinct history rows"},
+        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "kmeans_kernel", "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("beacon_kmeans_llama3_70b", "kmeans", "kmeans.hip"),
+                     "traffic_of": "kmeans_kernel", "ms": ev_ms, "bytes_per_launch": byts,
+                     "mfma_tflops": flops / (ev_ms / 1000.0) / 1e12},
+        "setup_s": {"settle_s": round(t_settle, 2)},
+    }
+    if not args.no_cpu_baseline:
+        # parity: one GPU iteration from c0 on sampled problems against the oracle (a valid
+        # argmin within the fp32 bound, the update bit for bit); then the oracle's own rate
+        cent.copy_(c0)
+        K.kvs_beacon_kmeans(pts, cent, 1, assign=asg)
+        torch.cuda.synchronize()
+        pick = [0, P // 2 + 7, P - 1]
+        mism, flips = 0, 0
+        xs = {}
+        for p in pick:
+            x = bf16_bits_to_f64(pts[p].view(torch.int16).cpu().numpy().view(np.uint16))
+            xs[p] = x
+            cp = c0[p].cpu().numpy()
+            a = asg[p].cpu().numpy()
+            _, sc = O.kmeans.assign(x, cp)
+            cmax = float(np.sqrt((cp.astype(np.float64) ** 2).sum(1)).max())
+            tol = 1e-4 * (cmax ** 2 + np.sqrt((x * x).sum(1)) * cmax)
+            got = sc[np.arange(N), a]
+            mism += int(np.sum(got > sc.min(axis=1) + tol))
+            flips += int(np.sum(a != np.argmin(sc, axis=1)))
+            mism += int(np.sum(O.kmeans.update(x, a, cp) != cent[p].cpu().numpy()))
+        t_cpu, n_it = 0.0, 0
+        cc = {p: c0[p].cpu().numpy() for p in pick}
+        while t_cpu < args.cpu_seconds:
+            for p in pick:
+                ta = time.perf_counter()
+                a, _ = O.kmeans.assign(xs[p], cc[p])
+                cc[p] = O.kmeans.update(xs[p], a, cc[p])
+                t_cpu += time.perf_counter() - ta
+                n_it += 1
+                if t_cpu >= args.cpu_seconds:
+                    break
+        res["cpu_baseline"] = {"value": n_it * N / t_cpu, "unit": "point-iterations/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n_it} Lloyd iterations over {len(pick)} of {P} problems "
+                                         f"({N} queries each) in {t_cpu:.1f} s of oracle time"}
+        res["parity"] = {"problems": len(pick), "invalid": mism, "argmin_flips_within_bound": flips}
+    if args.calibration_copy:
+        src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,6 +546,9 @@ def main():
         return
     if args.workload == "stepkv_llama3_8b_32k":
         bench_stepkv(args)
+        return
+    if args.workload == "beacon_kmeans_llama3_70b":
+        bench_kmeans(args)
         return
     from workloads import ALL
     from workloads.host import make_layout, observers

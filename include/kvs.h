@@ -256,7 +256,7 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
  * problems (one per layer and query head, say), each over num_points history queries
  * of 128 bf16 values, from given initial centroids, for iters iterations:
  *   assignment  a_i = the k minimising ||c_k||^2 - 2 <x_i, c_k> (ties to the lower k),
- *               taken in fp32 (products carry the full fp32 centroid);
+ *               scored in fp32 with each centroid carried to 16 significant bits;
  *   update      c_kd = fp32(fp64(sum over members of trunc(x_id * 2^16)) / n_k * 2^-16),
  *               exact integer sums; a group without members keeps its centroid.
  * points: bf16 [num_problems][num_points][128], finite with |x| < 2^15.

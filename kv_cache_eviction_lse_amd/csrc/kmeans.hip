@@ -10,20 +10,22 @@
 //               integer sums so the result does not depend on their order; an empty
 //               group keeps its centroid.
 //
-// One 256-thread workgroup per problem keeps the centroids in LDS for all iterations.
+// One 512-thread workgroup per problem keeps the centroids in LDS for all iterations;
+// two workgroups share a CU (at most 128 VGPRs).
 // Per 16-point tile a wave computes the 16 x 16 block of <c_k, x_i> on
-// v_mfma_f32_16x16x32_bf16 with the centroids on M (each fp32 centroid split into three
-// bf16 parts, so the products carry its full precision) and the points on N (each lane
+// v_mfma_f32_16x16x32_bf16 with the centroids on M (each fp32 centroid split into two
+// bf16 parts, 16 significant bits; the points are exact bf16) and the points on N (each lane
 // loads 16 bytes of one point row per slice), takes the argmin, then adds the tile's
 // points to their groups' integer sums with LDS 64-bit atomics (lane = two dimensions;
-// the rows come back from the cache that just served the MFMA operands).
+// the rows come back from the cache that just served the MFMA operands).  Member counts
+// stay in registers (lane k counts group k) until the end of the iteration.
 #include "kvs_device.h"
 
 namespace kvs {
 namespace {
 
 constexpr int kKmMaxK = 16;
-constexpr int kKmThreads = 256;
+constexpr int kKmThreads = 512;
 constexpr int kKmWaves = kKmThreads / 64;
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float kfloatx4;
@@ -48,7 +50,7 @@ __device__ __forceinline__ float km_wave_sum(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
+__global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
   __shared__ float c_lds[kKmMaxK][kHeadDim];
   __shared__ float cn_lds[kKmMaxK];
   __shared__ unsigned long long sum_lds[kKmMaxK][kHeadDim];
@@ -70,28 +72,25 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
     for (int e = tid; e < kKmMaxK * kHeadDim; e += kKmThreads) sum_lds[e / kHeadDim][e % kHeadDim] = 0ull;
     if (tid < kKmMaxK) cnt_lds[tid] = 0u;
     __syncthreads();                                   // c_lds (initial or updated) visible
-    // ||c_k||^2: wave w takes groups 4w .. 4w+3 (groups beyond K score +inf)
+    // ||c_k||^2: wave w takes groups 2w, 2w + 1 (groups beyond K score +inf)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = 4 * wave + q;
+    for (int q = 0; q < kKmMaxK / kKmWaves; ++q) {
+      const int k = (kKmMaxK / kKmWaves) * wave + q;
       const float v0 = c_lds[k][2 * lane], v1 = c_lds[k][2 * lane + 1];
       const float s = km_wave_sum(__builtin_fmaf(v1, v1, v0 * v0));
       if (lane == 0) cn_lds[k] = k < K ? s : __builtin_inff();
     }
     // MFMA A operands: lane (group n16, block blk) holds dims 32 sl + 8 blk .. + 7 of its
-    // group's centroid as hi + mid + lo bf16 parts
-    bf16x8 ah[4], am[4], al[4];
+    // group's centroid as hi + lo bf16 parts (|c - hi - lo| <= 2^-17 |c|)
+    bf16x8 ah[4], al[4];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float c = c_lds[n16][32 * sl + 8 * blk + e];
         const uint16_t h = bf16_rn(c);
-        const float r1 = c - bf16_f(h);
-        const uint16_t m = bf16_rn(r1);
-        const uint16_t lo = bf16_rn(r1 - bf16_f(m));
+        const uint16_t lo = bf16_rn(c - bf16_f(h));
         ah[sl][e] = __builtin_bit_cast(__bf16, h);
-        am[sl][e] = __builtin_bit_cast(__bf16, m);
         al[sl][e] = __builtin_bit_cast(__bf16, lo);
       }
     }
@@ -100,6 +99,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) cn4[i] = cn_lds[4 * blk + i];
 
+    uint32_t cnt_reg = 0;                              // lane k < 16: members of group k seen by this wave
     for (int32_t tile = wave; tile < ntiles; tile += kKmWaves) {
       const int32_t base = tile * 16;
       // B operands: lane (point n16, block blk) loads dims 32 sl + 8 blk .. + 7
@@ -119,7 +119,6 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[sl], b[sl], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[sl], b[sl], d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[sl], b[sl], d, 0, 0, 0);
       }
       // lane (point n16, blk) holds <c_k, x> for k = 4 blk + i: argmin, then across the
@@ -153,10 +152,11 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
           const int32_t v1 = __float2int_rz(__uint_as_float(rw[q] & 0xFFFF0000u) * 65536.0f);
           atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)(long long)v0);
           atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)(long long)v1);
-          if (lane == 0) atomicAdd(&cnt_lds[aq], 1u);
+          cnt_reg += lane == aq ? 1u : 0u;
         }
       }
     }
+    if (lane < kKmMaxK && cnt_reg) atomicAdd(&cnt_lds[lane], cnt_reg);
     __syncthreads();                                   // every sum and count in
     for (int e = tid; e < K * kHeadDim; e += kKmThreads) {
       const int k = e / kHeadDim, d = e % kHeadDim;

@@ -12,3 +12,4 @@ from .kvs_oracle import (  # noqa: F401
 from . import confidence_oracle as confidence  # noqa: F401
 from . import decode_oracle as decode  # noqa: F401
 from . import stepkv_oracle as stepkv  # noqa: F401
+from . import kmeans_oracle as kmeans  # noqa: F401

@@ -3,12 +3,12 @@ oracle.
 
 The assignment is taken in fp32 on the GPU and in fp64 by the oracle, so where two
 groups are nearly equidistant either choice is correct: a GPU choice passes when its
-exact score is within the fp32 error bound of the exact minimum.  The bound: ||c||^2
-is a sum of 128 fp32 squares (error <= 128 u ||c||^2, u = 2^-24) and <x, c> a sum of
-384 exact bf16 products (the centroid in three bf16 parts, residual <= 2^-24 |c|)
-accumulated in fp32 (error <= 385 u |x| |c|); two scores are compared, so
-tol = 2 (128 u max||c||^2 + 2 385 u |x| max|c|) + 1e-6, taken here as
-1e-4 (max||c||^2 + |x| max|c|).  Given the GPU's assignments the update is integer
+exact score is within the GPU's error bound of the exact minimum.  The bound: ||c||^2
+is a sum of 128 fp32 squares (error <= 128 u ||c||^2, u = 2^-24); <x, c> is a sum of
+256 exact bf16 products (the centroid in two bf16 parts, residual <= 2^-17 |c|)
+accumulated in fp32, so its error is <= (2^-17 + 257 u) |x| |c| <= 2.3e-5 |x| |c|;
+two scores are compared, so tol = 2 (128 u max||c||^2 + 2 2.3e-5 |x| max|c|), taken
+here as 1e-4 (max||c||^2 + |x| max|c|).  Given the GPU's assignments the update is integer
 arithmetic and a defined rounding sequence: the centroids must match bit for bit.
 """
 import numpy as np
