@@ -523,6 +523,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle CPU time")
     ap.add_argument("--separate", action="store_true",
                     help="run cut/LRFU, keep set, plan and move as four calls instead of two fused ones")
+    ap.add_argument("--layer-chunks", type=int, default=0,
+                    help="time rounds as one kvs_eviction_round call pipelined over this many layer "
+                         "chunks (1: one call, no overlap); 0 (default): the stage calls in turn, with "
+                         "the scorer timed by events inside the timed rounds")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MiB",
                     help="after timing, copy MiB of device memory 3 times (counter calibration)")
     ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
@@ -553,6 +557,7 @@ def main():
     from workloads import ALL
     from workloads.host import make_layout, observers
     w = ALL[args.workload]
+    chunks = 0 if args.separate else args.layer_chunks
     lay = make_layout(w)
     L, Hkv, Hq = w.num_layers, w.num_kv_heads, w.num_q_heads
     # sampled streams: spread over layers and heads
@@ -600,7 +605,8 @@ def main():
 
     # first round: keep the outputs of the sampled streams for a parity spot check
     if samples:
-        K.eviction_round(cache, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate)
+        K.eviction_round(cache, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate,
+                         layer_chunks=chunks)
         torch.cuda.synchronize()
         s_gpu = bufs.scores.cpu().numpy()
         keep_gpu = bufs.keep.cpu().numpy().astype(bool)
@@ -610,12 +616,13 @@ def main():
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle:
         for _ in range(20):
-            K.eviction_round(caches[-1], seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate)
+            K.eviction_round(caches[-1], seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate,
+                             layer_chunks=chunks)
         torch.cuda.synchronize()
     t_settle = time.perf_counter() - t_settle
     for wi in range(args.warmup):
         K.eviction_round(caches[1 + wi % max(n_warm, 1)], seqs, obs, bufs, decay, n_prev, scale,
-                         fused=not args.separate)
+                         fused=not args.separate, layer_chunks=chunks)
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -624,6 +631,11 @@ def main():
     t0 = time.perf_counter()
     for k in range(args.steps):
         c = caches[1 + n_warm + k]
+        if chunks > 0:
+            # the whole round in one call, scoring overlapped with the cut, keep set and
+            # moves of the previous layer chunk (the scorer is timed alone below)
+            K.eviction_round(c, seqs, obs, bufs, decay, n_prev, scale, layer_chunks=chunks)
+            continue
         evs[k][0].record(st)
         K.kvs_score(c, seqs, obs, scale, bufs.scores, bufs.workspace)
         evs[k][1].record(st)
@@ -638,6 +650,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    if chunks > 0:
+        # the dominant kernel's launch time, live with HIP events on its stream: the scorer
+        # alone on the same inputs, as many launches as timed steps
+        for k in range(args.steps):
+            evs[k][0].record(st)
+            K.kvs_score(caches[1 + n_warm + k], seqs, obs, scale, bufs.scores, bufs.workspace)
+            evs[k][1].record(st)
+        torch.cuda.synchronize()
     score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     entries = int(lay.entry_off[-1]) * L * Hkv
@@ -655,7 +675,8 @@ def main():
         while time.perf_counter() - th0 < args.hold:
             for _ in range(50):
                 c.crf.copy_(d.crf)
-                K.eviction_round(c, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate)
+                K.eviction_round(c, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate,
+                                 layer_chunks=chunks)
             torch.cuda.synchronize()
             n_hold += 50
         hold = {"seconds": round(time.perf_counter() - th0, 2), "steps": n_hold,
@@ -697,7 +718,7 @@ def main():
         "config": {"workload": w.name, "layers": L, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": D, "page_size": 16, "context": int(lay.length[0]),
                    "pool_pages": lay.num_pages, "observers": int(lay.obs[0]), "budget": w.budget,
-                   "entries_per_step": entries},
+                   "entries_per_step": entries, "layer_chunks": chunks},
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "required_bytes_per_step": req_bytes,

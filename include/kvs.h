@@ -344,6 +344,28 @@ kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const 
                             int64_t *freed_count_h, void *stream);
 
 /*
+ * kvs_eviction_round -- the whole round in one call: kvs_score, then kvs_lrfu_select,
+ * then kvs_plan_compact, with the union of their arguments and validation and the
+ * same results (scores, crf, hit, keep, pairs, pair_count, moved rows, host outputs).
+ * ActKV, Component 3: eviction runs beside decoding on the engine's paged blocks.
+ * layer_chunks > 1 splits the layers into that many contiguous chunks and overlaps
+ * the scoring of chunk c + 1 (on `stream`) with the cut, keep set and moves of chunk c
+ * (on a library-owned side stream of the same device, default priority; every array
+ * has the layer outermost, so chunks touch disjoint memory).  All work is ordered
+ * after what `stream` held at the call and before what it is given next.
+ * workspace: >= kvs_score_workspace_size(cache, seqs, obs), as for kvs_score (the
+ * chunks use it in turn).  Calls that overlap on one device share the side stream.
+ */
+kvs_status kvs_eviction_round(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *obs,
+                              float scale, uint32_t mass_num, uint32_t mass_den, const float *decay,
+                              const int32_t *n_prev, const int32_t *budget, const int32_t *budget_h,
+                              float *scores, uint8_t *hit, uint8_t *keep, int32_t *pairs,
+                              int32_t *pair_count, void *workspace, size_t workspace_bytes,
+                              int32_t layer_chunks, int32_t *shift_h, int32_t *new_start_h,
+                              int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                              int64_t *freed_count_h, void *stream);
+
+/*
  * Host-side budget ratchet (ActKV, Component 2 and Lineage): for each sequence
  * whose flag_h is non-zero, budget_h[i] <- max(budget_h[i],
  * min(cap, floor(budget_h[i] * num / den))).  The pages' ratchet is num/den = 7/4,

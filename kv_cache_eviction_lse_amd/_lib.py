@@ -26,7 +26,7 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
            "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
-           "kvs_step_select", "kvs_beacon_kmeans")
+           "kvs_step_select", "kvs_beacon_kmeans", "kvs_eviction_round")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -110,6 +110,9 @@ def lib() -> C.CDLL:
         L.kvs_step_select_workspace_size.argtypes = [P, P, P]
         L.kvs_step_select.restype = C.c_int
         L.kvs_step_select.argtypes = [P, P, P, P, C.c_float, P, P, P, P, P, C.c_size_t, P]
+        L.kvs_eviction_round.restype = C.c_int
+        L.kvs_eviction_round.argtypes = [P, P, P, C.c_float, C.c_uint32, C.c_uint32, P, P, P, P, P, P, P, P, P, P,
+                                         C.c_size_t, C.c_int32, P, P, P, P, C.c_int64, P, P]
         L.kvs_beacon_kmeans.restype = C.c_int
         L.kvs_beacon_kmeans.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
@@ -318,6 +321,26 @@ def kvs_plan_compact(cache: PagedCache, seqs: SeqBatch, keep, budget, budget_h: 
     _check(lib().kvs_plan_compact(cache.ref, seqs.ref, _ptr(keep), _ptr(budget), _ptr(budget_h), _ptr(pairs),
                                   _ptr(pair_count), _ptr(shift), _ptr(new_start), _ptr(new_len), _ptr(freed),
                                   cap, _ptr(nfreed), _stream(stream)))
+    return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
+
+
+def kvs_eviction_round(cache: PagedCache, seqs: SeqBatch, obs: ObserverSet, scale: float, mass_num: int,
+                       mass_den: int, decay, n_prev, budget, budget_h: np.ndarray, scores, hit, keep, pairs,
+                       pair_count, workspace=None, layer_chunks: int = 1, stream=None) -> PlanHost:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    S = seqs.num_seqs
+    shift = np.zeros(S, np.int32)
+    new_start = np.zeros(S, np.int32)
+    new_len = np.zeros(S, np.int32)
+    cap = int(seqs.block_table_h.size)
+    freed = np.zeros(max(cap, 1), np.int32)
+    nfreed = np.zeros(1, np.int64)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvs_eviction_round(cache.ref, seqs.ref, obs.ref, C.c_float(scale), mass_num, mass_den,
+                                    _ptr(decay), _ptr(n_prev), _ptr(budget), _ptr(budget_h), _ptr(scores),
+                                    _ptr(hit), _ptr(keep), _ptr(pairs), _ptr(pair_count), _ptr(workspace),
+                                    ws_bytes, int(layer_chunks), _ptr(shift), _ptr(new_start), _ptr(new_len),
+                                    _ptr(freed), cap, _ptr(nfreed), _stream(stream)))
     return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
 
 

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kvs_internal.h"
@@ -625,6 +626,187 @@ kvs_status kvs_confidence_trend(const float *conf_h, int64_t n, int32_t window, 
   if (slope_h) *slope_h = slope;
   *flag_h = slope < 0.0 ? 1 : 0;
   return ok();
+}
+
+}  // extern "C"
+
+// ---- one eviction round, pipelined over layer chunks ----
+namespace {
+
+// Per device: a non-blocking side stream at the default priority and a pool of events,
+// created once and reused (an event may be recorded again once the waits on its previous
+// record are enqueued).  The mutex is held while a round is enqueued.
+struct RoundRes {
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev;
+};
+std::mutex g_round_mu;
+std::vector<RoundRes> g_round_res;
+
+hipError_t round_resources(int32_t n_events, RoundRes **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((size_t)dev >= g_round_res.size()) g_round_res.resize((size_t)dev + 1);
+  RoundRes &r = g_round_res[dev];
+  if (!r.side && (e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking)) != hipSuccess) return e;
+  while ((int32_t)r.ev.size() < n_events) {
+    hipEvent_t x = nullptr;
+    if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    r.ev.push_back(x);
+  }
+  *out = &r;
+  return hipSuccess;
+}
+
+// Every per-layer array has the layer outermost, so layers [l0, l0 + n) of the batch
+// are a contiguous sub-array of each: the same kernels run on a chunk through offset
+// pointers and num_layers = n.
+struct RoundArgs {
+  kvs_cache cache;
+  kvs_observers obs;
+  float scale;
+  uint32_t mass_num, mass_den;
+  const float *decay;
+  const int32_t *n_prev, *budget;
+  float *scores;
+  uint8_t *hit, *keep;
+  int32_t *pairs, *pair_count;
+  int64_t pair_cap;
+  int32_t max_npages, max_len;
+  void *ws;
+  size_t ws_bytes;
+};
+
+RoundArgs layer_chunk(const RoundArgs &r, const kvs_seqs *seqs, int32_t l0, int32_t n) {
+  RoundArgs c = r;
+  const int64_t P = r.cache.num_pages, Hkv = r.cache.num_kv_heads, S = seqs->num_seqs;
+  const int64_t E = S ? seqs->entry_off_h[S] : 0;
+  const int64_t Hq = r.obs.num_q_heads, O = r.obs.obs_total;
+  c.cache.num_layers = n;
+  c.cache.k = (uint16_t *)r.cache.k + l0 * P * Hkv * kvs::kPageElems;
+  c.cache.v = (uint16_t *)r.cache.v + l0 * P * Hkv * kvs::kPageElems;
+  c.cache.crf = r.cache.crf + l0 * P * Hkv * kvs::kPage;
+  c.obs.q = (const uint16_t *)r.obs.q + l0 * Hq * O * kvs::kHeadDim;
+  c.obs.lse = r.obs.lse + l0 * Hq * O;
+  c.scores = r.scores + l0 * Hkv * E;
+  c.keep = r.keep + l0 * Hkv * E;
+  c.hit = r.hit ? r.hit + l0 * Hkv * E : nullptr;
+  c.pairs = r.pairs ? r.pairs + l0 * Hkv * S * r.pair_cap * 2 : nullptr;
+  c.pair_count = r.pair_count + l0 * Hkv * S;
+  return c;
+}
+
+hipError_t round_score(const RoundArgs &r, const kvs_seqs *seqs, hipStream_t st) {
+  const kvs::Batch b = make_batch(&r.cache, seqs);
+  return kvs::launch_score(r.cache, b, r.obs, r.scale, r.scores, r.ws, r.ws_bytes, r.obs.obs_off_h, seqs->len_h,
+                           seqs->start_h, st);
+}
+
+hipError_t round_select_move(const RoundArgs &r, const kvs_seqs *seqs, hipStream_t st) {
+  const kvs::Batch b = make_batch(&r.cache, seqs);
+  hipError_t e;
+  if (kvs::stream_reg_fits(r.max_len, r.cache.num_pages, r.cache.num_kv_heads)) {
+    e = kvs::launch_stream_reg(r.cache, b, r.scores, true, true, r.mass_num, r.mass_den, r.decay, r.n_prev, r.hit,
+                               r.budget, r.keep, st);
+  } else {
+    e = kvs::launch_lrfu(r.cache, b, r.scores, r.mass_num, r.mass_den, r.decay, r.n_prev, r.hit, r.max_len, st);
+    if (e == hipSuccess) e = kvs::launch_select(r.cache, b, r.scores, r.budget, r.keep, r.max_len, st);
+  }
+  if (e != hipSuccess) return e;
+  if (kvs::plan_move_fits(r.pair_cap, r.max_npages))
+    return kvs::launch_plan_move(r.cache, b, r.keep, r.budget, r.pairs, r.pair_count, r.pair_cap, r.max_npages, st);
+  e = kvs::launch_plan(b, r.keep, r.budget, r.pairs, r.pair_count, r.pair_cap, st);
+  if (e != hipSuccess || r.pair_cap == 0) return e;
+  return kvs::launch_compact(r.cache, b, r.pairs, r.pair_count, r.pair_cap, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvs_status kvs_eviction_round(const kvs_cache *cache, const kvs_seqs *seqs, const kvs_observers *obs, float scale,
+                              uint32_t mass_num, uint32_t mass_den, const float *decay, const int32_t *n_prev,
+                              const int32_t *budget, const int32_t *budget_h, float *scores, uint8_t *hit,
+                              uint8_t *keep, int32_t *pairs, int32_t *pair_count, void *workspace,
+                              size_t workspace_bytes, int32_t layer_chunks, int32_t *shift_h, int32_t *new_start_h,
+                              int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity, int64_t *freed_count_h,
+                              void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if ((st = check_obs(obs, seqs, cache->num_kv_heads)) != KVS_OK) return st;
+  if (!std::isfinite(scale)) return fail(KVS_ERR_SHAPE, "scale is not finite");
+  if (mass_den == 0 || mass_num > mass_den)
+    return fail(KVS_ERR_SHAPE, "mass fraction %u/%u must satisfy 0 <= num <= den, den > 0", mass_num, mass_den);
+  if (layer_chunks < 1) return fail(KVS_ERR_SHAPE, "layer_chunks = %d < 1", layer_chunks);
+  if (seqs->num_seqs > 0 && (!budget || !budget_h)) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  if ((st = kvs_plan_host(seqs, budget_h, shift_h, new_start_h, new_len_h, freed_h, freed_capacity,
+                          freed_count_h)) != KVS_OK)
+    return st;
+  if (seqs->num_seqs == 0) return ok();
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E == 0) return ok();
+  const int64_t P = pair_cap_of(seqs, budget_h);
+  if (!scores || !decay || !n_prev || !keep || !pair_count || (P > 0 && !pairs))
+    return fail(KVS_ERR_NULL, "scores/decay/n_prev/keep/pairs/pair_count is NULL");
+  const size_t need = kvs::score_workspace_bytes(b, obs->num_q_heads, obs->obs_off_h, seqs->len_h, seqs->start_h);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KVS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  RoundArgs r{};
+  r.cache = *cache;
+  r.obs = *obs;
+  r.scale = scale;
+  r.mass_num = mass_num;
+  r.mass_den = mass_den;
+  r.decay = decay;
+  r.n_prev = n_prev;
+  r.budget = budget;
+  r.scores = scores;
+  r.hit = hit;
+  r.keep = keep;
+  r.pairs = pairs;
+  r.pair_count = pair_count;
+  r.pair_cap = P;
+  r.max_len = max_len_of(seqs);
+  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
+    const int32_t n = seqs->len_h[i];
+    const int32_t np = n == 0 ? 0 : (seqs->start_h[i] + n + kvs::kPage - 1) / kvs::kPage;
+    r.max_npages = np > r.max_npages ? np : r.max_npages;
+  }
+  r.ws = workspace;
+  r.ws_bytes = workspace_bytes;
+  const hipStream_t main = (hipStream_t)stream;
+  const int32_t L = cache->num_layers;
+  const int32_t chunks = layer_chunks < L ? layer_chunks : L;
+  if (chunks == 1) {
+    hipError_t e = round_score(r, seqs, main);
+    if (e == hipSuccess) e = round_select_move(r, seqs, main);
+    return hip_status(e);
+  }
+  // Scoring of chunk c + 1 (on the caller's stream) overlaps the cut, keep set and moves
+  // of chunk c (on a side stream): different layers, so different memory.
+  std::lock_guard<std::mutex> lock(g_round_mu);
+  RoundRes *res = nullptr;
+  hipError_t e = round_resources(chunks + 2, &res);
+  if (e != hipSuccess) return hip_status(e);
+  const hipStream_t side = res->side;
+  const std::vector<hipEvent_t> &ev = res->ev;
+  e = hipEventRecord(ev[0], main);                               // the inputs are ready
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[0], 0);
+  for (int32_t c = 0; c < chunks && e == hipSuccess; ++c) {
+    const int32_t l0 = (int32_t)((int64_t)L * c / chunks), l1 = (int32_t)((int64_t)L * (c + 1) / chunks);
+    const RoundArgs rc = layer_chunk(r, seqs, l0, l1 - l0);
+    e = round_score(rc, seqs, main);
+    if (e == hipSuccess) e = hipEventRecord(ev[c + 1], main);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev[c + 1], 0);
+    if (e == hipSuccess) e = round_select_move(rc, seqs, side);
+  }
+  if (e == hipSuccess) e = hipEventRecord(ev[chunks + 1], side);
+  if (e == hipSuccess) e = hipStreamWaitEvent(main, ev[chunks + 1], 0);   // the caller's stream sees it all
+  return hip_status(e);
 }
 
 }  // extern "C"

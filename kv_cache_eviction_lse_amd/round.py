@@ -35,10 +35,16 @@ class RoundBuffers:
 
 def eviction_round(cache: K.PagedCache, seqs: K.SeqBatch, obs: K.ObserverSet, bufs: RoundBuffers,
                    decay, n_prev, scale: float, mass_num: int = 9, mass_den: int = 10,
-                   stream=None, fused: bool = True) -> K.PlanHost:
+                   stream=None, fused: bool = True, layer_chunks: int = 0) -> K.PlanHost:
     """Enqueue one full round; returns the host-side plan (shift, new start/len, freed pages).
-    fused: the cut/LRFU/keep set and the plan/move as one call each (same results)."""
+    fused: the cut/LRFU/keep set and the plan/move as one call each (same results).
+    layer_chunks > 0: the whole round as one kvs_eviction_round call, pipelined over that
+    many layer chunks (1: no overlap)."""
     L, Hkv = cache.c.num_layers, cache.c.num_kv_heads
+    if layer_chunks > 0:
+        return K.kvs_eviction_round(cache, seqs, obs, scale, mass_num, mass_den, decay, n_prev, bufs.budget,
+                                    bufs.budget_h, bufs.scores, bufs.hit, bufs.keep, bufs.pairs, bufs.pair_count,
+                                    bufs.workspace, layer_chunks, stream)
     K.kvs_score(cache, seqs, obs, scale, bufs.scores, bufs.workspace, stream)
     if fused:
         K.kvs_lrfu_select(cache, seqs, bufs.scores, mass_num, mass_den, decay, n_prev, bufs.budget,

@@ -324,3 +324,25 @@ def test_beacon_kmeans_validation():
     assert run(pts=None) == 1 and run(cent=None) == 1
     assert run(P=0, pts=None, cent=None) == 0          # nothing to do
     _ = ok_args
+
+
+def test_eviction_round_validation():
+    L = K.lib()
+    hs = HostSeqs([[0, 1]], [0], [20])
+    c = _cache(P=2)
+    o, off = _obs(1)
+    bud = np.array([8], np.int32)
+
+    def run(chunks=2, mass=(9, 10), budget=bud, obs=o, ws_bytes=0):
+        return L.kvs_eviction_round(C.byref(c), C.byref(hs.s), C.byref(obs), C.c_float(0.1), mass[0], mass[1],
+                                    FAKE, FAKE, FAKE, budget.ctypes.data, FAKE, None, FAKE, FAKE, FAKE, None,
+                                    ws_bytes, chunks, None, None, None, None, 0, None, None)
+
+    assert run(chunks=0) == 2
+    assert run(mass=(11, 10)) == 2 and run(mass=(1, 0)) == 2
+    assert run(budget=np.array([-1], np.int32)) == 2
+    o2 = K.Observers(FAKE, FAKE, FAKE, off.ctypes.data, 6, int(off[-1]))     # 6 heads over 1 KV head: fine
+    c2 = _cache(Hkv=4, P=2)
+    assert L.kvs_eviction_round(C.byref(c2), C.byref(hs.s), C.byref(o2), C.c_float(0.1), 9, 10, FAKE, FAKE, FAKE,
+                                bud.ctypes.data, FAKE, None, FAKE, FAKE, FAKE, None, 0, 1, None, None, None,
+                                None, 0, None, None) == 2
