@@ -91,6 +91,39 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Ranks of flagged slots in slot order (slot u * 1024 + t: row u, then thread t) with
+// a handful of barriers: every wave counts its flags per row (ballots), one block scan
+// over the (row, wave) counts in row-major order gives each (row, wave) its offset, and
+// a lane adds the flags of the lower lanes of its wave.  take(u, rank) is called for
+// every row u < rounds (rank is meaningful where bit u of fmask is set).  cnt must hold
+// kRegU * kStreamWaves words of LDS that no other thread uses meanwhile.
+template <typename F>
+__device__ __forceinline__ void rank_flags(uint32_t fmask, int rounds, uint32_t *cnt, uint32_t *scratch, F take) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < kRegU; ++u) {
+    const uint64_t b = __ballot(u < rounds && ((fmask >> u) & 1u));
+    if (lane == 0) cnt[u * kStreamWaves + wave] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  static_assert(kRegU * kStreamWaves <= kStreamThreads, "one (row, wave) count per thread");
+  const uint32_t v = threadIdx.x < kRegU * kStreamWaves ? cnt[threadIdx.x] : 0u;
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan(v, tot, scratch);
+  if (threadIdx.x < kRegU * kStreamWaves) cnt[threadIdx.x] = ex;
+  __syncthreads();
+  const uint32_t *mine = cnt + opaque(wave);
+#pragma unroll
+  for (int u = 0; u < kRegU; ++u) {
+    if (u < rounds) {
+      const uint64_t b = __ballot((fmask >> u) & 1u);
+      take(u, mine[u * kStreamWaves] + (uint32_t)__popcll(b & lanemask_lt()));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();     // cnt is free again
+}
+
 // v* with weight(keys > v*) < target <= weight(keys >= v*) over the candidates
 // (slot valid and cand(u)); key[u] holds the key of this thread's row u.  With CUT the
 // target is ceil(num * W / den) for the candidates' total weight W, which the first
@@ -306,19 +339,15 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     uint64_t hbits = 0;
     if (!none && k_needed < ties) {
       // ties at the threshold exceed the hits still needed: lowest slots first
-      uint64_t carry = 0;
+      uint32_t tmask = 0;
 #pragma unroll
-      for (int u = 0; u < kRegU; ++u) {
-        if (u < rounds) {
-          const bool valid = u < cnt;
-          const bool tie = valid && s[u] == vstar;
-          uint32_t tot;
-          const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
-          const bool h = valid && (s[u] > vstar || (tie && carry + rk < k_needed));
-          carry += tot;
-          hbits |= (uint64_t)h << u;
-        }
-      }
+      for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(u < cnt && s[u] == vstar) << u;
+      rank_flags(tmask, rounds, (uint32_t *)sh.hist, flag_scratch, [&](int u, uint32_t rk) {
+        const bool valid = u < cnt;
+        const bool tie = (tmask >> u) & 1u;
+        const bool h = valid && (s[u] > vstar || (tie && rk < k_needed));
+        hbits |= (uint64_t)h << u;
+      });
     } else if (!none) {
 #pragma unroll
       for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(u < cnt && s[u] >= vstar) << u;
@@ -357,6 +386,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       }
     }
     if (!SELECT) return;
+    have_s = false;     // the selection reloads the scores only for ties at the threshold
     if (K == 0 || K == n) {
       const int t = opaque(tid);
 #pragma unroll
@@ -480,19 +510,14 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = k ? 1 : 0;)
     }
   } else {
-    uint64_t carry = 0;
+    uint32_t tmask = 0;
 #pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      if (u < rounds) {
-        const bool valid = u < cnt;
-        const bool tie = valid && c[u] == cstar && s[u] == sstar;
-        uint32_t tot;
-        const uint32_t rk = block_flag_rank(tie, tot, flag_scratch);
-        const bool k = c[u] > cstar || (c[u] == cstar && (s[u] > sstar || (tie && carry + rk < need2)));
-        carry += tot;
-        if (valid) kp[u * kStreamThreads + tid] = k ? 1 : 0;
-      }
-    }
+    for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(u < cnt && c[u] == cstar && s[u] == sstar) << u;
+    rank_flags(tmask, rounds, (uint32_t *)sh.hist, flag_scratch, [&](int u, uint32_t rk) {
+      const bool tie = (tmask >> u) & 1u;
+      const bool k = c[u] > cstar || (c[u] == cstar && (s[u] > sstar || (tie && rk < need2)));
+      if (u < cnt) kp[u * kStreamThreads + tid] = k ? 1 : 0;
+    });
   }
 }
 
