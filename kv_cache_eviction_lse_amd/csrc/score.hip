@@ -108,14 +108,15 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
 // whole prefetch ring at every step.  Ordering is explicit instead: a slot is read
 // only after the ring barrier's vmcnt wait and s_barrier, and refilled only after
 // the barrier that follows the last read of it.  No output registers; the address
-// registers are consumed at issue.  M0 is saved and restored around the DMA.
+// registers are consumed at issue.  M0 is saved and restored around the DMA.  The K
+// rows are read once per call, so the load is marked non-temporal (streaming).
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds)
