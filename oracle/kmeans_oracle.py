@@ -22,6 +22,9 @@ Readings (the page names no algorithm; stated here and in the design notes):
       members c_kd = fp32(fp64(fp64(sum_i q_id) / n_k) 2^-16), each step rounded to
       nearest; an empty group keeps its centroid.
   K4. The assignments reported are those of the last iteration's assignment step.
+  K5. Initial centroids by k-means++ (the configuration's seeded start), drawn by
+      inverting the cumulative distribution of the squared distances in row order with
+      given uniforms u_0 .. u_{k-1} in [0, 1); the first row is floor(u_0 n).
 
 The assignment here is taken in fp64 from the exact inputs; the GPU takes it in fp32,
 so the tests accept any choice whose exact score is within the fp32 error bound of
@@ -81,3 +84,52 @@ def to_bf16_bits(c: np.ndarray) -> np.ndarray:
     u = np.asarray(c, np.float32).view(np.uint32).astype(np.uint64)
     r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return r.astype(np.uint16)
+
+
+def seed_index(u: float, n: int) -> int:
+    """Row floor(u n) (at most n - 1) for a uniform u in [0, 1) (reading K5)."""
+    return min(int(np.floor(float(np.float32(u)) * n)), n - 1)
+
+
+def kmeanspp(x: np.ndarray, uniforms: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """(centroids fp32 [k][D], chosen rows [k]): k-means++ seeding (reading K5).
+
+    The first centroid is row floor(u_0 n).  Then, with D2_i the squared distance from
+    row i to its nearest chosen centroid, centroid c is the first row i (in row order)
+    whose running sum of D2 exceeds u_c * sum(D2), i.e. row i is drawn with probability
+    D2_i / sum(D2) by inverting the cumulative sum; if every D2 is 0 the row is
+    floor(u_c n).  Distances in fp64 from the exact values.
+    """
+    x = check_points(x)
+    n = x.shape[0]
+    u = np.asarray(uniforms, np.float32).astype(np.float64)
+    rows = [seed_index(u[0], n)]
+    d2 = ((x - x[rows[0]]) ** 2).sum(axis=1)
+    for c in range(1, len(u)):
+        tot = d2.sum()
+        if not tot > 0:
+            rows.append(seed_index(u[c], n))
+        else:
+            cum = np.cumsum(d2)
+            i = int(np.searchsorted(cum, u[c] * tot, side="right"))
+            rows.append(min(i, n - 1))
+        d2 = np.minimum(d2, ((x - x[rows[-1]]) ** 2).sum(axis=1))
+    return x[rows].astype(np.float32), np.asarray(rows, np.int64)
+
+
+def seed_step_valid(x: np.ndarray, rows_before, u: float, row: int, rtol: float) -> bool:
+    """Whether `row` is a correct k-means++ draw for uniform u given the rows chosen
+    before it: the target u * sum(D2) lies in [cum_{row-1}, cum_row] up to rtol * sum(D2)
+    (fp32 sums may move the target across a boundary by that much)."""
+    x = check_points(x)
+    n = x.shape[0]
+    d2 = np.full(n, np.inf)
+    for r in rows_before:
+        d2 = np.minimum(d2, ((x - x[int(r)]) ** 2).sum(axis=1))
+    tot = d2.sum()
+    if not tot > 0:
+        return row == seed_index(u, n)
+    cum = np.cumsum(d2)
+    t = float(np.float32(u)) * tot
+    lo = cum[row - 1] if row > 0 else 0.0
+    return d2[row] > 0 and lo - rtol * tot <= t <= cum[row] + rtol * tot

@@ -114,3 +114,45 @@ def test_bf16_rounding_matches_torch():
 def test_bad_points():
     with pytest.raises(ValueError):
         KO.lloyd(line_points([2.0 ** 15]), np.zeros((1, D), np.float32), 1)
+
+
+def test_kmeanspp_hand_worked():
+    # rows 0, 1, 10 on the first axis; u_0 = 0 picks row 0, so D2 = [0, 1, 100] and
+    # the cumulative sums are [0, 1, 101]: u = 0.5 (target 50.5) draws row 2, u = 0.005
+    # (target 0.505) draws row 1
+    x = line_points([0.0, 1.0, 10.0])
+    c, rows = KO.kmeanspp(x, np.array([0.0, 0.5], np.float32))
+    np.testing.assert_array_equal(rows, [0, 2])
+    np.testing.assert_array_equal(c[:, 0], [0.0, 10.0])
+    _, rows = KO.kmeanspp(x, np.array([0.0, 0.005], np.float32))
+    np.testing.assert_array_equal(rows, [0, 1])
+    # u_0 = 0.7 of 3 rows -> row 2
+    assert KO.kmeanspp(x, np.array([0.7], np.float32))[1][0] == 2
+
+
+def test_kmeanspp_draws_in_proportion_to_d2():
+    # from row 0, rows 1..4 sit at squared distances 1, 2, 3, 4: over many uniforms the
+    # second draw lands on row i with frequency D2_i / 10
+    x = np.zeros((5, D))
+    x[1:, 0] = np.sqrt([1.0, 2.0, 3.0, 4.0])
+    u = (np.arange(20000) + 0.5) / 20000
+    counts = np.zeros(5)
+    for ui in u[::7]:
+        counts[KO.kmeanspp(x, np.array([0.0, ui], np.float32))[1][1]] += 1
+    freq = counts / counts.sum()
+    np.testing.assert_allclose(freq, [0.0, 0.1, 0.2, 0.3, 0.4], atol=2e-3)
+
+
+def test_kmeanspp_degenerate_and_consistency():
+    # all rows equal: D2 is 0, so each draw is floor(u n)
+    x = np.ones((10, D))
+    _, rows = KO.kmeanspp(x, np.array([0.05, 0.55, 0.95], np.float32))
+    np.testing.assert_array_equal(rows, [0, 5, 9])
+    # random rows: chosen rows are distinct, and every draw is a valid step
+    y = rng.normal(size=(300, D)).astype(np.float32).astype(np.float64)
+    uu = rng.random(16).astype(np.float32)
+    _, rows = KO.kmeanspp(y, uu)
+    assert len(set(rows.tolist())) == 16
+    for c in range(1, 16):
+        assert KO.seed_step_valid(y, rows[:c], uu[c], int(rows[c]), 0.0)
+        assert not KO.seed_step_valid(y, rows[:c], uu[c], int(rows[c - 1]), 0.0)
