@@ -395,17 +395,17 @@ def bench_stepkv(args) -> None:
     print(json.dumps(res), flush=True)
 
 
-KM_METRIC = ("history-query point-iterations of beacon k-means (Lloyd, assignment + exact update)/sec; "
-             "achieved HBM GB/s vs peak (70B shape: 80 layers x 64 query heads, 4096 queries, k = 16, "
-             "25 iterations)")
+KM_METRIC = ("history-query passes of beacon maintenance (k-means++ seeding, then Lloyd k-means: assignment + "
+             "exact update)/sec; achieved HBM GB/s vs peak (70B shape: 80 layers x 64 query heads, 4096 "
+             "queries, k = 16, 25 iterations)")
 
 
 def bench_kmeans(args) -> None:
-    """kvs_beacon_kmeans for every (layer, query head) of the 70B shape; one JSON line."""
+    """kvs_beacon_seed then kvs_beacon_kmeans for every (layer, query head) of the 70B
+    shape; one JSON line."""
     import torch
     import kv_cache_eviction_lse_amd as K
     from workloads import ALL
-    from workloads import beacons as WB
     from workloads.logits import bf16_bits_to_f64
     import oracle as O
 
@@ -415,16 +415,14 @@ def bench_kmeans(args) -> None:
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev).manual_seed(11)
     pts = torch.randn((P, N, 128), generator=g, device=dev).to(torch.bfloat16)
-    # initial centroids: K distinct history rows per problem
-    rows = torch.rand((P, N), generator=g, device=dev).argsort(dim=1)[:, :Kc]
-    c0 = torch.gather(pts, 1, rows[:, :, None].expand(P, Kc, 128)).float()
-    cent = c0.clone()
+    uni = torch.rand((P, Kc), generator=g, device=dev)          # the k-means++ draws
+    cent = torch.empty((P, Kc, 128), dtype=torch.float32, device=dev)
     asg = torch.empty((P, N), dtype=torch.int32, device=dev)
     bcn = torch.empty((P, Kc, 128), dtype=torch.bfloat16, device=dev)
     st = torch.cuda.current_stream()
 
     def run():
-        cent.copy_(c0)
+        K.kvs_beacon_seed(pts, uni, cent)
         K.kvs_beacon_kmeans(pts, cent, T, assign=asg, beacons=bcn)
 
     t_settle = time.perf_counter()
@@ -434,41 +432,50 @@ def bench_kmeans(args) -> None:
     t_settle = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         run()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0_, e1_ in evs:
-        cent.copy_(c0)
+    for e0_, e1_, e2_ in evs:
         e0_.record(st)
-        K.kvs_beacon_kmeans(pts, cent, T, assign=asg, beacons=bcn)
+        K.kvs_beacon_seed(pts, uni, cent)
         e1_.record(st)
+        K.kvs_beacon_kmeans(pts, cent, T, assign=asg, beacons=bcn)
+        e2_.record(st)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1000.0 / args.steps
-    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    pit = P * N * T
-    # every iteration reads each history row once; centroids in and out, beacons and
-    # the assignments written once
-    byts = P * N * 128 * 2 * T + P * Kc * 128 * (4 + 4 + 2) + P * N * 4
-    gbps = byts / (ev_ms / 1000.0) / 1e9
+    seed_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    km_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    passes = P * N * (Kc - 1 + T)
+    # each Lloyd iteration and each seeding round reads every history row once; the
+    # centroids, beacons and assignments are written once
+    km_bytes = P * N * 128 * 2 * T + P * Kc * 128 * (4 + 4 + 2) + P * N * 4
+    seed_bytes = P * N * 128 * 2 * (Kc - 1) + P * Kc * (128 * 4 + 4)
+    gbps = km_bytes / (km_ms / 1000.0) / 1e9
     flops = 2.0 * 2 * 128 * 16 * P * N * T          # two bf16 centroid parts x 16 groups (MFMA)
     res = {
-        "metric": KM_METRIC, "value": pit / (ev_ms / 1000.0), "unit": "point-iterations/s", "n_gpus": 1,
+        "metric": KM_METRIC, "value": passes / (ms / 1000.0), "unit": "point-passes/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "beacon_kmeans_llama3_70b", "layers": L, "q_heads": Hq, "problems": P,
-                   "history": N, "k": Kc, "iters": T, "init": "k distinct history rows"},
-        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+                   "history": N, "k": Kc, "iters": T, "init": "k-means++ (device, seeded uniforms)"},
+        "hbm_gbps": (km_bytes + seed_bytes) / (ms / 1000.0) / 1e9,
+        "hbm_frac": (km_bytes + seed_bytes) / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"kernel": "kmeans_kernel", "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                      "traffic": load_traffic("beacon_kmeans_llama3_70b", "kmeans", "kmeans.hip"),
-                     "traffic_of": "kmeans_kernel", "ms": ev_ms, "bytes_per_launch": byts,
-                     "mfma_tflops": flops / (ev_ms / 1000.0) / 1e12},
+                     "traffic_of": "kmeans_kernel", "ms": km_ms, "bytes_per_launch": km_bytes,
+                     "mfma_tflops": flops / (km_ms / 1000.0) / 1e12},
+        "seed": {"kernel": "kmeanspp_kernel", "ms": seed_ms, "bytes_per_launch": seed_bytes,
+                 "gbps": seed_bytes / (seed_ms / 1000.0) / 1e9},
         "setup_s": {"settle_s": round(t_settle, 2)},
     }
     if not args.no_cpu_baseline:
-        # parity: one GPU iteration from c0 on sampled problems against the oracle (a valid
-        # argmin within the fp32 bound, the update bit for bit); then the oracle's own rate
-        cent.copy_(c0)
+        # parity on sampled problems: every seeding draw is a valid k-means++ step of the
+        # oracle's fp64 distances; then one Lloyd iteration from the GPU's seeds gives a
+        # valid argmin (within the fp32 bound) and the oracle's update bit for bit
+        rows_dev = torch.empty((P, Kc), dtype=torch.int32, device=dev)
+        K.kvs_beacon_seed(pts, uni, cent, rows=rows_dev)
+        c_seed = cent.clone()
         K.kvs_beacon_kmeans(pts, cent, 1, assign=asg)
         torch.cuda.synchronize()
         pick = [0, P // 2 + 7, P - 1]
@@ -477,17 +484,22 @@ def bench_kmeans(args) -> None:
         for p in pick:
             x = bf16_bits_to_f64(pts[p].view(torch.int16).cpu().numpy().view(np.uint16))
             xs[p] = x
-            cp = c0[p].cpu().numpy()
+            up = uni[p].cpu().numpy()
+            rows = rows_dev[p].cpu().numpy()
+            mism += int(rows[0] != O.kmeans.seed_index(up[0], N))
+            mism += sum(int(not O.kmeans.seed_step_valid(x, rows[:c], up[c], int(rows[c]), 3e-4))
+                        for c in range(1, Kc))
+            cp = c_seed[p].cpu().numpy()
+            mism += int(np.sum(cp != x[rows].astype(np.float32)))
             a = asg[p].cpu().numpy()
             _, sc = O.kmeans.assign(x, cp)
             cmax = float(np.sqrt((cp.astype(np.float64) ** 2).sum(1)).max())
             tol = 1e-4 * (cmax ** 2 + np.sqrt((x * x).sum(1)) * cmax)
-            got = sc[np.arange(N), a]
-            mism += int(np.sum(got > sc.min(axis=1) + tol))
+            mism += int(np.sum(sc[np.arange(N), a] > sc.min(axis=1) + tol))
             flips += int(np.sum(a != np.argmin(sc, axis=1)))
             mism += int(np.sum(O.kmeans.update(x, a, cp) != cent[p].cpu().numpy()))
         t_cpu, n_it = 0.0, 0
-        cc = {p: c0[p].cpu().numpy() for p in pick}
+        cc = {p: c_seed[p].cpu().numpy() for p in pick}
         while t_cpu < args.cpu_seconds:
             for p in pick:
                 ta = time.perf_counter()
@@ -497,7 +509,7 @@ def bench_kmeans(args) -> None:
                 n_it += 1
                 if t_cpu >= args.cpu_seconds:
                     break
-        res["cpu_baseline"] = {"value": n_it * N / t_cpu, "unit": "point-iterations/s", "cores": 1,
+        res["cpu_baseline"] = {"value": n_it * N / t_cpu, "unit": "point-passes/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{n_it} Lloyd iterations over {len(pick)} of {P} problems "
                                          f"({N} queries each) in {t_cpu:.1f} s of oracle time"}

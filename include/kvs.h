@@ -250,6 +250,21 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kvs_beacon_seed -- the initial centroids of kvs_beacon_kmeans by k-means++: for each
+ * problem, centroid 0 is row floor(u_0 * n); then, with D2_i the squared distance
+ * (fp32 sums) from row i to its nearest chosen centroid, centroid c is the first row
+ * in row order whose running sum of D2 exceeds u_c * sum(D2) (a draw with probability
+ * D2_i / sum(D2)), or row floor(u_c * n) when every D2 is 0.  Rows with D2 = 0 are
+ * never drawn otherwise.  points: bf16 [num_problems][num_points][128], finite.
+ * uniforms: fp32 [num_problems][k] in [0, 1), the draws (the caller's generator).
+ * centroids: fp32 [num_problems][k][128] out (the chosen rows, exact).  rows: int32
+ * [num_problems][k] out (the chosen row indices) or NULL.  1 <= k <= 16,
+ * 1 <= num_points <= 16384.  One workgroup per problem; no workspace.
+ */
+kvs_status kvs_beacon_seed(const void *points, int64_t num_problems, int32_t num_points, int32_t k,
+                           const float *uniforms, float *centroids, int32_t *rows, void *stream);
+
+/*
  * kvs_beacon_kmeans -- BeaconKV, Key ideas: queries that revisit distant context form
  * a few similarity groups, and one representative per group (a beacon query) joins the
  * recent queries as an observer.  Lloyd's k-means for num_problems independent

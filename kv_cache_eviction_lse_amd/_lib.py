@@ -26,7 +26,7 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
            "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
-           "kvs_step_select", "kvs_beacon_kmeans", "kvs_eviction_round")
+           "kvs_step_select", "kvs_beacon_kmeans", "kvs_beacon_seed", "kvs_eviction_round")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -113,6 +113,8 @@ def lib() -> C.CDLL:
         L.kvs_eviction_round.restype = C.c_int
         L.kvs_eviction_round.argtypes = [P, P, P, C.c_float, C.c_uint32, C.c_uint32, P, P, P, P, P, P, P, P, P, P,
                                          C.c_size_t, C.c_int32, P, P, P, P, C.c_int64, P, P]
+        L.kvs_beacon_seed.restype = C.c_int
+        L.kvs_beacon_seed.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, P, P, P, P]
         L.kvs_beacon_kmeans.restype = C.c_int
         L.kvs_beacon_kmeans.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.kvs_token_confidence_workspace_size.restype = C.c_size_t
@@ -412,10 +414,20 @@ def kvs_step_select(cache: PagedCache, seqs: SeqBatch, steps: StepSet, scores, b
                                  _stream(stream)))
 
 
+def kvs_beacon_seed(points, uniforms, centroids, rows=None, stream=None) -> None:
+    """points bf16 [P][N][128]; uniforms fp32 [P][K]; centroids fp32 [P][K][128] (out)."""
+    P, N, D = points.shape
+    assert D == 128 and points.element_size() == 2 and uniforms.shape[0] == P
+    assert centroids.shape[0] == P and centroids.shape[1] == uniforms.shape[1] and centroids.element_size() == 4
+    _check(lib().kvs_beacon_seed(_ptr(points), P, N, int(uniforms.shape[1]), _ptr(uniforms), _ptr(centroids),
+                                 _ptr(rows), _stream(stream)))
+
+
 def kvs_beacon_kmeans(points, centroids, iters: int, assign=None, beacons=None, stream=None) -> None:
     """points bf16 [P][N][128]; centroids fp32 [P][K][128] (initial in, final out)."""
     P, N, D = points.shape
-    assert D == 128 and centroids.shape[0] == P and centroids.shape[2] == 128
+    assert D == 128 and points.element_size() == 2
+    assert centroids.shape[0] == P and centroids.shape[2] == 128 and centroids.element_size() == 4
     _check(lib().kvs_beacon_kmeans(_ptr(points), P, N, int(centroids.shape[1]), int(iters), _ptr(centroids),
                                    _ptr(assign), _ptr(beacons), _stream(stream)))
 

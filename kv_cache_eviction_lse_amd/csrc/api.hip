@@ -304,6 +304,21 @@ kvs_status kvs_step_select(const kvs_cache *cache, const kvs_seqs *seqs, const k
   return hip_status(kvs::launch_select(*cache, b, scores, budget, keep, max_len, hs, keys));
 }
 
+kvs_status kvs_beacon_seed(const void *points, int64_t num_problems, int32_t num_points, int32_t k,
+                           const float *uniforms, float *centroids, int32_t *rows, void *stream) {
+  if (num_problems < 0 || num_problems > INT32_MAX)
+    return fail(KVS_ERR_SHAPE, "num_problems = %lld not in [0, 2^31)", (long long)num_problems);
+  if (num_points < 1) return fail(KVS_ERR_SHAPE, "num_points = %d < 1", num_points);
+  if (num_points > kvs::kmeans_seed_max_points())
+    return fail(KVS_ERR_UNSUPPORTED, "num_points = %d > %d", num_points, kvs::kmeans_seed_max_points());
+  if (k < 1 || k > kvs::kmeans_max_k())
+    return fail(KVS_ERR_UNSUPPORTED, "k = %d not in [1, %d]", k, kvs::kmeans_max_k());
+  if (num_problems == 0) return ok();
+  if (!points || !uniforms || !centroids) return fail(KVS_ERR_NULL, "points/uniforms/centroids is NULL");
+  return hip_status(kvs::launch_kmeanspp((const uint16_t *)points, num_problems, num_points, k, uniforms, centroids,
+                                         rows, (hipStream_t)stream));
+}
+
 kvs_status kvs_beacon_kmeans(const void *points, int64_t num_problems, int32_t num_points, int32_t k, int32_t iters,
                              float *centroids, int32_t *assign, void *beacons, void *stream) {
   if (num_problems < 0 || num_problems > INT32_MAX)

@@ -175,6 +175,128 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
   }
 }
 
+// ---- k-means++ seeding ----
+//
+// The initial centroids: row floor(u_0 n); then, with D2_i the squared distance from row
+// i to its nearest chosen centroid, the first row (in row order) whose running sum of D2
+// exceeds u_c sum(D2) -- a draw with probability D2_i / sum(D2) by inverting the
+// cumulative sum -- or floor(u_c n) when every D2 is 0.  The uniforms are inputs.  One
+// 256-thread workgroup per problem: D2 lives in LDS; per round every thread takes whole
+// rows (fp32 sums of squares) for the newest centroid, then per-thread runs of D2 in row
+// order, a block scan and a block minimum find the drawn row.
+constexpr int kSeedThreads = 256;
+constexpr int kSeedMaxN = 16384;
+
+struct SeedArgs {
+  const uint16_t *x;       // bf16 [P][N][128]
+  const float *u;          // [P][K] uniforms in [0, 1)
+  float *cent;             // fp32 [P][K][128]
+  int32_t *rows;           // int32 [P][K] or null
+  int32_t N, K;
+};
+
+__device__ __forceinline__ int32_t seed_row(float u, int32_t n) {
+  const int32_t r = (int32_t)floor((double)u * (double)n);
+  return r < n - 1 ? (r > 0 ? r : 0) : n - 1;
+}
+
+__global__ __launch_bounds__(kSeedThreads) void kmeanspp_kernel(SeedArgs a) {
+  __shared__ float d2[kSeedMaxN];
+  __shared__ __attribute__((aligned(16))) float cen[kHeadDim];
+  __shared__ float wtot[kSeedThreads / 64];
+  __shared__ int32_t wred[2][kSeedThreads / 64];
+  const int64_t p = blockIdx.x;
+  const int32_t N = a.N, K = a.K;
+  const uint16_t *xp = a.x + p * (int64_t)N * kHeadDim;
+  const float *up = a.u + p * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t per = (N + kSeedThreads - 1) / kSeedThreads;
+  const int32_t j0 = min(tid * per, N), j1 = min(j0 + per, N);
+  int32_t row = seed_row(up[0], N);
+  for (int32_t c = 0; c < K; ++c) {
+    __syncthreads();                                   // the previous round is done with cen
+    if (tid < kHeadDim) {
+      const float v = bf16_f(xp[(int64_t)row * kHeadDim + tid]);
+      cen[tid] = v;
+      a.cent[(p * K + c) * kHeadDim + tid] = v;
+    }
+    if (tid == 0 && a.rows) a.rows[p * K + c] = row;
+    if (c == K - 1) break;
+    __syncthreads();
+    for (int32_t j = tid; j < N; j += kSeedThreads) {
+      const uint4 *xr = (const uint4 *)(xp + (int64_t)j * kHeadDim);
+      float acc = 0.f;
+#pragma unroll 4
+      for (int q = 0; q < kHeadDim / 8; ++q) {
+        const uint4 w = xr[q];
+        const float4 c0 = *(const float4 *)&cen[8 * q], c1 = *(const float4 *)&cen[8 * q + 4];
+        const float t[8] = {__uint_as_float(w.x << 16) - c0.x, __uint_as_float(w.x & 0xFFFF0000u) - c0.y,
+                            __uint_as_float(w.y << 16) - c0.z, __uint_as_float(w.y & 0xFFFF0000u) - c0.w,
+                            __uint_as_float(w.z << 16) - c1.x, __uint_as_float(w.z & 0xFFFF0000u) - c1.y,
+                            __uint_as_float(w.w << 16) - c1.z, __uint_as_float(w.w & 0xFFFF0000u) - c1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(t[e], t[e], acc);
+      }
+      d2[j] = c == 0 ? acc : fminf(d2[j], acc);
+    }
+    __syncthreads();
+    // running sums in row order: thread t owns rows j0 .. j1 - 1
+    float part = 0.f;
+    for (int32_t j = j0; j < j1; ++j) part += d2[j];
+    float incl = part;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    float before = 0.f, total = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSeedThreads / 64; ++w) {
+      before += w < wave ? wtot[w] : 0.f;
+      total += wtot[w];
+    }
+    const float un = up[c + 1];
+    int32_t next;
+    if (!(total > 0.f)) {
+      next = seed_row(un, N);
+    } else {
+      const float target = un * total;
+      int32_t cand = INT32_MAX, last = -1;
+      float run = before + (incl - part);
+      for (int32_t j = j0; j < j1; ++j) {
+        const float v = d2[j];
+        run += v;
+        if (v > 0.f) {
+          last = j;
+          if (cand == INT32_MAX && run > target) cand = j;
+        }
+      }
+      // the first candidate row of the block (else the last row with D2 > 0)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        cand = min(cand, __shfl_xor(cand, o));
+        last = max(last, __shfl_xor(last, o));
+      }
+      if (lane == 0) {
+        wred[0][wave] = cand;
+        wred[1][wave] = last;
+      }
+      __syncthreads();
+      cand = INT32_MAX;
+      last = -1;
+#pragma unroll
+      for (int w = 0; w < kSeedThreads / 64; ++w) {
+        cand = min(cand, wred[0][w]);
+        last = max(last, wred[1][w]);
+      }
+      next = cand != INT32_MAX ? cand : last;
+    }
+    row = next;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K, int32_t T, float *centroids,
@@ -193,5 +315,20 @@ hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K
 }
 
 int32_t kmeans_max_k() { return kKmMaxK; }
+int32_t kmeans_seed_max_points() { return kSeedMaxN; }
+
+hipError_t launch_kmeanspp(const uint16_t *points, int64_t P, int32_t N, int32_t K, const float *uniforms,
+                           float *centroids, int32_t *rows, hipStream_t st) {
+  if (P == 0) return hipSuccess;
+  SeedArgs a{};
+  a.x = points;
+  a.u = uniforms;
+  a.cent = centroids;
+  a.rows = rows;
+  a.N = N;
+  a.K = K;
+  kmeanspp_kernel<<<dim3((unsigned)P), kSeedThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
 
 }  // namespace kvs

@@ -86,6 +86,9 @@ hipError_t launch_step_keys(const Batch &b, const float *scores, const int64_t *
 int32_t kmeans_max_k();
 hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K, int32_t T, float *centroids,
                          int32_t *assign, uint16_t *beacons, hipStream_t st);
+int32_t kmeans_seed_max_points();
+hipError_t launch_kmeanspp(const uint16_t *points, int64_t P, int32_t N, int32_t K, const float *uniforms,
+                           float *centroids, int32_t *rows, hipStream_t st);
 
 // Token confidence (mean NLL of the k most probable tokens per logits row).
 int64_t conf_max_vocab();

@@ -346,3 +346,15 @@ def test_eviction_round_validation():
     assert L.kvs_eviction_round(C.byref(c2), C.byref(hs.s), C.byref(o2), C.c_float(0.1), 9, 10, FAKE, FAKE, FAKE,
                                 bud.ctypes.data, FAKE, None, FAKE, FAKE, FAKE, None, 0, 1, None, None, None,
                                 None, 0, None, None) == 2
+
+
+def test_beacon_seed_validation():
+    L = K.lib()
+
+    def run(P=4, N=100, k=16, pts=FAKE, u=FAKE, cent=FAKE):
+        return L.kvs_beacon_seed(pts, P, N, k, u, cent, None, None)
+
+    assert run(P=-1) == 2 and run(N=0) == 2
+    assert run(N=16385) == 3 and run(k=0) == 3 and run(k=17) == 3
+    assert run(pts=None) == 1 and run(u=None) == 1 and run(cent=None) == 1
+    assert run(P=0, pts=None, u=None, cent=None) == 0

@@ -110,3 +110,79 @@ def test_kmeans_zero_iterations_and_empty_groups():
     c, a, _ = run(xb, c0, 3)
     np.testing.assert_array_equal(c[:, 3], c0[:, 3])
     assert not np.any(a == 3)
+
+
+def seed(xb, u):
+    import torch
+    K = _K()
+    dev = torch.device("cuda", 0)
+    P, N, _ = xb.shape
+    pts = torch.from_numpy(xb.view(np.int16)).to(dev)
+    uu = torch.from_numpy(np.ascontiguousarray(u, np.float32)).to(dev)
+    cent = torch.full((P, u.shape[1], 128), float("nan"), dtype=torch.float32, device=dev)
+    rows = torch.full((P, u.shape[1]), -1, dtype=torch.int32, device=dev)
+    K.kvs_beacon_seed(pts, uu, cent, rows=rows)
+    torch.cuda.synchronize()
+    return cent.cpu().numpy(), rows.cpu().numpy()
+
+
+# fp32 running sums of up to 16 384 squared distances: the target u * sum can move
+# across a row boundary by the sums' rounding, at most about n u_32 of the total
+SEED_RTOL = 3e-4
+
+
+@pytest.mark.parametrize("N,K", [(4096, 16), (1000, 7), (300, 16), (17, 4), (1, 3)])
+def test_seed_draws_are_valid_kmeanspp_steps(N, K):
+    # every draw, given the GPU's earlier rows, is a valid inverse-CDF draw of the
+    # oracle's fp64 D2; the centroids are the drawn rows exactly; most draws equal the
+    # oracle's own
+    rng = np.random.default_rng(N * 7 + K)
+    P = 3
+    xb = WB.normal_history(rng, P, N)
+    x = bf16_bits_to_f64(xb)
+    u = rng.random((P, K)).astype(np.float32)
+    print(f"kmeans++ seed N={N} K={K}", flush=True)
+    cent, rows = seed(xb, u)
+    same = 0
+    for p in range(P):
+        assert rows[p, 0] == KO.seed_index(u[p, 0], N)
+        for c in range(1, K):
+            assert KO.seed_step_valid(x[p], rows[p, :c], u[p, c], int(rows[p, c]), SEED_RTOL), (p, c)
+        np.testing.assert_array_equal(cent[p], x[p, rows[p]].astype(np.float32))
+        same += int(np.array_equal(rows[p], KO.kmeanspp(x[p], u[p])[1]))
+    assert same >= P - 1
+
+
+def test_seed_degenerate_rows():
+    # every row equal: D2 is 0 after the first draw, so each draw is floor(u n); a
+    # history with duplicated rows never draws a row already chosen while D2 > 0
+    rng = np.random.default_rng(9)
+    xb = np.repeat(WB.normal_history(rng, 1, 1), 64, axis=1)
+    u = np.array([[0.05, 0.5, 0.99, 0.0]], np.float32)
+    cent, rows = seed(xb, u)
+    np.testing.assert_array_equal(rows[0], [3, 32, 63, 0])
+    yb = np.concatenate([WB.normal_history(rng, 1, 8)] * 20, axis=1)       # 160 rows, 8 distinct
+    u2 = rng.random((1, 8)).astype(np.float32)
+    _, rows2 = seed(yb, u2)
+    distinct = {tuple(yb[0, r]) for r in rows2[0]}
+    assert len(distinct) == 8
+
+
+def test_seed_then_lloyd_matches_oracle_on_separated_groups():
+    # seeding and 10 Lloyd iterations on separated groups: the draws match the oracle's
+    # and so does the whole run
+    rng = np.random.default_rng(12)
+    xs, _ = zip(*[WB.grouped_history(rng, 2000, 16, spread=6.0, noise=0.2) for _ in range(2)])
+    xb = np.stack(xs)
+    x = bf16_bits_to_f64(xb)
+    u = rng.random((2, 16)).astype(np.float32)
+    cent, rows = seed(xb, u)
+    for p in range(2):
+        c_ref, r_ref = KO.kmeanspp(x[p], u[p])
+        np.testing.assert_array_equal(rows[p], r_ref)
+        np.testing.assert_array_equal(cent[p], c_ref)
+    c, a, _ = run(xb, cent, 10)
+    for p in range(2):
+        cw, aw = KO.lloyd(x[p], cent[p], 10)
+        np.testing.assert_array_equal(a[p], aw)
+        np.testing.assert_array_equal(c[p], cw)
