@@ -416,14 +416,22 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   // Common case first: when at least K entries share the largest CRF (every recent hit
   // has CRF exactly 1 once the decayed prior rounds away), that value is c* and no
   // radix pass over CRF is needed.
-  uint32_t band = ~0u, bor = 0u, cmax = 0u;
+  // Otherwise the keys are split at 1.0 first (a hit's CRF is at least 1): c* lies among
+  // the keys >= 1 when there are at least K of them, else among the keys below 1 (with
+  // every key >= 1 kept).  The radix search then runs on one side only, whose keys
+  // share a longer prefix, so it needs fewer passes.
+  constexpr uint32_t kOne = 0x3F800000u;           // 1.0f; keys are fp32 bits of values >= 0
+  uint32_t band_hi = ~0u, bor_hi = 0u, band_lo = ~0u, bor_lo = 0u, cmax = 0u, ge = 0u;
 #pragma unroll
   for (int u = 0; u < kRegU; ++u) {
-    band &= u < cnt ? c[u] : ~0u;
-    bor |= c[u];
+    const bool v = u < cnt, hi = c[u] >= kOne;
+    band_hi &= v && hi ? c[u] : ~0u;
+    bor_hi |= v && hi ? c[u] : 0u;
+    band_lo &= v && !hi ? c[u] : ~0u;
+    bor_lo |= v && !hi ? c[u] : 0u;
+    ge += v && hi ? 1u : 0u;
     cmax = c[u] > cmax ? c[u] : cmax;
   }
-  block_and_or(band, bor, (uint32_t *)sh.scratch);
   cmax = block_max_u32(cmax, (uint32_t *)sh.scratch);
   uint32_t at_max = 0;
 #pragma unroll
@@ -435,7 +443,13 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     r1.above = 0;
     r1.at = n_max;
   } else {
-    r1 = reg_select<true, false>(c, cnt, all, one, (uint64_t)K, 0, 1, band, bor, sh);
+    const uint64_t n_ge = block_sum_u64(ge, sh.scratch);
+    const bool upper = n_ge >= (uint64_t)K;
+    uint32_t band = upper ? band_hi : band_lo, bor = upper ? bor_hi : bor_lo;
+    block_and_or(band, bor, (uint32_t *)sh.scratch);
+    auto side = [&](int u) { return (c[u] >= kOne) == upper; };
+    r1 = reg_select<true, false>(c, cnt, side, one, upper ? (uint64_t)K : (uint64_t)K - n_ge, 0, 1, band, bor, sh);
+    if (!upper) r1.above += n_ge;
   }
   const uint32_t cstar = r1.key;
   const uint64_t need = K - r1.above;          // entries to keep among CRF == c*
