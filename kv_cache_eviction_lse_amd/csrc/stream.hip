@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   __shared__ int32_t bt_lds[kRegBtCap];
   __shared__ RegShared sh;
   __shared__ uint32_t flag_scratch[kStreamWaves];
-  __shared__ uint32_t tie_s[kTieList];
-  __shared__ int32_t tie_j[kTieList];
+  __shared__ __attribute__((aligned(16))) uint32_t tie_s[kTieList];
+  __shared__ __attribute__((aligned(16))) int32_t tie_j[kTieList];
   __shared__ uint32_t tie_count;
 
   const int32_t i = blockIdx.y;
@@ -482,8 +482,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     for (int x = tid; x < nt; x += kStreamThreads) {
       const uint32_t sx = tie_s[x];
       const int32_t jx = tie_j[x];
+      // ties ahead of x in (s desc, slot asc), four at a time (16-byte LDS reads, the
+      // same address in every lane); the slots past nt are never compared
       uint32_t rank = 0;
-      for (int y = 0; y < nt; ++y) {
+      int y = 0;
+#pragma unroll 4
+      for (; y + 4 <= nt; y += 4) {
+        const uint4 sy = *(const uint4 *)&tie_s[y];
+        const int4 jy = *(const int4 *)&tie_j[y];
+        rank += (sy.x > sx || (sy.x == sx && jy.x < jx)) ? 1u : 0u;
+        rank += (sy.y > sx || (sy.y == sx && jy.y < jx)) ? 1u : 0u;
+        rank += (sy.z > sx || (sy.z == sx && jy.z < jx)) ? 1u : 0u;
+        rank += (sy.w > sx || (sy.w == sx && jy.w < jx)) ? 1u : 0u;
+      }
+      for (; y < nt; ++y) {
         const uint32_t sy = tie_s[y];
         rank += (sy > sx || (sy == sx && tie_j[y] < jx)) ? 1u : 0u;
       }
