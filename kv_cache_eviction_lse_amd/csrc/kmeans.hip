@@ -196,8 +196,8 @@ struct SeedArgs {
 };
 
 __device__ __forceinline__ int32_t seed_row(float u, int32_t n) {
-  const int32_t r = (int32_t)floor((double)u * (double)n);
-  return r < n - 1 ? (r > 0 ? r : 0) : n - 1;
+  const double v = u >= 0.f ? (double)u * (double)n : 0.0;   // (a NaN outside the contract: row 0)
+  return v < (double)(n - 1) ? (int32_t)floor(v) : n - 1;
 }
 
 __global__ __launch_bounds__(kSeedThreads) void kmeanspp_kernel(SeedArgs a) {
