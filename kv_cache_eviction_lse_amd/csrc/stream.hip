@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   // Common case first: when at least K entries share the largest CRF (every recent hit
   // has CRF exactly 1 once the decayed prior rounds away), that value is c* and no
   // radix pass over CRF is needed.
-  // Otherwise the keys are split at 1.0 first (a hit's CRF is at least 1): c* lies among
+  // Otherwise CRF keys are split at 1.0 first (a hit's CRF is at least 1): c* lies among
   // the keys >= 1 when there are at least K of them, else among the keys below 1 (with
   // every key >= 1 kept).  The radix search then runs on one side only, whose keys
   // share a longer prefix, so it needs fewer passes.
@@ -442,6 +442,11 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     r1.key = cmax;
     r1.above = 0;
     r1.at = n_max;
+  } else if (!LRFU && a.keys) {
+    // caller keys (step-aware ranking) have no reason to straddle 1.0: no split
+    uint32_t band = band_hi & band_lo, bor = bor_hi | bor_lo;
+    block_and_or(band, bor, (uint32_t *)sh.scratch);
+    r1 = reg_select<true, false>(c, cnt, all, one, (uint64_t)K, 0, 1, band, bor, sh);
   } else {
     const uint64_t n_ge = block_sum_u64(ge, sh.scratch);
     const bool upper = n_ge >= (uint64_t)K;
