@@ -333,13 +333,30 @@ __device__ __forceinline__ void conf_reduce(const ConfArgs &a, int64_t cidx, uin
   // only the at most k-1 threads whose maximum is above M_k hold any ----
   fence_words(w);
   if (tkey > mk) {
-    // one pass, one LDS atomic per value appended (a few per such thread)
+    // Count this thread's values above M_k, reserve that many slots with one LDS
+    // atomic, then write them (an atomic per value, each waiting for its slot index,
+    // cost more than the rest of the chunk).  A thread with one such value holds only
+    // its maximum, which it writes without a second pass.  The compare is on floats:
+    // it differs from the key order only in placing +0 level with a -0 M_k, and both
+    // add the same zero to the sum of the k largest.
     const float fmk = key_f(mk);
+    uint32_t n = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const float x = logit<BF16, W>(w, i);
-      if (x > fmk || (x == fmk && fkey(x) > mk)) sh.cand[atomicAdd(&sh.ncand, 1u)] = fkey(x);
+      n += logit<BF16, W>(w, i) > fmk ? 1u : 0u;
       if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (n == 1) {
+      sh.cand[atomicAdd(&sh.ncand, 1u)] = tkey;
+    } else {
+      uint32_t at = atomicAdd(&sh.ncand, n);
+      fence_words(w);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const float x = logit<BF16, W>(w, i);
+        if (x > fmk) sh.cand[at++] = fkey(x);
+        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   lds_barrier();
