@@ -90,13 +90,6 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   return x;
 }
 
-// Address (in elements) of the row of key position pos of stream (l, g).
-__device__ __forceinline__ int64_t row_elem(const DecodeArgs &a, const int32_t *bt_row, int32_t l, int32_t g,
-                                            int32_t pos) {
-  const int64_t page = bt_row[pos >> 4];
-  return ((((int64_t)l * a.b.num_pages + page) * a.b.Hkv + g) * kPage + (pos & 15)) * kHeadDim;
-}
-
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 // LDS written by some lanes of a wave and then read by others: the wave's LDS
@@ -170,6 +163,32 @@ __global__ __launch_bounds__(64, RMAX <= 4 ? 4 : (RMAX <= 8 ? 2 : 1)) void decod
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; }
 
+  // Element offset of (l, physical page, g, row 0) for each of the split's (at most 32)
+  // logical pages, lane p % 32 holding page p0 / 16 + p.  Every position visited lies in
+  // [p0, p1), so its K and V rows are found with a lane exchange (K, per-lane
+  // positions) or a lane read (V, one position per load) instead of a block-table load
+  // that the row load would have to wait for.
+  const int32_t pg0 = p0 >> 4, pg_last = (p1 - 1) >> 4;
+  int64_t pbase;
+  {
+    const int32_t pg = pg0 + (lane & 31);
+    const int64_t page = pg <= pg_last ? bt_row[pg] : 0;
+    pbase = ((int64_t)l * a.b.num_pages + page) * a.b.Hkv * (kPage * kHeadDim) + (int64_t)g * (kPage * kHeadDim);
+  }
+  const int32_t pb_lo = (int32_t)(uint32_t)pbase, pb_hi = (int32_t)(pbase >> 32);
+  auto page_base_of = [&](int32_t pos) {       // pos per lane, in [p0, p1)
+    const int src = (pos >> 4) - pg0;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, pb_lo);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, pb_hi);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  auto page_base_uniform = [&](int32_t pos) {  // pos the same in every lane, in [p0, p1)
+    const int src = (pos >> 4) - pg0;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(pb_lo, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(pb_hi, src);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+
   // tiles that lie wholly before the first live position are skipped, so every tile
   // visited holds a live key
   const int32_t tbeg = p0 + ((max(start, p0) - p0) / kTile) * kTile;
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(64, RMAX <= 4 ? 4 : (RMAX <= 8 ? 2 : 1)) void decod
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const int32_t pos = min(max(tp + 16 * kg + n, start), p1 - 1);
-      const uint16_t *kr = a.k + row_elem(a, bt_row, l, g, pos) + 8 * blk;
+      const uint16_t *kr = a.k + page_base_of(pos) + (pos & 15) * kHeadDim + 8 * blk;
       d[kg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(64, RMAX <= 4 ? 4 : (RMAX <= 8 ? 2 : 1)) void decod
 #pragma unroll
     for (int q = 0; q < kTile; ++q) {
       const int32_t kp = min(max(tp + q, start), p1 - 1);
-      vw[q] = ((const uint32_t *)(a.v + row_elem(a, bt_row, l, g, kp)))[lane];
+      vw[q] = ((const uint32_t *)(a.v + page_base_uniform(kp) + (kp & 15) * kHeadDim))[lane];
     }
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
