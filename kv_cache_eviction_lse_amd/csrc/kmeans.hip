@@ -17,7 +17,8 @@
 // bf16 parts, 16 significant bits; the points are exact bf16) and the points on N (each lane
 // loads 16 bytes of one point row per slice), takes the argmin, then adds the tile's
 // points to their groups' integer sums with LDS 64-bit atomics (lane = two dimensions;
-// the rows come back from the cache that just served the MFMA operands).  Member counts
+// the rows come back from the cache that just served the MFMA operands).  The next
+// tile's rows are loaded while a tile is processed.  Member counts
 // stay in registers (lane k counts group k) until the end of the iteration.
 #include "kvs_device.h"
 
@@ -100,21 +101,30 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
     for (int i = 0; i < 4; ++i) cn4[i] = cn_lds[4 * blk + i];
 
     uint32_t cnt_reg = 0;                              // lane k < 16: members of group k seen by this wave
-    for (int32_t tile = wave; tile < ntiles; tile += kKmWaves) {
-      const int32_t base = tile * 16;
-      // B operands: lane (point n16, block blk) loads dims 32 sl + 8 blk .. + 7
-      const int32_t pc = min(base + n16, N - 1);
-      const uint16_t *xr = xp + (int64_t)pc * kHeadDim + 8 * blk;
-      bf16x8 b[4];
+    // B operands: lane (point n16, block blk) loads dims 32 sl + 8 blk .. + 7; then the
+    // tile's rows again, lane = dims 2 lane, 2 lane + 1 (for the update).
+    // A tile of 16 whole rows starting at base <= N - 16: one address, rows at offsets.
+    auto load_full = [&](int32_t base, bf16x8 (&b)[4], uint32_t (&rw)[16]) {
+      const uint16_t *xr = xp + (int64_t)(base + n16) * kHeadDim + 8 * blk;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) b[sl] = *(const bf16x8 *)(xr + 32 * sl);
-      // the tile's rows again, lane = dims 2 lane, 2 lane + 1 (for the update)
-      uint32_t rw[16];
+      const uint32_t *rr = (const uint32_t *)(xp + (int64_t)base * kHeadDim) + lane;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) rw[q] = rr[q * (kHeadDim / 2)];
+    };
+    // The last, partial tile: rows past the end are clamped to row N - 1 (and not added).
+    auto load_tail = [&](int32_t base, bf16x8 (&b)[4], uint32_t (&rw)[16]) {
+      const int32_t pc = min(base + n16, N - 1);
+      const uint16_t *xr = xp + (int64_t)pc * kHeadDim + 8 * blk;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) b[sl] = *(const bf16x8 *)(xr + 32 * sl);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int32_t pq = min(base + q, N - 1);
         rw[q] = ((const uint32_t *)(xp + (int64_t)pq * kHeadDim))[lane];
       }
+    };
+    auto process = [&](int32_t base, const bf16x8 (&b)[4], const uint32_t (&rw)[16]) {
       kfloatx4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
@@ -155,6 +165,31 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
           cnt_reg += lane == aq ? 1u : 0u;
         }
       }
+    };
+    // Whole tiles, the next tile's loads issued before this one is processed (the last
+    // whole tile of a wave loads itself again instead, from the cache); then the partial
+    // tile, if any.
+    const int32_t nfull = N / 16;
+    int32_t tile = wave;
+    bf16x8 b0[4];
+    uint32_t rw0[16];
+    if (tile < nfull) {
+      load_full(tile * 16, b0, rw0);
+      for (; tile < nfull; tile += kKmWaves) {
+        bf16x8 b1[4];
+        uint32_t rw1[16];
+        const int32_t next = tile + kKmWaves < nfull ? tile + kKmWaves : tile;
+        load_full(next * 16, b1, rw1);
+        process(tile * 16, b0, rw0);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) b0[sl] = b1[sl];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) rw0[q] = rw1[q];
+      }
+    }
+    for (; tile < ntiles; tile += kKmWaves) {
+      load_tail(tile * 16, b0, rw0);
+      process(tile * 16, b0, rw0);
     }
     if (lane < kKmMaxK && cnt_reg) atomicAdd(&cnt_lds[lane], cnt_reg);
     __syncthreads();                                   // every sum and count in
