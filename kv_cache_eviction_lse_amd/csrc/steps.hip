@@ -34,7 +34,9 @@ struct StepArgs {
 constexpr int kStepWaves = 4;
 
 __global__ __launch_bounds__(64 * kStepWaves) void step_key_kernel(StepArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform within the wave: saying so makes every per-step value
+  // below scalar (scalar loads through the constant cache, not vector loads)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t gk = (int64_t)blockIdx.x * kStepWaves + wave;
   if (gk >= a.M) return;
   const int32_t lg = blockIdx.y;
@@ -49,7 +51,8 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_key_kernel(StepArgs a) {
   const int32_t i = lo;
   const int32_t n = a.b.len[i];
   const int32_t first = a.first[gk];
-  const int32_t last = gk + 1 < a.step_off[i + 1] ? a.first[gk + 1] : n;     // one past the step
+  const int32_t next_first = a.first[gk + 1 < a.M ? gk + 1 : gk];           // read with the others
+  const int32_t last = gk + 1 < a.step_off[i + 1] ? next_first : n;          // one past the step
   const int64_t e0 = a.b.entry_off[i];
   const uint32_t *sp = (const uint32_t *)(a.scores + (int64_t)lg * a.b.E + e0);
   // four loads in flight per lane, then the tail
