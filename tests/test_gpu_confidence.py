@@ -96,6 +96,29 @@ def test_confidence_largest_vocabulary(dtype):
     check(gpu_conf(x, 20), exact, 20, "2^20")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [4097, 32768])
+def test_confidence_signed_zeros_at_the_kth(dtype, V):
+    # rows whose k-th largest logit is a zero, with +0 and -0 spread over many threads
+    # (the chunk kernel compares candidates against M_k as floats, where +0 and -0 are
+    # level; both add the same zero to the top-k sum)
+    rng = np.random.default_rng(11)
+    rows = []
+    for n_pos, n_pz, n_nz in [(0, 15, 15), (5, 10, 20), (0, 0, 25), (0, 25, 0), (19, 1, 1), (3, 40, 40)]:
+        z = (-1.0 - 3.0 * rng.random(V)).astype(np.float32)
+        pos = rng.choice(V, n_pos + n_pz + n_nz, replace=False)
+        z[pos[:n_pos]] = (1.0 + rng.random(n_pos)).astype(np.float32)
+        z[pos[n_pos:n_pos + n_pz]] = np.float32(0.0)
+        z[pos[n_pos + n_pz:]] = np.float32(-0.0)
+        rows.append(z)
+    z = np.stack(rows)
+    assert np.signbit(z).any() and (z == 0).sum() > 0
+    print(f"confidence signed zeros dtype={dtype} V={V}", flush=True)
+    x, exact = device_rows(z, dtype)
+    check(gpu_conf(x, 20), exact, 20, ("zeros", dtype, V))
+    check(gpu_conf(x, 1), exact, 1, ("zeros k=1", dtype, V))
+
+
 def test_confidence_bench_shape_sampled():
     # the benchmark's shape (4096 steps x 128 256 bf16 logits, drawn on the device);
     # a sample of rows is read back and checked against the oracle
