@@ -18,7 +18,8 @@
 // loads 16 bytes of one point row per slice), takes the argmin, then adds the tile's
 // points to their groups' integer sums with LDS 64-bit atomics (lane = two dimensions;
 // the rows come back from the cache that just served the MFMA operands).  The next
-// tile's rows are loaded while a tile is processed.  Member counts
+// tile's rows are loaded while a tile is processed.  From the second iteration on, the
+// integer sums are carried over and corrected by the points that changed group only.  Member counts
 // stay in registers (lane k counts group k) until the end of the iteration.
 #include "kvs_device.h"
 
@@ -28,6 +29,9 @@ namespace {
 constexpr int kKmMaxK = 16;
 constexpr int kKmThreads = 512;
 constexpr int kKmWaves = kKmThreads / 64;
+// Up to this many points per problem, iterations after the first update the integer
+// sums by the points that changed group only (their previous groups are kept in LDS).
+constexpr int kKmDeltaMaxN = 16384;
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float kfloatx4;
 
@@ -56,6 +60,7 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
   __shared__ float cn_lds[kKmMaxK];
   __shared__ unsigned long long sum_lds[kKmMaxK][kHeadDim];
   __shared__ uint32_t cnt_lds[kKmMaxK];
+  __shared__ uint8_t prev_lds[kKmDeltaMaxN];      // each point's group in the previous iteration
 
   const int64_t p = blockIdx.x;
   const int32_t N = a.N, K = a.K;
@@ -70,8 +75,14 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
   const int32_t ntiles = (N + 15) / 16;
 
   for (int32_t t = 0; t < a.T; ++t) {
-    for (int e = tid; e < kKmMaxK * kHeadDim; e += kKmThreads) sum_lds[e / kHeadDim][e % kHeadDim] = 0ull;
-    if (tid < kKmMaxK) cnt_lds[tid] = 0u;
+    // The sums are exact integers, so they can be carried from one iteration to the next
+    // and corrected by the points that moved (subtracted from the old group, added to the
+    // new): the same integers as summing all members afresh.
+    const bool delta = t > 0 && N <= kKmDeltaMaxN;
+    if (!delta) {
+      for (int e = tid; e < kKmMaxK * kHeadDim; e += kKmThreads) sum_lds[e / kHeadDim][e % kHeadDim] = 0ull;
+      if (tid < kKmMaxK) cnt_lds[tid] = 0u;
+    }
     __syncthreads();                                   // c_lds (initial or updated) visible
     // ||c_k||^2: wave w takes groups 2w, 2w + 1 (groups beyond K score +inf)
 #pragma unroll
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) cn4[i] = cn_lds[4 * blk + i];
 
-    uint32_t cnt_reg = 0;                              // lane k < 16: members of group k seen by this wave
+    uint32_t cnt_reg = 0;   // lane k < 16: change of group k's member count seen by this wave (mod 2^32)
     // B operands: lane (point n16, block blk) loads dims 32 sl + 8 blk .. + 7; then the
     // tile's rows again, lane = dims 2 lane, 2 lane + 1 (for the update).
     // A tile of 16 whole rows starting at base <= N - 16: one address, rows at offsets.
@@ -153,16 +164,31 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
         }
       }
       if (t == a.T - 1 && a.assign && blk == 0 && base + n16 < N) a.assign[p * N + base + n16] = bi;
+      // previous groups of the tile's points (read before this wave overwrites them)
+      int prev = 0;
+      if (N <= kKmDeltaMaxN) {
+        const bool live = base + n16 < N;
+        if (delta) prev = live ? prev_lds[base + n16] : 0;
+        if (blk == 0 && live) prev_lds[base + n16] = (uint8_t)bi;
+      }
       // integer sums of the members (trunc(x 2^16), exact below 2^31 for |x| < 2^15)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         if (base + q < N) {
           const int aq = __builtin_amdgcn_readlane(bi, q);
-          const int32_t v0 = __float2int_rz(__uint_as_float(rw[q] << 16) * 65536.0f);
-          const int32_t v1 = __float2int_rz(__uint_as_float(rw[q] & 0xFFFF0000u) * 65536.0f);
-          atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)(long long)v0);
-          atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)(long long)v1);
-          cnt_reg += lane == aq ? 1u : 0u;
+          const int pq = delta ? __builtin_amdgcn_readlane(prev, q) : -1;
+          if (aq != pq) {
+            const int32_t v0 = __float2int_rz(__uint_as_float(rw[q] << 16) * 65536.0f);
+            const int32_t v1 = __float2int_rz(__uint_as_float(rw[q] & 0xFFFF0000u) * 65536.0f);
+            atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)(long long)v0);
+            atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)(long long)v1);
+            cnt_reg += lane == aq ? 1u : 0u;
+            if (pq >= 0) {
+              atomicAdd(&sum_lds[pq][2 * lane], (unsigned long long)(-(long long)v0));
+              atomicAdd(&sum_lds[pq][2 * lane + 1], (unsigned long long)(-(long long)v1));
+              cnt_reg -= lane == pq ? 1u : 0u;
+            }
+          }
         }
       }
     };

@@ -75,6 +75,28 @@ def test_kmeans_chained_iterations(N, K):
     np.testing.assert_array_equal(a6, a)
 
 
+@pytest.mark.parametrize("N", [16384, 16400])
+def test_kmeans_long_histories(N):
+    # up to 16 384 points, iterations after the first carry the integer sums and correct
+    # them by the points that moved; beyond that every iteration sums afresh.  Both must
+    # give the chain of single iterations, each checked against the oracle's update
+    rng = np.random.default_rng(N)
+    P, K = 1, 16
+    xb = WB.normal_history(rng, P, N)
+    x = bf16_bits_to_f64(xb)
+    c0 = np.stack([x[p, WB.initial_rows(rng, N, K)] for p in range(P)]).astype(np.float32)
+    print(f"kmeans long history N={N}", flush=True)
+    c = c0
+    for it in range(3):
+        c_new, a, _ = run(xb, c, 1)
+        check_assignment(x[0], c[0], a[0])
+        np.testing.assert_array_equal(c_new[0], KO.update(x[0], a[0], c[0]), err_msg=f"iter {it}")
+        c = c_new
+    c3, a3, _ = run(xb, c0, 3)
+    np.testing.assert_array_equal(c3, c)
+    np.testing.assert_array_equal(a3, a)
+
+
 def test_kmeans_separated_groups_match_oracle_exactly():
     # well separated groups: no near ties, so the whole run (assignments and centroids
     # after 10 iterations) equals the oracle's
