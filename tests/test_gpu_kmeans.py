@@ -153,7 +153,7 @@ def seed(xb, u):
 SEED_RTOL = 3e-4
 
 
-@pytest.mark.parametrize("N,K", [(4096, 16), (1000, 7), (300, 16), (17, 4), (1, 3)])
+@pytest.mark.parametrize("N,K", [(16384, 5), (4096, 16), (1000, 7), (300, 16), (17, 4), (1, 3)])
 def test_seed_draws_are_valid_kmeanspp_steps(N, K):
     # every draw, given the GPU's earlier rows, is a valid inverse-CDF draw of the
     # oracle's fp64 D2; the centroids are the drawn rows exactly; most draws equal the
