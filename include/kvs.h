@@ -272,14 +272,19 @@ kvs_status kvs_beacon_seed(const void *points, int64_t num_problems, int32_t num
  * of 128 bf16 values, from given initial centroids, for iters iterations:
  *   assignment  a_i = the k minimising ||c_k||^2 - 2 <x_i, c_k> (ties to the lower k),
  *               scored in fp32 with each centroid carried to 16 significant bits;
- *   update      c_kd = fp32(fp64(sum over members of trunc(x_id * 2^16)) / n_k * 2^-16),
- *               exact integer sums; a group without members keeps its centroid.
+ *   update      c_kd = the mean of the members' coordinates d, rounded once to fp32
+ *               (nearest, ties to even); a group without members keeps its centroid.
+ *               The sums are exact integers on the 2^-32 grid, so the result is the
+ *               exact mean rounded once whenever no member coordinate lies in
+ *               0 < |x| < 2^-25 (those are truncated toward zero on the grid, which
+ *               moves the mean by less than 2^-32), and never depends on member order.
  * points: bf16 [num_problems][num_points][128], finite with |x| < 2^15.
  * centroids: fp32 [num_problems][k][128], the initial centroids in, the final out.
  * assign: int32 [num_problems][num_points] (the last iteration's assignments; not
  * written when iters = 0) or NULL.  beacons: bf16 [num_problems][k][128] (the final
- * centroids rounded to nearest, ties to even) or NULL.  1 <= k <= 16, num_points >= 1,
- * iters >= 0.  One workgroup per problem; no workspace.
+ * centroids rounded to nearest, ties to even) or NULL.  1 <= k <= 16,
+ * 1 <= num_points <= 65536 (KVS_ERR_UNSUPPORTED beyond), iters >= 0.  One workgroup
+ * per problem; no workspace.
  */
 kvs_status kvs_beacon_kmeans(const void *points, int64_t num_problems, int32_t num_points, int32_t k,
                              int32_t iters, float *centroids, int32_t *assign, void *beacons,

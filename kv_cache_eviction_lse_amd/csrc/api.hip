@@ -326,6 +326,8 @@ kvs_status kvs_beacon_kmeans(const void *points, int64_t num_problems, int32_t n
   if (num_points < 1) return fail(KVS_ERR_SHAPE, "num_points = %d < 1", num_points);
   if (k < 1 || k > kvs::kmeans_max_k())
     return fail(KVS_ERR_UNSUPPORTED, "k = %d not in [1, %d]", k, kvs::kmeans_max_k());
+  if (num_points > kvs::kmeans_max_points())
+    return fail(KVS_ERR_UNSUPPORTED, "num_points = %d > %d", num_points, kvs::kmeans_max_points());
   if (iters < 0) return fail(KVS_ERR_SHAPE, "iters = %d < 0", iters);
   if (num_problems == 0) return ok();
   if (!points || !centroids) return fail(KVS_ERR_NULL, "points/centroids is NULL");

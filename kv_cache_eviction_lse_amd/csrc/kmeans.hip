@@ -6,9 +6,13 @@
 // one representative per group (a beacon) is kept beside the recent queries.  The
 // groups are found here by Lloyd's k-means from given initial centroids:
 //   assignment  a_i = argmin_k ||c_k||^2 - 2 <x_i, c_k>   (ties to the lower k);
-//   update      c_kd = fp32(fp64(sum_i trunc(x_id 2^16)) / n_k * 2^-16) over the members,
-//               integer sums so the result does not depend on their order; an empty
-//               group keeps its centroid.
+//   update      c_kd = the mean of the members' coordinates, rounded once to fp32
+//               (nearest, ties to even); an empty group keeps its centroid.
+// The member sums are exact int64 sums of the coordinates on the 2^-32 grid
+// (trunc(x 2^32), exact for every bf16 value with |x| >= 2^-25, and |x| < 2^15), so
+// they do not depend on the members' order, and the quotient sum / n_k is rounded
+// exactly from those integers.  A coordinate 0 < |x| < 2^-25 is truncated toward zero
+// on the grid, which moves the mean by less than 2^-32.
 //
 // One 512-thread workgroup per problem keeps the centroids in LDS for all iterations;
 // two workgroups share a CU (at most 128 VGPRs).
@@ -32,6 +36,8 @@ constexpr int kKmWaves = kKmThreads / 64;
 // Up to this many points per problem, iterations after the first update the integer
 // sums by the points that changed group only (their previous groups are kept in LDS).
 constexpr int kKmDeltaMaxN = 16384;
+// Points per problem: the int64 grid sums stay below 2^63 for |x| < 2^15.
+constexpr int kKmMaxN = 65536;
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float kfloatx4;
 
@@ -48,6 +54,50 @@ __device__ __forceinline__ uint16_t bf16_rn(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 __device__ __forceinline__ float bf16_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// trunc(x 2^32) of a bf16 value x (bit pattern h) with |x| < 2^15, as an exact integer
+// (|result| < 2^47): the 8-bit significand shifted to the 2^-32 grid, truncated toward
+// zero below it (subnormal bf16 values are below 2^-126, so they give 0).
+__device__ __forceinline__ long long bf16_grid32(uint32_t h) {
+  const int32_t e = (int32_t)((h >> 7) & 0xFFu);
+  const uint64_t sig = (uint64_t)(0x80u | (h & 0x7Fu));
+  const int32_t sh = e - 102;                       // value = sig 2^(e - 134) = sig 2^sh 2^-32
+  uint64_t v;
+  if (e == 0) v = 0;
+  else if (sh >= 0) v = sig << (sh < 40 ? sh : 40);
+  else v = sh > -8 ? sig >> (-sh) : 0;
+  return (h & 0x8000u) ? -(long long)v : (long long)v;
+}
+
+// Sign of T - m n 2^32 for a double m with at most 25 significant bits (the product is
+// exact: at most 42 bits).
+__device__ __forceinline__ int cmp_scaled(uint64_t T, uint32_t n, double m) {
+  const double v = m * (double)n * 0x1p32;
+  if (v >= 0x1p63) return -1;                       // T < 2^63
+  const double fl = floor(v);
+  const uint64_t vi = (uint64_t)fl;                 // exact
+  if (T != vi) return T > vi ? 1 : -1;
+  return v > fl ? -1 : 0;
+}
+
+// fp32(S 2^-32 / n), rounded to nearest with ties to even, exactly, for |S| < 2^63 and
+// 1 <= n <= 2^16.  A double quotient lands within one fp32 step of the exact value; the
+// midpoints to both neighbours are then compared with S exactly in integers.
+__device__ __forceinline__ float grid_mean_rn(long long S, uint32_t n) {
+  if (S == 0) return 0.f;
+  const uint64_t T = S < 0 ? 0ull - (uint64_t)S : (uint64_t)S;
+  float f = (float)((double)T / (double)n * 0x1p-32);   // >= 2^-48, a normal number
+  const uint32_t fb = __float_as_uint(f);
+  const float up = __uint_as_float(fb + 1u), dn = __uint_as_float(fb - 1u);
+  const int hi = cmp_scaled(T, n, 0.5 * ((double)f + (double)up));
+  if (hi > 0 || (hi == 0 && (fb & 1u))) {
+    f = up;
+  } else {
+    const int lo = cmp_scaled(T, n, 0.5 * ((double)dn + (double)f));
+    if (lo < 0 || (lo == 0 && (fb & 1u))) f = dn;
+  }
+  return S < 0 ? -f : f;
+}
 
 __device__ __forceinline__ float km_wave_sum(float x) {
 #pragma unroll
@@ -171,21 +221,21 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
         if (delta) prev = live ? prev_lds[base + n16] : 0;
         if (blk == 0 && live) prev_lds[base + n16] = (uint8_t)bi;
       }
-      // integer sums of the members (trunc(x 2^16), exact below 2^31 for |x| < 2^15)
+      // exact integer sums of the members on the 2^-32 grid (|sum| < 2^47 N <= 2^63)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         if (base + q < N) {
           const int aq = __builtin_amdgcn_readlane(bi, q);
           const int pq = delta ? __builtin_amdgcn_readlane(prev, q) : -1;
           if (aq != pq) {
-            const int32_t v0 = __float2int_rz(__uint_as_float(rw[q] << 16) * 65536.0f);
-            const int32_t v1 = __float2int_rz(__uint_as_float(rw[q] & 0xFFFF0000u) * 65536.0f);
-            atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)(long long)v0);
-            atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)(long long)v1);
+            const long long v0 = bf16_grid32(rw[q] & 0xFFFFu);
+            const long long v1 = bf16_grid32(rw[q] >> 16);
+            atomicAdd(&sum_lds[aq][2 * lane], (unsigned long long)v0);
+            atomicAdd(&sum_lds[aq][2 * lane + 1], (unsigned long long)v1);
             cnt_reg += lane == aq ? 1u : 0u;
             if (pq >= 0) {
-              atomicAdd(&sum_lds[pq][2 * lane], (unsigned long long)(-(long long)v0));
-              atomicAdd(&sum_lds[pq][2 * lane + 1], (unsigned long long)(-(long long)v1));
+              atomicAdd(&sum_lds[pq][2 * lane], (unsigned long long)(-v0));
+              atomicAdd(&sum_lds[pq][2 * lane + 1], (unsigned long long)(-v1));
               cnt_reg -= lane == pq ? 1u : 0u;
             }
           }
@@ -222,10 +272,7 @@ __global__ __launch_bounds__(kKmThreads, 4) void kmeans_kernel(KmArgs a) {
     for (int e = tid; e < K * kHeadDim; e += kKmThreads) {
       const int k = e / kHeadDim, d = e % kHeadDim;
       const uint32_t cnt = cnt_lds[k];
-      if (cnt) {
-        const double mean = (double)(long long)sum_lds[k][d] / (double)cnt;
-        c_lds[k][d] = (float)(mean * 0x1p-16);
-      }
+      if (cnt) c_lds[k][d] = grid_mean_rn((long long)sum_lds[k][d], cnt);
     }
     __syncthreads();                                   // sums read before the next iteration clears them
   }
@@ -376,6 +423,7 @@ hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K
 }
 
 int32_t kmeans_max_k() { return kKmMaxK; }
+int32_t kmeans_max_points() { return kKmMaxN; }
 int32_t kmeans_seed_max_points() { return kSeedMaxN; }
 
 hipError_t launch_kmeanspp(const uint16_t *points, int64_t P, int32_t N, int32_t K, const float *uniforms,

@@ -84,6 +84,7 @@ hipError_t launch_step_keys(const Batch &b, const float *scores, const int64_t *
 
 // Beacon k-means: Lloyd iterations over P problems of N bf16 points (128 dims), K <= 16.
 int32_t kmeans_max_k();
+int32_t kmeans_max_points();
 hipError_t launch_kmeans(const uint16_t *points, int64_t P, int32_t N, int32_t K, int32_t T, float *centroids,
                          int32_t *assign, uint16_t *beacons, hipStream_t st);
 int32_t kmeans_seed_max_points();

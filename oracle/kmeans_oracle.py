@@ -17,10 +17,10 @@ Readings (the page names no algorithm; stated here and in the design notes):
       are the final centroids rounded to bf16.
   K2. Assignment: a_i = the k minimising ||c_k||^2 - 2 <x_i, c_k> (the squared distance
       less ||x_i||^2); ties go to the lower k.
-  K3. Update on a fixed-point grid, so that centroids do not depend on summation order:
-      q_id = trunc(x_id 2^16) (exact integers, |x| < 2^15), and for a group with n_k > 0
-      members c_kd = fp32(fp64(fp64(sum_i q_id) / n_k) 2^-16), each step rounded to
-      nearest; an empty group keeps its centroid.
+  K3. Update: the plain member mean.  For a group with n_k > 0 members,
+      c_kd = (sum over members of x_id) / n_k, taken exactly (rational arithmetic) and
+      rounded once to fp32, nearest with ties to even; an empty group keeps its
+      centroid.
   K4. The assignments reported are those of the last iteration's assignment step.
   K5. Initial centroids by k-means++ (the configuration's seeded start), drawn by
       inverting the cumulative distribution of the squared distances in row order with
@@ -28,13 +28,14 @@ Readings (the page names no algorithm; stated here and in the design notes):
 
 The assignment here is taken in fp64 from the exact inputs; the GPU takes it in fp32,
 so the tests accept any choice whose exact score is within the fp32 error bound of
-the minimum (several answers are then correct), and check the update bit for bit.
+the minimum (several answers are then correct), and compare the update with the plain
+mean of the GPU's assignments.
 """
 from __future__ import annotations
 
-import numpy as np
+import math
 
-GRID = 2.0 ** 16
+import numpy as np
 
 
 def check_points(x: np.ndarray) -> np.ndarray:
@@ -52,18 +53,70 @@ def assign(x: np.ndarray, c: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return np.argmin(sc, axis=1), sc          # argmin returns the first (lowest k) minimum
 
 
+def round_to_f32(num: int, den: int) -> np.float32:
+    """The rational num / den (den > 0) rounded once to fp32: nearest, ties to even,
+    with gradual underflow below 2^-126 (IEEE 754 round-to-nearest-even)."""
+    if den <= 0:
+        raise ValueError("den must be positive")
+    if num == 0:
+        return np.float32(0.0)
+    a = abs(num)
+    e = a.bit_length() - den.bit_length()          # 2^e <= a/den < 2^(e+2)
+    if (a << max(0, -e)) < (den << max(0, e)):
+        e -= 1                                      # now 2^e <= a/den < 2^(e+1)
+    qexp = max(e - 23, -149)                        # the fp32 spacing at that magnitude
+    n2, d2 = (a, den << qexp) if qexp >= 0 else (a << -qexp, den)
+    q, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and (q & 1)):
+        q += 1
+    v = math.ldexp(q, qexp)                         # q <= 2^24: exact
+    if v >= 2.0 ** 128:
+        v = math.inf
+    return np.float32(-v if num < 0 else v)
+
+
+def exact_column_sums(x: np.ndarray) -> tuple[list[int], int]:
+    """Exact sums of the columns of a finite fp64 array as (integers S_d, exponent b),
+    column sum d = S_d 2^b.  Each x = m 2^e with m 2^53 an integer (frexp), grouped by
+    exponent and added in Python integers."""
+    x = np.asarray(x, np.float64)
+    if x.shape[0] == 0:
+        return [0] * x.shape[1], 0
+    m, e = np.frexp(x)
+    M = (m * 2.0 ** 53).astype(np.int64)            # exact, |M| < 2^53
+    base = int(e.min()) - 53
+    Mh, Ml = M >> 26, M & ((1 << 26) - 1)           # M = Mh 2^26 + Ml; column sums stay in int64
+    sums = [0] * x.shape[1]
+    for ev in np.unique(e):
+        sel = e == ev
+        h = np.where(sel, Mh, 0).sum(axis=0)
+        lo = np.where(sel, Ml, 0).sum(axis=0)
+        sh = int(ev) - 53 - base
+        for d in range(x.shape[1]):
+            if h[d] or lo[d]:
+                sums[d] += ((int(h[d]) << 26) + int(lo[d])) << sh
+    return sums, base
+
+
+def member_mean(x: np.ndarray) -> np.ndarray:
+    """fp32 [D]: the exact mean of the rows of x, each coordinate rounded once."""
+    n = x.shape[0]
+    sums, b = exact_column_sums(x)
+    if b >= 0:
+        return np.array([round_to_f32(s << b, n) for s in sums], np.float32)
+    return np.array([round_to_f32(s, n << -b) for s in sums], np.float32)
+
+
 def update(x: np.ndarray, a: np.ndarray, c_prev: np.ndarray) -> np.ndarray:
-    """New fp32 centroids from assignments a (reading K3)."""
+    """New fp32 centroids from assignments a: each group's plain member mean, exact
+    and rounded once; an empty group keeps its centroid (reading K3)."""
     x = check_points(x)
     K = c_prev.shape[0]
-    q = np.trunc(x * GRID)                    # exact integers below 2^31
     out = np.array(c_prev, np.float32, copy=True)
     for k in range(K):
         members = np.nonzero(a == k)[0]
-        if members.size == 0:
-            continue
-        sums = [sum(int(v) for v in q[members, d]) for d in range(x.shape[1])]   # exact
-        out[k] = [np.float32((float(s) / float(members.size)) * (1.0 / GRID)) for s in sums]
+        if members.size:
+            out[k] = member_mean(x[members])
     return out
 
 

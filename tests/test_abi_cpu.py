@@ -320,6 +320,7 @@ def test_beacon_kmeans_validation():
     assert run(P=-1) == 2
     assert run(N=0) == 2
     assert run(k=0) == 3 and run(k=17) == 3
+    assert run(N=65537) == 3                           # grid sums would leave int64
     assert run(T=-1) == 2
     assert run(pts=None) == 1 and run(cent=None) == 1
     assert run(P=0, pts=None, cent=None) == 0          # nothing to do

@@ -8,8 +8,15 @@ is a sum of 128 fp32 squares (error <= 128 u ||c||^2, u = 2^-24); <x, c> is a su
 256 exact bf16 products (the centroid in two bf16 parts, residual <= 2^-17 |c|)
 accumulated in fp32, so its error is <= (2^-17 + 257 u) |x| |c| <= 2.3e-5 |x| |c|;
 two scores are compared, so tol = 2 (128 u max||c||^2 + 2 2.3e-5 |x| max|c|), taken
-here as 1e-4 (max||c||^2 + |x| max|c|).  Given the GPU's assignments the update is integer
-arithmetic and a defined rounding sequence: the centroids must match bit for bit.
+here as 1e-4 (max||c||^2 + |x| max|c|).
+
+Given the GPU's assignments, the update is compared with the oracle's plain member mean
+(exact, rounded once to fp32).  The GPU sums the members exactly as integers on the
+2^-32 grid, which holds every bf16 value with |x| >= 2^-25 exactly, and rounds the
+quotient exactly: wherever no member coordinate lies in 0 < |x| < 2^-25 the centroid
+must match bit for bit.  Elsewhere each such member is truncated toward zero by less
+than 2^-32, so the mean moves by less than 2^-32 and the rounded centroids differ by at
+most that plus one fp32 spacing of the result.
 """
 import numpy as np
 import pytest
@@ -41,6 +48,28 @@ def run(xb, c0, iters, sentinel=-7):
     return cent.cpu().numpy(), asg.cpu().numpy(), bcn.cpu().numpy().view(np.uint16)
 
 
+TINY = 2.0 ** -25
+
+
+def check_update(x, a, c_prev, c_gpu, err_msg=""):
+    """The GPU's centroids against the oracle's plain means of the GPU's assignments:
+    bit for bit where no member coordinate is in (0, 2^-25); within 2^-32 plus one fp32
+    spacing elsewhere.  Returns the number of (group, dim) pairs held to the bound."""
+    want = KO.update(x, a, c_prev)
+    tiny = (np.abs(x) > 0) & (np.abs(x) < TINY)
+    loose = np.zeros(want.shape, bool)
+    for k in range(want.shape[0]):
+        m = a == k
+        if m.any():
+            loose[k] = tiny[m].any(axis=0)
+    np.testing.assert_array_equal(c_gpu[~loose], want[~loose], err_msg=err_msg)
+    if loose.any():
+        w = want[loose].astype(np.float64)
+        tol = 2.0 ** -32 + np.spacing(np.abs(want[loose])).astype(np.float64)
+        assert np.all(np.abs(c_gpu[loose].astype(np.float64) - w) <= tol), err_msg
+    return int(loose.sum())
+
+
 def check_assignment(x, c, a):
     _, sc = KO.assign(x, c)
     cc = c.astype(np.float64)
@@ -67,7 +96,7 @@ def test_kmeans_chained_iterations(N, K):
         c_new, a, bcn = run(xb, c, 1)
         for p in range(P):
             check_assignment(x[p], c[p], a[p])
-            np.testing.assert_array_equal(c_new[p], KO.update(x[p], a[p], c[p]), err_msg=f"iter {it} problem {p}")
+            check_update(x[p], a[p], c[p], c_new[p], err_msg=f"iter {it} problem {p}")
         np.testing.assert_array_equal(bcn, KO.to_bf16_bits(c_new))
         c = c_new
     c6, a6, _ = run(xb, c0, 6)
@@ -90,7 +119,7 @@ def test_kmeans_long_histories(N):
     for it in range(3):
         c_new, a, _ = run(xb, c, 1)
         check_assignment(x[0], c[0], a[0])
-        np.testing.assert_array_equal(c_new[0], KO.update(x[0], a[0], c[0]), err_msg=f"iter {it}")
+        check_update(x[0], a[0], c[0], c_new[0], err_msg=f"iter {it}")
         c = c_new
     c3, a3, _ = run(xb, c0, 3)
     np.testing.assert_array_equal(c3, c)
@@ -115,6 +144,63 @@ def test_kmeans_separated_groups_match_oracle_exactly():
         np.testing.assert_array_equal(a[p], labs[p])
         np.testing.assert_array_equal(c[p], cw)
     np.testing.assert_array_equal(bcn, KO.to_bf16_bits(c))
+
+
+def _midpoint_count(xv, want):
+    """How many exact member means sit exactly halfway between two fp32 values."""
+    from fractions import Fraction
+    n = 0
+    for d in range(xv.shape[1]):
+        exact = sum(Fraction(float(v)) for v in xv[:, d]) / xv.shape[0]
+        w = want[d]
+        for nb in (np.nextafter(w, np.float32(-np.inf)), np.nextafter(w, np.float32(np.inf))):
+            n += int(exact == (Fraction(float(w)) + Fraction(float(nb))) / 2)
+    return n
+
+
+def test_kmeans_update_rounding_cases():
+    # one group per problem (k = 1) with 2, 3 or 4 members of mixed magnitudes: the means
+    # need the exact quotient, and many of them sit halfway between two fp32 values
+    # (ties to even)
+    rng = np.random.default_rng(8)
+    P = 256
+    for N in (2, 3, 4):
+        mant = 1.0 + rng.integers(0, 128, (P, N, 128)) / 128.0
+        expo = rng.integers(-24, 3, (P, N, 128)).astype(np.float64)
+        x = rng.choice([-1.0, 1.0], (P, N, 128)) * mant * 2.0 ** expo
+        x[: P // 2, N - 1] = x[: P // 2, 0]          # half the problems: a repeated member
+        xb = WB.f64_to_bf16_bits(x)
+        xv = bf16_bits_to_f64(xb)
+        c0 = np.zeros((P, 1, 128), np.float32)
+        print(f"kmeans update rounding cases N={N}", flush=True)
+        c, a, _ = run(xb, c0, 1)
+        assert np.all(a == 0)
+        ties = 0
+        for p in range(P):
+            want = KO.update(xv[p], a[p], c0[p])
+            np.testing.assert_array_equal(c[p], want, err_msg=f"N {N} problem {p}")
+            if p < 16:
+                ties += _midpoint_count(xv[p], want[0])
+        assert N == 2 or ties > 0, N
+
+
+def test_kmeans_tiny_coordinates_within_bound():
+    # coordinates in (0, 2^-25) are truncated on the GPU's 2^-32 grid: held to the bound
+    rng = np.random.default_rng(10)
+    P, N, K = 2, 700, 4
+    x = rng.standard_normal((P, N, 128))
+    pick = rng.random((P, N, 128)) < 0.05
+    x[pick] = rng.choice([-1.0, 1.0], pick.sum()) * 2.0 ** rng.uniform(-60, -25.5, pick.sum())
+    xb = WB.f64_to_bf16_bits(x)
+    xv = bf16_bits_to_f64(xb)
+    c0 = np.stack([xv[p, :K] for p in range(P)]).astype(np.float32)
+    print("kmeans tiny coordinates", flush=True)
+    c, a, _ = run(xb, c0, 1)
+    loose = 0
+    for p in range(P):
+        check_assignment(xv[p], c0[p], a[p])
+        loose += check_update(xv[p], a[p], c0[p], c[p])
+    assert loose > 0
 
 
 def test_kmeans_zero_iterations_and_empty_groups():
