@@ -80,3 +80,43 @@ def random_batch(seed: int, L: int, Hkv: int, Hq: int, lengths, starts, observer
                  rng.integers(1, 65, S).astype(np.int32), n_prev.astype(np.int32),
                  np.zeros(S, np.int64))
     return lay, HostInputs(k, v, crf, q, lse)
+
+
+CRAFTED_KINDS = ("quantised", "zeros_and_tiny", "dominant", "uniform", "all_zero", "low_bits",
+                 "large", "below_grid", "subnormal_mix")
+
+
+def crafted_scores(rng: np.random.Generator, n: int, kind: str) -> np.ndarray:
+    """fp32 [n] scores built to stress the attention-mass cut: many exact duplicates at
+    the crossing value, zero and sub-grid (< 2^-32) values, one dominant entry, values
+    that differ only in their low mantissa bits, and values near the top of the range."""
+    if kind == "quantised":                       # 9 levels k 2^-10: every level a large tie class
+        s = rng.integers(0, 9, n) * 2.0 ** -10
+    elif kind == "zeros_and_tiny":                # 60 % zeros, 20 % below 2^-32, 20 % two levels
+        u = rng.random(n)
+        s = np.where(u < 0.6, 0.0, np.where(u < 0.8, 2.0 ** rng.uniform(-60, -33, n),
+                                             rng.integers(1, 3, n) * 2.0 ** -9))
+    elif kind == "dominant":                      # one entry with nearly all of the mass
+        s = np.full(n, 2.0 ** -20)
+        s[rng.integers(0, n)] = 1000.0
+    elif kind == "uniform":
+        s = np.full(n, 0.0078125)
+    elif kind == "all_zero":
+        s = np.zeros(n)
+    elif kind == "low_bits":                      # same exponent and high bits, few low-bit patterns
+        s = 2.0 ** -8 * (1.0 + rng.integers(0, 4, n) * 2.0 ** -22)
+    elif kind == "large":                         # masses near 2^42 mixed with small ones
+        s = np.where(rng.random(n) < 0.01, 1023.5, rng.integers(0, 3, n) * 0.25)
+    elif kind == "below_grid":                    # positive scores, all of zero integer mass
+        s = 2.0 ** rng.uniform(-80, -32.5, n)
+    elif kind == "subnormal_mix":                 # fp32 subnormals (mass 0) among two levels
+        s = np.where(rng.random(n) < 0.5, rng.integers(1, 100, n) * 2.0 ** -149,
+                     rng.integers(1, 3, n) * 2.0 ** -12)
+    else:
+        raise ValueError(kind)
+    return np.asarray(s, np.float32)
+
+
+def quantised_priors(rng: np.random.Generator, shape) -> np.ndarray:
+    """Prior CRF values from a few levels, so that updated CRFs tie exactly."""
+    return rng.choice(np.array([0.0, 0.25, 0.5, 1.0, 1.5], np.float32), shape)
