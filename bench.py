@@ -44,28 +44,91 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 D = 128
 
 
-def _stream_job(args):
+# ---------------------------------------------------------------------------
+# the oracle leg of the round benchmark: host bytes of sampled streams, the oracle's
+# replay of the workload's LRFU history, then the oracle's measured round timed over a
+# process pool (one BLAS thread per worker); all of it before the GPU is touched
+# ---------------------------------------------------------------------------
+
+_ORACLE_INPUTS: list = []
+
+
+def _prepare_stream(args):
+    """Host bytes of one sampled stream (mini-pools) and, for a workload with history
+    rounds, the oracle's replay of that history."""
+    from threadpoolctl import threadpool_limits
     from workloads import ALL
     from workloads.device import host_stream_inputs
     from workloads.host import make_layout, observers
-    name, streams = args
-    w = ALL[name]
+    from tests.gpu_util import oracle_history
+    wname, (i, l, g) = args
+    w = ALL[wname]
     lay = make_layout(w)
     G = w.num_q_heads // w.num_kv_heads
-    heads = {(l, h) for (_, l, g) in streams for h in range(g * G, (g + 1) * G)}
-    q = observers(w, lay, heads=heads, only_heads=True, rest_zero=True)
-    return host_stream_inputs(w, lay, q, streams)
+    heads = {(l, h) for h in range(g * G, (g + 1) * G)}
+    with threadpool_limits(1):
+        q0 = observers(w, lay, heads=heads, only_heads=True, rest_zero=True)
+        mini = host_stream_inputs(w, lay, q0, [(i, l, g)])
+        hist = None
+        if w.history_rounds:
+            qh = [observers(w, lay, rnd=r, heads=heads, only_heads=True, rest_zero=True)
+                  for r in range(1, w.history_rounds + 1)]
+            hist = oracle_history(w, lay, q0, qh, (i, l, g), mini)
+    return mini, hist
 
 
-def host_samples(wname, streams, workers):
-    """Host-generated inputs of the sampled streams (one mini-batch per stream), built
-    in worker processes before the GPU is touched."""
-    jobs = [(wname, [s]) for s in streams]
-    if workers <= 1:
-        return [_stream_job(j) for j in jobs]
+def _oracle_round(idx):
+    """The oracle's measured round (score, cut, LRFU, keep set, plan, moves) on sampled
+    stream idx, from its own post-history state, on one BLAS thread; timed."""
+    import oracle as O
+    G, scale, dt, n_prev, budget, mini, hist = _ORACLE_INPUTS[idx]
+    k, v, c, qq, lse, bt, stt, ln, oo = mini
+    c0 = hist[0] if hist is not None else c
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        res = O.eviction_round(k.copy(), v.copy(), c0.copy(), qq, lse, oo, bt, stt, ln, G, scale, 0.5,
+                               np.array([dt]), np.array([n_prev]), np.array([budget]))
+        t = time.perf_counter() - t
+    return {"s": res["s"][(0, 0, 0)], "hit": res["hit"][(0, 0, 0)], "t": t}
+
+
+def oracle_leg(w, lay, sample, workers, min_cpu_s):
+    """Prepare the sampled streams, then time the oracle's round over them with a pool of
+    `workers` processes (fork, before any GPU work), in passes over the sample until the
+    processes have spent min_cpu_s in the oracle.  Returns the first pass's per-stream
+    results and the totals of the timed passes."""
     import multiprocessing as mp
-    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
-        return list(ex.map(_stream_job, jobs))
+    global _ORACLE_INPUTS
+    ctx = mp.get_context("fork")
+    nw = max(1, min(workers, len(sample)))
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=nw, mp_context=ctx) as ex:
+        prep = list(ex.map(_prepare_stream, [(w.name, s) for s in sample]))
+    t_prep = time.perf_counter() - t0
+    G = w.num_q_heads // w.num_kv_heads
+    _ORACLE_INPUTS = [(G, w.scale, int(lay.dt[i]), int(lay.n_prev[i]), int(w.budget), mini, hist)
+                      for (i, _, _), (mini, hist) in zip(sample, prep)]
+    rounds, wall, cpu_s, passes = None, 0.0, 0.0, 0
+    with cf.ProcessPoolExecutor(max_workers=nw, mp_context=ctx) as ex:
+        while passes == 0 or (cpu_s < min_cpu_s and passes < 20):
+            t0 = time.perf_counter()
+            res = list(ex.map(_oracle_round, range(len(sample))))
+            wall += time.perf_counter() - t0
+            cpu_s += sum(r["t"] for r in res)
+            passes += 1
+            rounds = rounds or res
+    return {"hist": [h for (_, h) in prep], "minis": [m for (m, _) in prep], "rounds": rounds, "wall": wall,
+            "cpu_s": cpu_s, "passes": passes, "workers": nw, "prep_s": t_prep}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def load_traffic(workload, name="score_mfma", source="score.hip"):
@@ -408,6 +471,7 @@ def bench_kmeans(args) -> None:
     from workloads import ALL
     from workloads.logits import bf16_bits_to_f64
     import oracle as O
+    from tests.gpu_util import kmeans_update_mismatches
 
     w = ALL["llama3_70b_128k"]
     L, Hq, N, Kc, T = w.num_layers, w.num_q_heads, w.beacon_history, w.beacons, w.kmeans_iters
@@ -497,7 +561,7 @@ def bench_kmeans(args) -> None:
             tol = 1e-4 * (cmax ** 2 + np.sqrt((x * x).sum(1)) * cmax)
             mism += int(np.sum(sc[np.arange(N), a] > sc.min(axis=1) + tol))
             flips += int(np.sum(a != np.argmin(sc, axis=1)))
-            mism += int(np.sum(O.kmeans.update(x, a, cp) != cent[p].cpu().numpy()))
+            mism += kmeans_update_mismatches(x, a, cp, cent[p].cpu().numpy())
         t_cpu, n_it = 0.0, 0
         cc = {p: c_seed[p].cpu().numpy() for p in pick}
         while t_cpu < args.cpu_seconds:
@@ -531,7 +595,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-streams", type=int, default=8, help="streams in the oracle sample")
+    ap.add_argument("--cpu-streams", type=int, default=48, help="streams in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle CPU time")
     ap.add_argument("--separate", action="store_true",
                     help="run cut/LRFU, keep set, plan and move as four calls instead of two fused ones")
@@ -572,59 +636,98 @@ def main():
     chunks = 0 if args.separate else args.layer_chunks
     lay = make_layout(w)
     L, Hkv, Hq = w.num_layers, w.num_kv_heads, w.num_q_heads
-    # sampled streams: spread over layers and heads
+    G = Hq // Hkv
+    # sampled streams: spread over sequences, layers and heads
     rng = np.random.default_rng(0)
-    all_streams = [(0, l, g) for l in range(L) for g in range(Hkv)]
+    all_streams = [(i, l, g) for i in range(w.num_seqs) if lay.length[i] > 0
+                   for l in range(L) for g in range(Hkv)]
     pick = rng.choice(len(all_streams), size=min(args.cpu_streams, len(all_streams)), replace=False)
     sample = [all_streams[int(p)] for p in sorted(pick)]
     # counter-based draws for the sampled streams' observer heads, seeded PCG64 for the rest
-    G = Hq // Hkv
     heads = {(l, h) for (_, l, g) in sample for h in range(g * G, (g + 1) * G)}
     q_host = observers(w, lay, heads=heads, only_heads=True)
-    workers = min(len(sample), max(1, min(16, len(os.sched_getaffinity(0)))))
+    q_hist = [observers(w, lay, rnd=r, heads=heads, only_heads=True) for r in range(1, w.history_rounds + 1)]
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, cores))
     t0 = time.perf_counter()
-    samples = host_samples(w.name, sample, workers) if not args.no_cpu_baseline else []
+    ora = oracle_leg(w, lay, sample, workers, args.cpu_seconds) if not args.no_cpu_baseline else None
     t_host = time.perf_counter() - t0
 
     import torch
     import kv_cache_eviction_lse_amd as K
     from workloads import device as DV
     import oracle as O
+    from tests.gpu_util import gpu_history, pinned_keep_check
 
     dev = torch.device("cuda", 0)
     t0 = time.perf_counter()
-    d = DV.fill(w, lay, q_host, dev, exact_streams=sample if samples else ())
+    exact = sample if ora is not None else ()
+    pre = {s: DV.mini_stream_bytes(m, G) for s, m in zip(sample, ora["minis"])} if ora is not None else None
+    d = DV.fill(w, lay, q_host, dev, exact_streams=exact, exact_bytes=pre)
+    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
+    obs = K.ObserverSet(d.q, d.lse, lay.obs_off, device=dev)
+    budget_h = np.full(w.num_seqs, w.budget, np.int32)
+    bufs = K.RoundBuffers(K.PagedCache(d.k, d.v, d.crf), seqs, obs, budget_h, keep_hits=True)
+    if w.history_rounds:
+        # the LRFU history: untimed score -> LRFU rounds with fresh observers
+        ex_lse = {s: h[2] for s, h in zip(sample, ora["hist"])} if ora is not None else None
+        gpu_history(w, lay, d, K.PagedCache(d.k, d.v, d.crf), seqs, q_hist, exact, bufs.scores,
+                    bufs.workspace, exact_lse=ex_lse)
     torch.cuda.synchronize()
     t_fill = time.perf_counter() - t0
-    # Each step starts from the workload's prior LRFU state: steps use their own copy of
-    # the initial CRF pool (prepared before timing), so every step evicts from the same
-    # prior ranking instead of re-keeping what the previous step kept.
+    # Each step starts from the workload's prior LRFU state (after its history): steps
+    # use their own copy of that CRF pool (prepared before timing), so every step evicts
+    # from the same ranking instead of re-keeping what the previous step kept.
     # (warmup rounds cycle over at most 8 copies: their results are not used)
     n_warm = min(args.warmup, 8)
     n_copies = n_warm + args.steps + 2   # [0] parity round, [-1] settle and hold rounds
     crfs = [d.crf.clone() for _ in range(n_copies)]
+    # The moves write kept K rows into evicted slots, which changes what the next round
+    # on the same pool scores.  Each timed step therefore gets its own copy of the K pool
+    # as well (V rows only travel, their contents decide nothing), when they fit in
+    # device memory; otherwise the timed steps share the K pool and say so.
+    k_bytes = d.k.numel() * d.k.element_size()
+    fresh_k = k_bytes * (args.steps + 1) < torch.cuda.mem_get_info()[0] * 0.8
+    k_steps = [d.k.clone() for _ in range(args.steps)] if fresh_k else [d.k] * args.steps
     caches = [K.PagedCache(d.k, d.v, c) for c in crfs]
-    cache = caches[0]
-    seqs = K.SeqBatch(lay.block_table, lay.start, lay.length, device=dev)
-    obs = K.ObserverSet(d.q, d.lse, lay.obs_off, device=dev)
-    budget_h = np.full(w.num_seqs, w.budget, np.int32)
-    bufs = K.RoundBuffers(cache, seqs, obs, budget_h)
+    for k in range(args.steps):
+        caches[1 + n_warm + k] = K.PagedCache(k_steps[k], d.v, crfs[1 + n_warm + k])
     decay_h = np.array([K.kvs_lrfu_decay(0.5, int(x)) for x in lay.dt], np.float32)
     decay = torch.from_numpy(decay_h).to(dev)
     n_prev = torch.from_numpy(lay.n_prev.astype(np.int32)).to(dev)
     scale = w.scale
     st = torch.cuda.current_stream()
 
-    # first round: keep the outputs of the sampled streams for a parity spot check
-    if samples:
-        K.eviction_round(cache, seqs, obs, bufs, decay, n_prev, scale, fused=not args.separate,
-                         layer_chunks=chunks)
+    # first round, stage by stage: keep the sampled streams' intermediates for parity
+    rec = {}
+    if ora is not None:
+        c = caches[0]
+        pages = {s: torch.from_numpy(lay.block_table[s[0]][:(int(lay.start[s[0]]) + int(lay.length[s[0]]) + 15)
+                                                          // 16].astype(np.int64)).to(dev) for s in sample}
+
+        def crf_of(s):
+            return c.crf[s[1]][pages[s], s[2]].cpu().numpy()
+
+        def ent(buf, s):
+            i, l, g = s
+            return buf[l, g, int(lay.entry_off[i]):int(lay.entry_off[i + 1])].cpu().numpy()
+
         torch.cuda.synchronize()
-        s_gpu = bufs.scores.cpu().numpy()
-        keep_gpu = bufs.keep.cpu().numpy().astype(bool)
-        first = {"s": s_gpu, "keep": keep_gpu}
-    else:
-        first = None
+        for s in sample:
+            rec[s] = {"crf0": crf_of(s)}
+        K.kvs_score(c, seqs, obs, scale, bufs.scores, bufs.workspace)
+        if args.separate:
+            K.kvs_lrfu_update(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.hit)
+            K.kvs_select(c, seqs, bufs.scores, bufs.budget, bufs.budget_h, bufs.keep)
+        else:
+            K.kvs_lrfu_select(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h, bufs.keep,
+                              hit=bufs.hit)
+        torch.cuda.synchronize()
+        for s in sample:
+            rec[s].update(s=ent(bufs.scores, s), hit=ent(bufs.hit, s).astype(bool),
+                          keep=ent(bufs.keep, s).astype(bool), crf1=crf_of(s))
+        K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+        torch.cuda.synchronize()
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle:
         for _ in range(20):
@@ -637,8 +740,8 @@ def main():
                          fused=not args.separate, layer_chunks=chunks)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # per step: events before the scorer, after it, and after the round's last call
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -646,7 +749,9 @@ def main():
         if chunks > 0:
             # the whole round in one call, scoring overlapped with the cut, keep set and
             # moves of the previous layer chunk (the scorer is timed alone below)
+            evs[k][0].record(st)
             K.eviction_round(c, seqs, obs, bufs, decay, n_prev, scale, layer_chunks=chunks)
+            evs[k][2].record(st)
             continue
         evs[k][0].record(st)
         K.kvs_score(c, seqs, obs, scale, bufs.scores, bufs.workspace)
@@ -659,9 +764,11 @@ def main():
         else:
             K.kvs_lrfu_select(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h, bufs.keep)
             K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+        evs[k][2].record(st)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    round_ev = [a.elapsed_time(c_) for a, _, c_ in evs]
     if chunks > 0:
         # the dominant kernel's launch time, live with HIP events on its stream: the scorer
         # alone on the same inputs, as many launches as timed steps
@@ -670,7 +777,8 @@ def main():
             K.kvs_score(caches[1 + n_warm + k], seqs, obs, scale, bufs.scores, bufs.workspace)
             evs[k][1].record(st)
         torch.cuda.synchronize()
-    score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    score_ev = [a.elapsed_time(b) for a, b, _ in evs]
+    score_ms = float(np.mean(score_ev))
 
     entries = int(lay.entry_off[-1]) * L * Hkv
     rows = int(sum((lay.obs_off[i + 1] - lay.obs_off[i]) for i in range(w.num_seqs))) * Hq * L
@@ -693,7 +801,8 @@ def main():
             n_hold += 50
         hold = {"seconds": round(time.perf_counter() - th0, 2), "steps": n_hold,
                 "ms_per_step": (time.perf_counter() - th0) * 1000.0 / n_hold,
-                "includes": "a CRF-pool reset copy per round"}
+                "includes": "a CRF-pool reset copy per round; the K pool is not reset, so these "
+                            "rounds score rows earlier moves wrote"}
     req_bytes = entries * (2 * D + 8) + rows * (2 * D + 4) + pairs * (4 * 2 * D + 8)
     gbps = req_bytes / (ms_per_step / 1000.0) / 1e9
     score_bytes = entries * (2 * D + 4) + rows * (2 * D + 4)
@@ -706,13 +815,13 @@ def main():
     if score_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > score_bytes / (HBM_PEAK_GBPS * 1e9):
         roofline = {"kernel": "score_mfma_kernel", "bound": "mfma", "achieved": score_tflops,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / MFMA_BF16_PEAK_TFLOPS,
-                    "traffic": traffic, "ms": score_ms, "flops_per_launch": score_flops,
-                    "hbm_gbps": score_gbps}
+                    "traffic": traffic, "ms": score_ms, "ms_median": float(np.median(score_ev)),
+                    "flops_per_launch": score_flops, "hbm_gbps": score_gbps}
     else:
         roofline = {"kernel": "score_mfma_kernel", "bound": "hbm", "achieved": score_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
-                    "traffic": traffic, "ms": score_ms, "bytes_per_launch": score_bytes,
-                    "mfma_tflops": score_tflops}
+                    "traffic": traffic, "ms": score_ms, "ms_median": float(np.median(score_ev)),
+                    "bytes_per_launch": score_bytes, "mfma_tflops": score_tflops}
 
     out = {
         "metric": METRIC,
@@ -730,64 +839,79 @@ def main():
         "config": {"workload": w.name, "layers": L, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": D, "page_size": 16, "context": int(lay.length[0]),
                    "pool_pages": lay.num_pages, "observers": int(lay.obs[0]), "budget": w.budget,
-                   "entries_per_step": entries, "layer_chunks": chunks},
+                   "entries_per_step": entries, "layer_chunks": chunks,
+                   "history_rounds": w.history_rounds,
+                   "step_state": ("each timed step starts from its own copy of the post-history CRF pool "
+                                  "and of the K pool" if fresh_k else
+                                  "each timed step starts from its own copy of the CRF pool; the K pool is "
+                                  "shared, so later steps score the rows earlier moves wrote")},
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "required_bytes_per_step": req_bytes,
         "pairs_per_step": pairs,
+        # per-step round times from HIP events (the events add a few microseconds)
+        "round_events_ms": {"mean": float(np.mean(round_ev)), "median": float(np.median(round_ev)),
+                            "min": float(np.min(round_ev)), "max": float(np.max(round_ev))},
         "roofline": roofline,
     }
     if hold is not None:
         hold["entries_per_s"] = entries / (hold["ms_per_step"] / 1000.0)
         out["hold"] = hold
 
-    if first is not None:
-        # parity spot check of the first round on the sampled streams + CPU baseline
-        worst = 0.0
-        bad = 0
-        pinned_total = 0
-        t_cpu = 0.0
-        n_done = 0
-        passes = 0
-        while True:
-            for (i, l, g), mb in zip(sample, samples):
-                k, v, c, qq, lse, bt, stt, ln, oo = mb
-                k, v, c = k.copy(), v.copy(), c.copy()
-                ta = time.perf_counter()
-                res = O.eviction_round(k, v, c, qq, lse, oo, bt, stt, ln, Hq // Hkv, scale, 0.5,
-                                       np.array([lay.dt[i]]), np.array([lay.n_prev[i]]),
-                                       np.array([w.budget]))
-                t_cpu += time.perf_counter() - ta
-                n_done += int(ln[0])
-                if passes == 0:
-                    e0, e1 = int(lay.entry_off[i]), int(lay.entry_off[i + 1])
-                    so = res["s"][(0, 0, 0)].astype(np.float64)
-                    sg = first["s"][l, g, e0:e1].astype(np.float64)
-                    worst = max(worst, float(np.max(np.abs(sg - so) / so)))
-                    from tests.gpu_util import pinned_keep_check
-                    # the GPU's post-update CRF is not kept; pin by the oracle's margins
-                    crf_o = res["crf"][(0, 0, 0)]
-                    pn, nb = pinned_keep_check(res["s"][(0, 0, 0)], crf_o, res["keep"][(0, 0, 0)],
-                                               res["hit"][(0, 0, 0)], first["s"][l, g, e0:e1],
-                                               crf_o, first["keep"][l, g, e0:e1])
-                    pinned_total += pn
-                    bad += nb
-            passes += 1
-            if t_cpu >= args.cpu_seconds or passes >= 50:
-                break
+    if ora is not None:
+        # parity of the first round on the sampled streams: scores against the oracle on
+        # the same bytes; cut, LRFU and keep set exact on the GPU's own inputs; the keep
+        # set end to end (the oracle's round from the GPU's pre-round CRF) wherever the
+        # oracle's margins pin it; the history's CRF exact wherever no history cut was
+        # within the score tolerance
+        worst, comp_bad, pinned_total, bad, hist_bad, hist_unamb = 0.0, 0, 0, 0, 0, 0
+        for idx, s in enumerate(sample):
+            i, l, g = s
+            n, stt = int(lay.length[i]), int(lay.start[i])
+            pos = stt + np.arange(n)
+            pi, row = pos // 16, pos % 16
+            r, o = rec[s], ora["rounds"][idx]
+            so, ho = o["s"], o["hit"]
+            sg, hg, kg = r["s"], r["hit"], r["keep"]
+            c0, c1 = r["crf0"][pi, row], r["crf1"][pi, row]
+            nz = so > 0
+            if nz.any():
+                worst = max(worst, float(np.max(np.abs(sg[nz].astype(np.float64) - so[nz]) / so[nz])))
+            comp_bad += int(np.sum(hg != O.mass_cut(sg)))
+            want1 = O.lrfu_update(c0, hg, np.float32(decay_h[i]), int(lay.n_prev[i]))
+            comp_bad += int(np.sum(c1.view(np.uint32) != want1.view(np.uint32)))
+            comp_bad += int(np.sum(kg != O.select_top_b(c1, sg, int(w.budget))))
+            crf_tf = O.lrfu_update(c0, ho, O.lrfu_decay(0.5, int(lay.dt[i])), int(lay.n_prev[i]))
+            keep_tf = O.select_top_b(crf_tf, so, int(w.budget))
+            pn, nb = pinned_keep_check(so, crf_tf, keep_tf, ho, sg, c1, kg)
+            pinned_total += pn
+            bad += nb
+            if ora["hist"][idx] is not None:
+                c_hist, unamb, _ = ora["hist"][idx]
+                ch = c_hist[0, pi, 0, row]
+                hist_bad += int(np.sum(c0[unamb].view(np.uint32) != ch[unamb].view(np.uint32)))
+                hist_unamb += int(unamb.sum())
+        n_ent = int(sum(int(lay.length[i]) for (i, _, _) in sample)) * ora["passes"]
+        t_sum = ora["cpu_s"]
         try:
             from threadpoolctl import threadpool_info
-            threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+            blas = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
         except Exception:
-            threads = 1
+            blas = None
         out["cpu_baseline"] = {
-            "value": n_done / t_cpu, "unit": "entries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(sample)} of {L * Hkv} streams (layer, KV head) of the same workload, "
-                      f"{passes} passes, {t_cpu:.1f} s of fp64 numpy oracle time on "
-                      f"{platform.processor() or platform.machine()}",
+            "value": n_ent / ora["wall"], "unit": "entries/s", "cores": ora["workers"], "kind": "oracle",
+            "sample": f"{len(sample)} of {len(all_streams)} streams (sequence, layer, KV head) of the same "
+                      f"workload, {ora['passes']} oracle rounds each (score, cut, LRFU, keep set, plan, moves; "
+                      f"fp64 numpy) over a pool of {ora['workers']} processes with one BLAS thread each: "
+                      f"{ora['wall']:.2f} s wall, {t_sum:.1f} s of process time",
+            "host_cores": cores, "cpu_model": cpu_model(), "blas_threads_per_process": 1,
+            "blas_threads_available": blas, "per_process_entries_per_s": n_ent / t_sum,
         }
         out["parity"] = {"streams": len(sample), "max_rel_score_err": worst,
+                         "component_mismatches": comp_bad,
                          "keep_pinned": pinned_total, "keep_pinned_mismatch": bad}
+        if w.history_rounds:
+            out["parity"].update(history_unambiguous=hist_unamb, history_crf_mismatch=hist_bad)
     if args.calibration_copy:
         # a plain device copy of known size, for scaling the HBM byte counters
         src = torch.empty(args.calibration_copy << 20, dtype=torch.uint8, device=dev)
@@ -796,8 +920,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    out["setup_s"] = {"host_samples": round(t_host, 2), "device_fill": round(t_fill, 2),
-                      "settle_s": round(t_settle, 2)}
+    out["setup_s"] = {"oracle_leg": round(t_host, 2), "oracle_prep": round(ora["prep_s"], 2) if ora else None,
+                      "device_fill_and_history": round(t_fill, 2), "settle_s": round(t_settle, 2)}
     print(json.dumps(out), flush=True)
 
 

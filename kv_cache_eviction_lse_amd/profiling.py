@@ -9,6 +9,14 @@ Socket power and graphics clock while a command runs (amd-smi samples):
 
     python -m kv_cache_eviction_lse_amd.profiling power --interval 0.5 -- python3 bench.py --hold 8
 
+Matrix-core and vector-ALU activity of a kernel per launch, from one counter run
+(SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_MFMA, SQ_INSTS_VALU,
+SQ_INSTS_VALU_TRANS_F32, SQ_ACTIVE_INST_VALU, SQ_VALU_MFMA_COEXEC_CYCLES,
+SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE):
+
+    python -m kv_cache_eviction_lse_amd.profiling compute --dir DIR --kernel score_mfma \
+        --json out.json --command "..." > summary.md
+
 HBM traffic of the scorer per launch, from two counter runs of bench.py with a plain
 copy of known size (`--calibration-copy MiB`) in the same process: FETCH_SIZE and
 WRITE_SIZE of each kernel are scaled by bytes / counter of the copy kernel.
@@ -130,6 +138,67 @@ def traffic(args) -> None:
     print(f"\n{args.source} sha256[:16] = {out['source_sha']}")
 
 
+COMPUTE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                    "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                    "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS, CUS, XCDS = 1024, 256, 8
+
+
+def compute(args) -> None:
+    """Per-launch averages of the compute counters of one kernel and the derived
+    figures: MFMA busy = sum of per-SIMD MFMA busy cycles / (GPU active cycles x 1024
+    SIMDs) (rocprofv3's MfmaUtil expression; GRBM_GUI_ACTIVE is summed over the 8 XCDs
+    in the CSV, so it is divided by 8), bf16 MFMA flops = MOPS x 512."""
+    avg = {}
+    n = {}
+    for c in COMPUTE_COUNTERS:
+        per = _counter(args.dir, c)
+        vals = [v for k, vs in per.items() if args.kernel in k for v in vs]
+        if not vals:
+            sys.exit(f"no {args.kernel} dispatch with {c}")
+        avg[c] = sum(vals) / len(vals)
+        n[c] = len(vals)
+    gui = avg["GRBM_GUI_ACTIVE"] / XCDS
+    out = {"kernel": args.kernel, "source": args.source, "source_sha": source_sha(args.source),
+           "dispatches": min(n.values()), "counters_per_launch": avg,
+           "gpu_active_cycles": gui,
+           "mfma_busy_frac": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS),
+           "mfma_bf16_flops": avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+           "valu_per_mfma": avg["SQ_INSTS_VALU"] / max(avg["SQ_INSTS_MFMA"], 1.0),
+           "trans_per_mfma": avg["SQ_INSTS_VALU_TRANS_F32"] / max(avg["SQ_INSTS_MFMA"], 1.0),
+           "valu_busy_frac": avg["SQ_ACTIVE_INST_VALU"] / CUS / gui,
+           "coexec_frac_of_mfma_busy": avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(avg["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0),
+           "commands": args.command}
+    if args.kernel_us:
+        out["kernel_us"] = args.kernel_us
+        out["clock_ghz_implied"] = gui / (args.kernel_us * 1e3)
+        out["mfma_bf16_tflops"] = out["mfma_bf16_flops"] / (args.kernel_us * 1e-6) / 1e12
+    with open(args.json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"# {args.kernel}: matrix-core and vector-ALU counters per launch ({args.workload})\n")
+    for c in args.command:
+        print(f"Command: `{c}`\n")
+    print(f"Dispatches averaged: {out['dispatches']}\n")
+    print("| counter | per launch |")
+    print("|---|---|")
+    for c in COMPUTE_COUNTERS:
+        print(f"| {c} | {avg[c]:.4e} |")
+    print("\n| derived | value |")
+    print("|---|---|")
+    print(f"| GPU active cycles (GRBM_GUI_ACTIVE / 8 XCDs) | {gui:.4e} |")
+    if args.kernel_us:
+        print(f"| kernel time (trace) | {args.kernel_us:.1f} us |")
+        print(f"| implied graphics clock | {out['clock_ghz_implied']:.2f} GHz |")
+        print(f"| bf16 MFMA rate | {out['mfma_bf16_tflops']:.0f} TFLOP/s |")
+    print(f"| MFMA busy (MFMA busy cycles / (active cycles x 1024 SIMDs)) | {out['mfma_busy_frac']:.3f} |")
+    print(f"| bf16 MFMA flops (MOPS x 512) | {out['mfma_bf16_flops']:.4e} |")
+    print(f"| VALU instructions per MFMA | {out['valu_per_mfma']:.2f} |")
+    print(f"| fp32 transcendental instructions per MFMA | {out['trans_per_mfma']:.2f} |")
+    print(f"| VALU busy (SQ_ACTIVE_INST_VALU / 256 CUs / active cycles) | {out['valu_busy_frac']:.3f} |")
+    print(f"| co-issue cycles / MFMA busy cycles | {out['coexec_frac_of_mfma_busy']:.3f} |")
+    print(f"\n{args.source} sha256[:16] = {out['source_sha']}")
+
+
 def _smi_sample() -> tuple[float, float] | None:
     """(socket power W, first GFX clock MHz) from `amd-smi metric -p -c`, or None."""
     import subprocess
@@ -200,11 +269,19 @@ def main() -> None:
     t.add_argument("--kernel", default=SCORER, help="kernel name substring")
     t.add_argument("--source", default="score.hip", help="csrc file the counters are tied to")
     t.add_argument("--workload", default="llama3_8b_32k")
+    cp = sub.add_parser("compute")
+    cp.add_argument("--dir", required=True)
+    cp.add_argument("--kernel", default=SCORER)
+    cp.add_argument("--json", required=True)
+    cp.add_argument("--source", default="score.hip")
+    cp.add_argument("--workload", default="llama3_8b_32k")
+    cp.add_argument("--kernel-us", type=float, default=0.0, help="the kernel's trace time per launch")
+    cp.add_argument("--command", action="append", default=[])
     pw = sub.add_parser("power")
     pw.add_argument("--interval", type=float, default=0.5)
     pw.add_argument("cmd_args", nargs=argparse.REMAINDER)
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "power": power}[args.cmd](args)
+    {"stats": stats, "traffic": traffic, "power": power, "compute": compute}[args.cmd](args)
 
 
 if __name__ == "__main__":

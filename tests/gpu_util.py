@@ -185,10 +185,86 @@ def _stream_pages(lay, i):
     return lay.block_table[i][:npg].astype(np.int64)
 
 
+def kmeans_update_mismatches(x, a, c_prev, c_gpu, tiny=2.0 ** -25):
+    """Centroids that break the k-means update's bar: bit-equal to the oracle's plain
+    member mean of the GPU's assignments wherever no member coordinate is in (0, tiny),
+    else within 2^-32 plus one fp32 spacing (the GPU sums on the 2^-32 grid)."""
+    want = O.kmeans.update(x, a, c_prev)
+    small = (np.abs(x) > 0) & (np.abs(x) < tiny)
+    loose = np.zeros(want.shape, bool)
+    for k in range(want.shape[0]):
+        m = a == k
+        if m.any():
+            loose[k] = small[m].any(axis=0)
+    bad = int(np.sum(c_gpu[~loose] != want[~loose]))
+    tol = 2.0 ** -32 + np.spacing(np.abs(want[loose])).astype(np.float64)
+    bad += int(np.sum(np.abs(c_gpu[loose].astype(np.float64) - want[loose].astype(np.float64)) > tol))
+    return bad
+
+
+def history_observers(w, lay, heads):
+    """Observer sets (bf16 bits) of the history rounds 1..H: counter-based draws for the
+    (layer, query head) pairs in `heads`, seeded PCG64 draws for the others."""
+    from workloads.host import observers
+    return [observers(w, lay, rnd=r, heads=heads, only_heads=True) for r in range(1, w.history_rounds + 1)]
+
+
+def gpu_history(w, lay, d, cache, seqs, q_hist, exact_streams, scores, workspace, exact_lse=None):
+    """The untimed history rounds on the device, in order: kvs_score with that round's
+    observers (their LSE over the cache's keys), then kvs_lrfu_update with that round's
+    dt; every live entry carries a prior.  exact_lse: {stream: [LSE rows of round r]}
+    computed on the host beforehand (else recomputed here)."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from workloads import device as DV
+    from workloads.host import history_dt
+    dev = _dev()
+    dts = history_dt(w)
+    n_prev = torch.from_numpy(lay.length.astype(np.int32)).to(dev)
+    for r, qh in enumerate(q_hist):
+        ex = {s: v[r] for s, v in exact_lse.items()} if exact_lse else None
+        q_dev, lse_dev = DV.observer_lse(w, lay, d, qh, dev, exact_streams, ex)
+        obs = K.ObserverSet(q_dev, lse_dev, lay.obs_off, device=dev)
+        decay = torch.from_numpy(np.array([K.kvs_lrfu_decay(0.5, int(x)) for x in dts[r]], np.float32)).to(dev)
+        K.kvs_score(cache, seqs, obs, w.scale, scores, workspace)
+        K.kvs_lrfu_update(cache, seqs, scores, 9, 10, decay, n_prev, None)
+        torch.cuda.synchronize()
+        del obs, q_dev, lse_dev
+
+
+def oracle_history(w, lay, q_host0, q_hist, stream, mini, tol=1e-3):
+    """The oracle's replay of the history rounds of one stream on its host bytes (the
+    mini-pools of host_stream_inputs).  Returns (crf_pool after the history,
+    unambiguous [n], LSE rows of each round): an entry is unambiguous when its score was
+    more than tol away from the cut threshold in every history round, so its hit bits,
+    and hence its CRF, do not depend on score rounding."""
+    from workloads import device as DV
+    from workloads.host import history_dt
+    k, v, c, qq, lse, bt, stt, ln, oo = mini
+    c = c.copy()
+    dts = history_dt(w)
+    i = stream[0]
+    n = int(ln[0])
+    unamb = np.ones(n, bool)
+    page, row = O.slot_location(bt[0], stt[0], np.arange(n))
+    lse_rows = []
+    for r, qh in enumerate(q_hist):
+        q_r, lse_r = DV.host_stream_observers(w, lay, q_host0, qh, [stream])
+        lse_rows.append(np.concatenate([lse_r[0, hh] for hh in range(w.group)]))
+        s = O.score(k, q_r, lse_r, oo, bt, stt, ln, w.group, w.scale)[(0, 0, 0)]
+        hit = O.mass_cut(s)
+        if hit.any():
+            tau = float(s[hit].min())
+            unamb &= np.abs(s.astype(np.float64) - tau) > tol * tau
+        c[0, page, 0, row] = O.lrfu_update(c[0, page, 0, row], hit, O.lrfu_decay(0.5, int(dts[r][i])), n)
+    return c, unamb, lse_rows
+
+
 def run_config_sampled(w, lay, q_host, sample, scale=None, fused=False):
     """One round of workload w over its whole cache on the GPU (device-drawn data, the
-    sampled streams overwritten with host-generated bytes), stage by stage; returns the
-    GPU's intermediates for the sampled streams only."""
+    sampled streams overwritten with host-generated bytes), stage by stage, after the
+    workload's history rounds (if any); returns the GPU's intermediates for the sampled
+    streams only."""
     import torch
     import kv_cache_eviction_lse_amd as K
     from workloads import device as DV
@@ -201,6 +277,10 @@ def run_config_sampled(w, lay, q_host, sample, scale=None, fused=False):
     obs = K.ObserverSet(d.q, d.lse, lay.obs_off, device=dev)
     budget_h = np.full(w.num_seqs, w.budget, np.int32)
     bufs = K.RoundBuffers(cache, seqs, obs, budget_h, keep_hits=True)
+    if w.history_rounds:
+        heads = {(l, h) for (_, l, g) in sample for h in range(g * w.group, (g + 1) * w.group)}
+        gpu_history(w, lay, d, cache, seqs, history_observers(w, lay, heads), sample, bufs.scores,
+                    bufs.workspace)
     decay_h = np.array([K.kvs_lrfu_decay(0.5, int(x)) for x in lay.dt], np.float32)
     decay = torch.from_numpy(decay_h).to(dev)
     n_prev = torch.from_numpy(lay.n_prev.astype(np.int32)).to(dev)
@@ -265,11 +345,29 @@ def check_config_sampled(w, lay, q_host, sample, out, score_rtol=1e-3):
     from workloads.device import host_stream_inputs
     G = w.group
     worst, pinned_all, bad_all = 0.0, 0, 0
+    if w.history_rounds:
+        heads = {(l, h) for (_, l, g) in sample for h in range(g * w.group, (g + 1) * w.group)}
+        q_hist = history_observers(w, lay, heads)
     for s in sample:
         i, l, g = s
         n, st = int(lay.length[i]), int(lay.start[i])
         B = int(w.budget)
-        k, v, c, qq, lse, bt, stt, ln, oo = host_stream_inputs(w, lay, q_host, [s])
+        mini = host_stream_inputs(w, lay, q_host, [s])
+        k, v, c, qq, lse, bt, stt, ln, oo = mini
+        if w.history_rounds:
+            # the history: the GPU's CRF before the measured round equals the oracle's
+            # replay wherever no history round's cut was within the score tolerance;
+            # the measured round then starts from the GPU's state (teacher forcing)
+            c_hist, unamb, _ = oracle_history(w, lay, q_host, q_hist, s, mini)
+            pos = st + np.arange(n)
+            gpu0 = out["rec"][s]["crf0"][pos // 16, pos % 16]
+            ora0 = c_hist[0, pos // 16, 0, pos % 16]
+            hist_bad = int(np.sum(gpu0[unamb].view(np.uint32) != ora0[unamb].view(np.uint32)))
+            print(f"history {s}: {int(unamb.sum())} of {n} entries unambiguous in every round, "
+                  f"{hist_bad} CRF mismatches", flush=True)
+            assert hist_bad == 0 and unamb.sum() > n // 2, (s, hist_bad)
+            c = c.copy()
+            c[0, pos // 16, 0, pos % 16] = gpu0
         res = O.eviction_round(k.copy(), v.copy(), c.copy(), qq, lse, oo, bt, stt, ln, G, w.scale, 0.5,
                                np.array([lay.dt[i]]), np.array([lay.n_prev[i]]), np.array([B]))
         plan3 = (out["plan"].shift[i], out["plan"].new_start[i], out["plan"].new_len[i])

@@ -43,6 +43,9 @@ class Workload:
     append_per_round: int = 0
     flag_prob: float = 0.0
     budget_cap: int = 30000
+    # untimed score -> LRFU rounds (fresh observers, dt uniform in [dt_lo, dt_hi]) that
+    # build the LRFU history before the measured round
+    history_rounds: int = 0
 
     @property
     def group(self) -> int:
@@ -66,7 +69,7 @@ TINY = Workload(
 LLAMA8B = Workload(
     name="llama3_8b_32k", num_layers=32, num_kv_heads=8, num_q_heads=32, num_seqs=1,
     len_lo=32768, len_hi=32768, obs_lo=64, obs_hi=64, budget=512, planted_frac=0.02,
-    page_placement="random", pool_pages=4096, prior_crf=True, dt_lo=8, dt_hi=64)
+    page_placement="random", pool_pages=4096, prior_crf=True, dt_lo=8, dt_hi=64, history_rounds=4)
 
 RAGGED = Workload(
     name="ragged64", num_layers=32, num_kv_heads=8, num_q_heads=32, num_seqs=64,
@@ -89,7 +92,7 @@ ALL = {w.name: w for w in (TINY, LLAMA8B, RAGGED, RATCHET, LLAMA70B)}
 
 # Philox tensor tags
 TAG_K, TAG_V, TAG_Q, TAG_CRF, TAG_PLANT, TAG_HIST, TAG_LAYOUT, TAG_LEN, TAG_OBS, \
-    TAG_DT, TAG_FLAG, TAG_KMPP = range(1, 13)
+    TAG_DT, TAG_FLAG, TAG_KMPP, TAG_HDT = range(1, 14)
 
 # index strides (element index = ((((seq*L + l)*Hkv + g)*TOKENS + t)*D + d)
 TOKENS_MAX = 1 << 20

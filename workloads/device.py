@@ -30,7 +30,7 @@ class DeviceInputs:
 
 
 def fill(w: Workload, lay: H.Layout, q_host: np.ndarray, device, exact_streams=(),
-         seed_offset: int = 0) -> DeviceInputs:
+         seed_offset: int = 0, exact_bytes=None) -> DeviceInputs:
     import torch
     L, Hkv, Hq, D = w.num_layers, w.num_kv_heads, w.num_q_heads, w.head_dim
     G = w.group
@@ -84,8 +84,78 @@ def fill(w: Workload, lay: H.Layout, q_host: np.ndarray, device, exact_streams=(
                     lse[l, g * G + hh, o0 + oo] = lr[g]
     out = DeviceInputs(k.view(torch.int16), v.view(torch.int16), crf, q.view(torch.int16), lse)
     for (i, l, g) in exact_streams:
-        write_exact_stream(w, lay, q_host, out, i, l, g, device)
+        pre = exact_bytes.get((i, l, g)) if exact_bytes else None
+        write_exact_stream(w, lay, q_host, out, i, l, g, device, pre)
     return out
+
+
+def observer_lse(w: Workload, lay: H.Layout, d: DeviceInputs, q_host: np.ndarray, device,
+                 exact_streams=(), exact_lse=None):
+    """(q, lse) on the device for another observer set (bf16 bits q_host) over the
+    cache's live keys: fp32 logits for every row, then the rows of `exact_streams`
+    recomputed in fp64 on the host from their keys (read back: they are host bytes), or
+    taken from exact_lse[stream] (the same fp64 rows, computed beforehand)."""
+    import torch
+    L, Hkv, Hq, D = w.num_layers, w.num_kv_heads, w.num_q_heads, w.head_dim
+    G = w.group
+    q = _bf16_dev(q_host, device).view(torch.bfloat16)
+    lse = torch.zeros((L, Hq, q.shape[2]), dtype=torch.float32, device=device)
+    kb16 = d.k.view(torch.bfloat16)
+    for i in range(w.num_seqs):
+        n, st = int(lay.length[i]), int(lay.start[i])
+        o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+        O = o1 - o0
+        if n == 0 or O == 0:
+            continue
+        pos = st + np.arange(n)
+        page = torch.from_numpy(lay.block_table[i][pos // PAGE].astype(np.int64)).to(device)
+        row = torch.from_numpy((pos % PAGE).astype(np.int64)).to(device)
+        R = O * G
+        for l in range(L):
+            keys = kb16[l][page, :, row, :].float()
+            qr = q[l, :, o0:o1, :].float().reshape(Hkv, R, D)
+            lr = live_lse(keys, qr, w.scale)
+            rows = torch.arange(R, device=device)
+            for g in range(Hkv):
+                lse[l, g * G + rows // O, o0 + rows % O] = lr[g]
+    for (i, l, g) in exact_streams:
+        if exact_lse is not None and (i, l, g) in exact_lse:
+            lr = exact_lse[(i, l, g)]
+        else:
+            n, st = int(lay.length[i]), int(lay.start[i])
+            pos = st + np.arange(n)
+            page = torch.from_numpy(lay.block_table[i][pos // PAGE].astype(np.int64)).to(device)
+            row = torch.from_numpy((pos % PAGE).astype(np.int64)).to(device)
+            kb = d.k[l][page, g, row, :].cpu().numpy().view(np.uint16)
+            lr = H.lse_rows(H.stream_observer_rows(w, lay, q_host, i, l, g), kb, w.scale)
+        o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+        O = o1 - o0
+        for hh in range(G):
+            lse[l, g * G + hh, o0:o1] = torch.from_numpy(lr[hh * O:(hh + 1) * O].copy()).to(device)
+    return q.view(torch.int16), lse
+
+
+def host_stream_observers(w: Workload, lay: H.Layout, q_host0: np.ndarray, q_host: np.ndarray, streams):
+    """(q, lse) of another observer set for the mini-pools of host_stream_inputs (same
+    stream order and offsets): the LSE over each stream's host keys, fp64 rounded to
+    fp32.  q_host0 is the measured round's observer set (it decides the planted keys)."""
+    G = w.group
+    Os = [int(lay.obs_off[i + 1] - lay.obs_off[i]) for (i, _, _) in streams]
+    obs_off = np.zeros(len(streams) + 1, np.int64)
+    obs_off[1:] = np.cumsum(Os)
+    q = np.zeros((1, G, int(obs_off[-1]), w.head_dim), np.uint16)
+    lse = np.zeros((1, G, int(obs_off[-1])), np.float32)
+    for s, (i, l, g) in enumerate(streams):
+        n = int(lay.length[i])
+        tokens = lay.tok0[i] + np.arange(n)
+        kb = H.stream_keys(w, H.stream_observer_rows(w, lay, q_host0, i, l, g), i, l, g, tokens)
+        lr = H.lse_rows(H.stream_observer_rows(w, lay, q_host, i, l, g), kb, w.scale)
+        o0, o1 = int(lay.obs_off[i]), int(lay.obs_off[i + 1])
+        O = o1 - o0
+        for hh in range(G):
+            q[0, hh, obs_off[s]:obs_off[s + 1]] = q_host[l, g * G + hh, o0:o1]
+            lse[0, hh, obs_off[s]:obs_off[s + 1]] = lr[hh * O:(hh + 1) * O]
+    return q, lse
 
 
 def host_stream(w: Workload, lay: H.Layout, q_host: np.ndarray, i: int, l: int, g: int):
@@ -100,10 +170,23 @@ def host_stream(w: Workload, lay: H.Layout, q_host: np.ndarray, i: int, l: int, 
     return kb, vb, crf, lr
 
 
+def mini_stream_bytes(mini, G: int):
+    """(K rows, V rows, prior CRF, LSE rows) of the single stream of a host_stream_inputs
+    mini-batch, in logical order: the same bytes host_stream returns."""
+    k_pool, v_pool, crf_pool, q, lse, bt, start, length, obs_off = mini
+    n, st = int(length[0]), int(start[0])
+    pos = st + np.arange(n)
+    pg, rw = bt[0][pos // PAGE], pos % PAGE
+    lr = np.concatenate([lse[0, hh, obs_off[0]:obs_off[1]] for hh in range(G)])
+    return k_pool[0, pg, 0, rw], v_pool[0, pg, 0, rw], crf_pool[0, pg, 0, rw], lr
+
+
 def write_exact_stream(w: Workload, lay: H.Layout, q_host: np.ndarray, d: DeviceInputs,
-                       i: int, l: int, g: int, device) -> None:
+                       i: int, l: int, g: int, device, pre=None) -> None:
+    """Overwrite stream (i, l, g) with the host generator's bytes (pre: those bytes,
+    already generated, as mini_stream_bytes returns them)."""
     import torch
-    kb, vb, crf, lr = host_stream(w, lay, q_host, i, l, g)
+    kb, vb, crf, lr = pre if pre is not None else host_stream(w, lay, q_host, i, l, g)
     n = int(lay.length[i])
     st = int(lay.start[i])
     pos = st + np.arange(n)

@@ -13,7 +13,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import philox
-from .configs import (OBS_MAX, TAG_CRF, TAG_DT, TAG_HIST, TAG_K, TAG_KMPP, TAG_LAYOUT,
+from .configs import (OBS_MAX, TAG_CRF, TAG_DT, TAG_HDT, TAG_HIST, TAG_K, TAG_KMPP, TAG_LAYOUT,
                       TAG_LEN, TAG_OBS, TAG_PLANT, TAG_Q, TAG_V, TOKENS_MAX, Workload)
 
 PAGE = 16
@@ -89,6 +89,16 @@ def make_layout(w: Workload) -> Layout:
     return Layout(bt.astype(np.int32), start.astype(np.int32), length.astype(np.int32),
                   obs.astype(np.int32), obs_off, entry_off, int(P), dt.astype(np.int32),
                   n_prev.astype(np.int32), np.zeros(S, np.int64))
+
+
+def history_dt(w: Workload) -> np.ndarray:
+    """int32 [history_rounds][S]: the decode steps between the history rounds that
+    precede the measured round, uniform in [dt_lo, dt_hi].  History round r (1-based)
+    uses the observer set of round index r (observers(..., rnd=r))."""
+    H, S = w.history_rounds, w.num_seqs
+    if H == 0:
+        return np.zeros((0, S), np.int32)
+    return philox.randint(w.key, TAG_HDT, H * S, w.dt_lo, w.dt_hi).reshape(H, S).astype(np.int32)
 
 
 # ---------------------------------------------------------------------------
