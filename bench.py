@@ -131,7 +131,22 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-def load_traffic(workload, name="score_mfma", source="score.hip"):
+def score_kernels(w, lay) -> str:
+    """The kvs_score kernels this workload launches (by the rows R = O G of its sequences)."""
+    G = w.num_q_heads // w.num_kv_heads
+    names = set()
+    for O in lay.obs.tolist():
+        R = O * G
+        if O < 16:
+            names.add("score_valu_kernel")
+        elif R <= 128:
+            names.add("score_mfma_kernel")
+        else:
+            names.add("score_pipe_kernel<4>" if R <= 256 else "score_pipe_kernel<8>")
+    return " + ".join(sorted(names))
+
+
+def load_traffic(workload, name="score", source="score.hip"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
     profiles/<name>_<workload>_traffic.json, if it was taken on the current source of
     that kernel; else None."""
@@ -813,12 +828,12 @@ def main():
     traffic = load_traffic(w.name)
     # the bound by the published peaks: whichever takes longer at its peak
     if score_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > score_bytes / (HBM_PEAK_GBPS * 1e9):
-        roofline = {"kernel": "score_mfma_kernel", "bound": "mfma", "achieved": score_tflops,
+        roofline = {"kernel": score_kernels(w, lay), "bound": "mfma", "achieved": score_tflops,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "traffic": traffic, "ms": score_ms, "ms_median": float(np.median(score_ev)),
                     "flops_per_launch": score_flops, "hbm_gbps": score_gbps}
     else:
-        roofline = {"kernel": "score_mfma_kernel", "bound": "hbm", "achieved": score_gbps,
+        roofline = {"kernel": score_kernels(w, lay), "bound": "hbm", "achieved": score_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
                     "traffic": traffic, "ms": score_ms, "ms_median": float(np.median(score_ev)),
                     "bytes_per_launch": score_bytes, "mfma_tflops": score_tflops}

@@ -6,18 +6,21 @@
 // attention it receives from all observer (action) tokens, here also summed over
 // the query heads of the entry's GQA group.
 //
-// Two kernels share one work decomposition (a work item is a chunk of consecutive
-// 8-page steps of one stream and one group of up to 256 observer rows):
-//   score_mfma_kernel : observers >= 16.  QK^T on v_mfma_f32_32x32x16_bf16 with the
-//       observer rows on M and the keys on N, so each lane ends up holding one key
-//       and 16 rows: the exp and the row sum stay in-lane.  K pages stream from HBM
-//       straight into LDS (global_load_lds_dwordx4, 1 KiB per instruction, XOR-
-//       swizzled 16-byte chunks) through a 4-step ring shared by the 4 waves; with more
-//       than 128 rows the MFMAs of one key tile overlap the exp work of the previous one.
-//   score_valu_kernel : observers < 16.  One key per lane, 64 keys per wave; the
-//       key row is pulled from LDS into registers and every observer row (uniform
-//       across the wave, so it lives in SGPRs) is dotted with v_dot2c_f32_bf16.
-// Both evaluate p = exp2(fma(dot, scale*log2 e, -LSE*log2 e)) and accumulate in fp32.
+// Work items are chunks of consecutive 4-page steps of one stream and one group of its
+// observer rows.  A sequence's rows R = O G decide its path:
+//   score_valu_kernel  (O < 16): one key per lane, 64 keys per wave; the key row is
+//       pulled from LDS into registers and every observer row (uniform across the wave,
+//       so it lives in SGPRs) is dotted with v_dot2c_f32_bf16.  Row groups of 256.
+//   score_mfma_kernel  (O >= 16, R <= 128): QK^T on v_mfma_f32_32x32x16_bf16 with the
+//       observer rows on M and the keys on N, so each lane holds one key and 16 rows and
+//       the exp and the row sum stay in-lane; 32- or 64-row sets, waves split the tiles.
+//   score_pipe_kernel<4> (128 < R <= 256) and score_pipe_kernel<8> (R > 256, row groups
+//       of 512): every wave owns 64 rows, so one workgroup stages each K step in LDS
+//       once for all its rows; the MFMAs of one key tile overlap the exp work of the
+//       previous one.
+// K pages stream from HBM straight into LDS (global_load_lds_dwordx4, 1 KiB per
+// instruction, XOR-swizzled 16-byte chunks) through a ring of 16 KiB steps.
+// All evaluate p = exp2(fma(dot, scale*log2 e, -LSE*log2 e)) and accumulate in fp32.
 #include "kvs_internal.h"
 
 #include <type_traits>
@@ -33,7 +36,8 @@ constexpr int kStepBytes = kStepPages * kPageElems * 2;
 constexpr int kRing = 4;                            // LDS ring depth: 3 steps in flight per workgroup
 constexpr int kTileKeys = 32;                       // one MFMA N tile (2 pages)
 constexpr int kStepTiles = kStepKeys / kTileKeys;   // 2
-constexpr int kRowsPerGroup = 256;                  // observer rows handled by one work item
+constexpr int kRowsPerGroup = 256;                  // observer rows of one item (VALU and small MFMA paths)
+constexpr int kWideRows = 512;                      // observer rows of one item of score_pipe_kernel<8>
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSmallSeqs = 255;                     // item offsets travel in the kernel arguments
 constexpr int kMaxChunkSteps = 128;                 // chunk length limit (block-table slice in LDS)
@@ -54,13 +58,25 @@ struct ScoreArgs {
   int32_t G;
   int32_t chunk_steps;
   int32_t partials;           // 1: write [rg][L][Hkv][E] partial sums
+  int32_t rows_per_group;     // observer rows per work item on this path
   float alpha;                // scale * log2(e)
   int32_t use_small;          // 1: item offsets are in small_off (batches of <= 255 sequences)
   int32_t small_off[kSmallSeqs + 1];
 };
 
+// The scoring path of a sequence with O observers and R = O G rows.
+enum Path : int { kPathValu = 0, kPathMfma = 1, kPathPipe4 = 2, kPathPipe8 = 3, kPaths = 4 };
+__host__ __device__ inline int path_of(int64_t O, int64_t R) {
+  if (O < kMfmaMinObservers) return kPathValu;
+  if (R <= 128) return kPathMfma;
+  return R <= 256 ? kPathPipe4 : kPathPipe8;
+}
+__host__ __device__ inline int32_t rows_per_group(int path) {
+  return path == kPathPipe8 ? kWideRows : kRowsPerGroup;
+}
+
 struct Item {
-  int32_t i, l, g, rg, chunk;
+  int32_t i, l, g, rg, nrg, chunk;
   int32_t start, n, O, npages, nsteps;
   int64_t e0, o0;
 };
@@ -93,12 +109,37 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
   it.nsteps = (it.npages + kStepPages - 1) / kStepPages;
   const int32_t nchunks = (it.nsteps + a.chunk_steps - 1) / a.chunk_steps;
   const int32_t local = rem - off[lo];
-  it.rg = local / nchunks;
-  it.chunk = local - it.rg * nchunks;
+  // the row groups of one chunk are consecutive items, so they run at the same time on
+  // the same XCD and share the chunk's K lines in its L2
+  it.nrg = (it.O * a.G + a.rows_per_group - 1) / a.rows_per_group;
+  it.chunk = local / it.nrg;
+  it.rg = local - it.chunk * it.nrg;
   // host and device item counts agree by construction; refuse anything else
-  const int32_t nrg = (it.O * a.G + kRowsPerGroup - 1) / kRowsPerGroup;
-  if (it.n <= 0 || it.O <= 0 || it.rg >= nrg) return false;
+  if (it.n <= 0 || it.O <= 0 || it.chunk >= nchunks) return false;
   return true;
+}
+
+// The item's fields are the same in every lane; saying so keeps the loop bounds, page
+// indices and branches that derive from them in scalar registers and scalar branches.
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void make_uniform(Item &it) {
+  it.i = __builtin_amdgcn_readfirstlane(it.i);
+  it.l = __builtin_amdgcn_readfirstlane(it.l);
+  it.g = __builtin_amdgcn_readfirstlane(it.g);
+  it.rg = __builtin_amdgcn_readfirstlane(it.rg);
+  it.nrg = __builtin_amdgcn_readfirstlane(it.nrg);
+  it.chunk = __builtin_amdgcn_readfirstlane(it.chunk);
+  it.start = __builtin_amdgcn_readfirstlane(it.start);
+  it.n = __builtin_amdgcn_readfirstlane(it.n);
+  it.O = __builtin_amdgcn_readfirstlane(it.O);
+  it.npages = __builtin_amdgcn_readfirstlane(it.npages);
+  it.nsteps = __builtin_amdgcn_readfirstlane(it.nsteps);
+  it.e0 = uni64(it.e0);
+  it.o0 = uni64(it.o0);
 }
 
 // One LDS DMA instruction: lane t's 16 bytes from src land at LDS byte address
@@ -108,19 +149,32 @@ __device__ __forceinline__ bool decode_item(const ScoreArgs &a, Item &it) {
 // whole prefetch ring at every step.  Ordering is explicit instead: a slot is read
 // only after the ring barrier's vmcnt wait and s_barrier, and refilled only after
 // the barrier that follows the last read of it.  No output registers; the address
-// registers are consumed at issue.  M0 is saved and restored around the DMA.  The K
-// rows are read once per call, so the load is marked non-temporal (streaming).
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+// registers are consumed at issue.  M0 is saved and restored around the DMA.  When a
+// stream's rows form one row group its K rows are read once per call, so the load is
+// marked non-temporal (streaming); with several row groups the other groups' workgroups
+// read the same lines, so they stay cacheable.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds, bool stream) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
+  if (stream)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds)
+        : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -145,7 +199,7 @@ __device__ __forceinline__ int issue_step(const ScoreArgs &a, const Item &it, in
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * r + row_in_instr;
     const uint16_t *src = page + row * kHeadDim + ((chunk ^ row) << 3);
-    lds_dma16(src, dst0 + r * 1024);
+    lds_dma16(src, dst0 + r * 1024, it.nrg == 1);
   }
   return 4;
 }
@@ -156,7 +210,11 @@ __device__ __forceinline__ int issue_step(const ScoreArgs &a, const Item &it, in
 // vector memory operation, i.e. the whole prefetch ring, at each step.)  Vector
 // loads complete in issue order; stores in between only make the wait longer.
 __device__ __forceinline__ void ring_barrier(int later) {
-  if (later >= 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  if (later >= 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
+  else if (later >= 20) asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
+  else if (later >= 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+  else if (later >= 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+  else if (later >= 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
   else if (later >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -329,6 +387,33 @@ __device__ __forceinline__ float exp_rows2(const floatx16 &x0, const floatx16 &x
   return (s0 + s1) + (s2 + s3);
 }
 
+// One LDS DMA instruction with a wave-uniform page base (SGPRs) and a per-lane byte
+// offset: lane t's 16 bytes from base + voff land at LDS byte address lds + 16 t.
+// Same ordering contract as lds_dma16.
+__device__ __forceinline__ void lds_dma16_s(const uint16_t *base, uint32_t voff, uint32_t lds, bool stream) {
+  uint32_t saved;
+  if (stream)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:0 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
+
 // One pipeline phase: the QK^T MFMAs of the next key tile (LDS bytes tile_base + rd[s]
 // for k-step s) overlapped with the exp/sum of the previous tile's accumulators.  The
 // scheduling barriers fix the issue order: the 8 LDS reads first, then one MFMA per
@@ -359,38 +444,73 @@ __device__ __forceinline__ float pipe_phase(const uint8_t *tile_base, const uint
   return v;
 }
 
-// Main loop for row groups of more than 128 rows: every active wave owns 64 rows (two
-// M tiles; rows past the end have zero Q and LSE +inf, so they add exactly 0) and
-// takes both key tiles of every step.  Tile j's MFMAs overlap tile j-1's exp work:
-//   phase A of step k:  MFMA(k, tile 1)    || exp(k, tile 0)
-//   phase B of step k:  ring barrier(k+1), refill, combine;
-//                       MFMA(k+1, tile 0)  || exp(k, tile 1)
-// The loop is unrolled over the 4 ring slots, so that every LDS address of a step is a
-// per-lane register plus an immediate.  Each wave writes its per-lane partial sums
-// (both lane halves) to part[k % 4]; wave 0 combines tile 0 and wave 1 tile 1 of a
-// step once a barrier has passed after every wave wrote them (a wave can be at most
-// one barrier ahead of the combining wave, so a buffer is never rewritten early).
-__device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item &it,
-                                                 uint8_t (*ring)[kStepBytes],
-                                                 float (*part)[kStepTiles][kWaves][64],
-                                                 const int32_t *bt_lds, int32_t page0, int wave, int lane,
-                                                 int wpr, int wrow, bool active, const bf16x8 (*qa)[8],
-                                                 const float (*nl)[16]) {
+// ---- The pipelined scorer for more than 128 rows ----
+//
+// W waves per workgroup, each owning 64 observer rows (two 32-row M tiles), so one
+// workgroup covers a row group of up to 64 W rows and stages each K step in LDS once
+// for all of them.  A step is 4 pages (64 keys, two 32-key tiles); waves 0..3 each DMA
+// one page of it.  Tile u's MFMAs overlap tile u-1's exp work:
+//   phase A of step j:  MFMA(j, tile 1)    || exp(j, tile 0)
+//   phase B of step j:  ring barrier(j+1), refill, combine;
+//                       MFMA(j+1, tile 0)  || exp(j, tile 1)
+// The loop is unrolled over the ring slots, so every LDS read is a per-lane register
+// plus an immediate and every DMA a scalar page base plus a per-lane offset computed
+// once; control flow in the loop is uniform across the workgroup.  Waves without rows
+// (a row group of fewer than 64 W rows) run the same barriers, loads and combines
+// without the arithmetic.  Each wave writes its per-lane partial sums (both lane
+// halves) to part[step % 2]; after barrier j+1, wave 0 sums tile 0 of step j and
+// wave 1 tile 1 of step j-1 in wave order (deterministic), and stores the 32 keys.
+// A wave is at most one barrier ahead of another, so two partial buffers suffice.
+template <int W>
+struct PipeShape {
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kSlots = W == 8 ? 8 : 4;       // ring depth: kSlots - 1 steps in flight
+  static constexpr int kWgPerCu = W == 8 ? 1 : 2;
+};
+
+template <int W, bool COMPUTE>
+__device__ __forceinline__ void pipe_loop(const ScoreArgs &a, const Item &it, uint8_t (*ring)[kStepBytes],
+                                          float (*part)[kStepTiles][W][64], const int32_t *bt_lds, int32_t page0,
+                                          int wave, int lane, int nact, const bf16x8 (*qa)[8],
+                                          const float (*nl)[16]) {
+  constexpr int S = PipeShape<W>::kSlots;
   const int half = lane >> 5;
   const int col = lane & 31;
+  const bool stream = it.nrg == 1;
+  const bool dma = wave < kStepPages;
   const int32_t s_begin = it.chunk * a.chunk_steps;
   const int32_t s_end = min(s_begin + a.chunk_steps, it.nsteps);
   const int32_t ntiles = (it.start + it.n + kTileKeys - 1) / kTileKeys;
-  auto nloads = [&](int32_t j) -> int { return (j < s_end && j * kStepPages + wave < it.npages) ? 4 : 0; };
-  // sum the wpr partials of (step, tt) and store the 32 keys
+  // this wave's page of step j is logical page 4j + wave
+  auto nloads = [&](int32_t j) -> int {
+    return (dma && j < s_end && j * kStepPages + wave < it.npages) ? 4 : 0;
+  };
+  // per-lane source offsets of the 4 DMA instructions of a page (bytes): lane t of
+  // instruction r fills LDS chunk t%16 of row 4r + t/16 with global chunk (t%16) ^ row
+  uint32_t voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * r + (lane >> 4);
+    voff[r] = (uint32_t)(row * kHeadDim * 2 + (((lane & 15) ^ row) << 4));
+  }
+  const int64_t head_base = ((int64_t)it.l * a.b.num_pages) * a.b.Hkv + it.g;
+  auto issue = [&](int32_t j, uint8_t *buf) {
+    const int lp = j * kStepPages + wave;
+    if (!dma || j >= s_end || lp >= it.npages) return;
+    const int64_t phys = __builtin_amdgcn_readfirstlane(bt_lds[lp - page0]);
+    const uint16_t *page = a.k + (head_base + phys * a.b.Hkv) * kPageElems;
+    const uint32_t dst0 = __builtin_amdgcn_readfirstlane(lds_addr(buf + wave * (kPageElems * 2)));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lds_dma16_s(page, voff[r], dst0 + r * 1024, stream);
+  };
   auto combine = [&](int32_t step, int tt) {
     // the buffer offset goes through an empty asm so that the compiler computes it here
-    // instead of keeping one address per (slot, tile) live across the loop
-    int off = (((step - s_begin) & (kRing - 1)) * kStepTiles + tt) * (kWaves * 64) + lane;
+    // instead of keeping one address per (buffer, tile) live across the loop
+    int off = ((((step - s_begin) & 1) * kStepTiles + tt) * W) * 64 + lane;
     asm volatile("" : "+v"(off));
     const float *pp = &part[0][0][0][0] + off;
     float v = 0.f;
-    for (int w = 0; w < wpr; ++w) v += pp[w * 64] + pp[w * 64 + 32];
+    for (int w = 0; w < nact; ++w) v += pp[w * 64] + pp[w * 64 + 32];
     const int32_t tile = step * kStepTiles + tt;
     if (tile < ntiles) store_key(a, it, tile, lane, v);
   };
@@ -400,15 +520,18 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
   for (int s = 0; s < 8; ++s) rd[s] = (uint32_t)(col * (kHeadDim * 2) + (((2 * s + half) ^ (col & 15)) << 4));
 
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u)
-    if (s_begin + u < s_end) issue_step(a, it, s_begin + u, ring[u], bt_lds, page0, wave, lane);
-  ring_barrier(nloads(s_begin + 1) + nloads(s_begin + 2));
-  if (s_begin + kRing - 1 < s_end)
-    issue_step(a, it, s_begin + kRing - 1, ring[kRing - 1], bt_lds, page0, wave, lane);
+  for (int u = 0; u < S - 1; ++u) issue(s_begin + u, ring[u]);
+  {
+    int later = 0;
+#pragma unroll
+    for (int u = 1; u < S - 1; ++u) later += nloads(s_begin + u);
+    ring_barrier(later);
+  }
+  issue(s_begin + S - 1, ring[S - 1]);
 
   constexpr int kTileBytes = kTileKeys * kHeadDim * 2;
   floatx16 t0a = {}, t0b = {}, t1a = {}, t1b = {};
-  if (active) {
+  if (COMPUTE) {
     bf16x8 kb[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kb[s] = *(const bf16x8 *)(ring[0] + rd[s]);
@@ -418,28 +541,29 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
       t0b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], t0b, 0, 0, 0);
     }
   }
-  // one step with its ring slot (== its part buffer) fixed at compile time
+  // one step with its ring slot fixed at compile time
   auto do_step = [&](auto slot_c, int32_t step) __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_c)::value;
-    constexpr int NEXT = (SLOT + 1) & (kRing - 1);
-    float *mine = &part[SLOT][0][wrow][0];
-    // phase A
-    if (active) mine[lane] = pipe_phase(ring[SLOT] + kTileBytes, rd, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
-    // phase B
+    constexpr int NEXT = (SLOT + 1) % S;
+    float *mine = &part[(SLOT & 1)][0][wave][0];
+    if (COMPUTE) mine[lane] = pipe_phase(ring[SLOT] + kTileBytes, rd, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
     if (step + 1 < s_end) {
-      ring_barrier(nloads(step + 2) + nloads(step + 3));
-      if (step + kRing < s_end) issue_step(a, it, step + kRing, ring[SLOT], bt_lds, page0, wave, lane);
+      int later = 0;
+#pragma unroll
+      for (int u = 2; u < S; ++u) later += nloads(step + u);
+      ring_barrier(later);
+      issue(step + S, ring[SLOT]);
       if (lane < 32) {
         if (wave == 0) combine(step, 0);
         else if (wave == 1 && step > s_begin) combine(step - 1, 1);
       }
-      if (active)
-        mine[kWaves * 64 + lane] = pipe_phase(ring[NEXT], rd, qa, t0a, t0b, t1a, t1b, a.alpha, nl);
-    } else if (active) {
-      mine[kWaves * 64 + lane] = exp_rows2(t1a, t1b, a.alpha, nl);
+      if (COMPUTE)
+        mine[W * 64 + lane] = pipe_phase(ring[NEXT], rd, qa, t0a, t0b, t1a, t1b, a.alpha, nl);
+    } else if (COMPUTE) {
+      mine[W * 64 + lane] = exp_rows2(t1a, t1b, a.alpha, nl);
     }
   };
-  for (int32_t step = s_begin; step < s_end; step += kRing) {
+  for (int32_t step = s_begin; step < s_end; step += S) {
     do_step(std::integral_constant<int, 0>{}, step);
     if (step + 1 >= s_end) break;
     do_step(std::integral_constant<int, 1>{}, step + 1);
@@ -447,6 +571,16 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
     do_step(std::integral_constant<int, 2>{}, step + 2);
     if (step + 3 >= s_end) break;
     do_step(std::integral_constant<int, 3>{}, step + 3);
+    if constexpr (S == 8) {
+      if (step + 4 >= s_end) break;
+      do_step(std::integral_constant<int, 4>{}, step + 4);
+      if (step + 5 >= s_end) break;
+      do_step(std::integral_constant<int, 5>{}, step + 5);
+      if (step + 6 >= s_end) break;
+      do_step(std::integral_constant<int, 6>{}, step + 6);
+      if (step + 7 >= s_end) break;
+      do_step(std::integral_constant<int, 7>{}, step + 7);
+    }
   }
   __syncthreads();
   if (lane < 32) {
@@ -457,29 +591,99 @@ __device__ __forceinline__ void score_steps_pipe(const ScoreArgs &a, const Item 
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
-  __shared__ float part[kRing][kStepTiles][kWaves][64];
+template <int W>
+__global__ __launch_bounds__(PipeShape<W>::kThreads, PipeShape<W>::kWgPerCu) void score_pipe_kernel(ScoreArgs a) {
+  constexpr int S = PipeShape<W>::kSlots;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S][kStepBytes];
+  __shared__ float part[2][kStepTiles][W][64];
   __shared__ int32_t bt_lds[kMaxChunkSteps * kStepPages];
 
   Item it;
   if (!decode_item(a, it)) return;
-  const int wave = threadIdx.x >> 6;
+  make_uniform(it);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int32_t R = it.O * a.G;
+  const int32_t r0 = it.rg * a.rows_per_group;
+  const int32_t rows_here = min(a.rows_per_group, R - r0);
+  const int nact = (rows_here + 63) / 64;                 // waves with rows
+  const bool active = wave < nact;
+  const int32_t wr0 = r0 + wave * 64;
+
+  // Observer rows of this wave as MFMA A operands: lane (m, h) holds row m,
+  // dims 16s + 8h .. +8 for k-step s.  Loads are unconditional (invalid rows read
+  // row 0 of the stream and are zeroed) so that they all issue back to back.
+  bf16x8 qa[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int32_t r = wr0 + 32 * t + col;
+    const bool ok = active && r < R;
+    const int32_t rc = ok ? r : 0;
+    const int32_t h = it.g * a.G + rc / it.O;
+    const int32_t o = rc - (rc / it.O) * it.O;
+    const uint16_t *qp = a.q + (((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o) * kHeadDim + 8 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 v = *(const bf16x8 *)(qp + 16 * s);
+      const bf16x8 z = {};
+      qa[t][s] = ok ? v : z;
+    }
+  }
+  // LSE of the wave's rows, one per lane, then spread to the accumulator layout:
+  // register k of M tile t holds row 32t + 8(k/4) + 4h + k%4.  Rows past the end have
+  // zero Q and LSE +inf, so they add exactly 0.
+  float my_nl;
+  {
+    const int32_t r = wr0 + lane;
+    const bool ok = active && r < R && r < r0 + rows_here;
+    const int32_t rc = ok ? r : 0;
+    const int32_t h = it.g * a.G + rc / it.O;
+    const int32_t o = rc - (rc / it.O) * it.O;
+    const float v = a.lse[((int64_t)it.l * a.Hq + h) * a.obs_total + it.o0 + o] * kLog2e;
+    my_nl = ok ? -v : -__builtin_inff();
+  }
+  const int32_t s_begin = it.chunk * a.chunk_steps;
+  const int32_t page0 = s_begin * kStepPages;
+  const int32_t page1 = min(it.npages, (s_begin + a.chunk_steps) * kStepPages);
+  const int32_t *bt_row = a.b.bt + (int64_t)it.i * a.b.max_pages;
+  for (int32_t p = page0 + (int32_t)threadIdx.x; p < page1; p += PipeShape<W>::kThreads) bt_lds[p - page0] = bt_row[p];
+  float nl[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) nl[t][k] = __shfl(my_nl, 32 * t + 8 * (k >> 2) + 4 * half + (k & 3));
+  __syncthreads();
+  if (active)
+    pipe_loop<W, true>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
+  else
+    pipe_loop<W, false>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes];
+  __shared__ float part[kRing][kStepTiles][kWaves][kTileKeys];
+  __shared__ int32_t bt_lds[kMaxChunkSteps * kStepPages];
+
+  Item it;
+  if (!decode_item(a, it)) return;
+  make_uniform(it);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // Row sets: more than 128 rows -> 64-row sets (2 M tiles per wave), 3-4 waves per
-  // set, each wave takes both tiles of a step; 65..128 rows -> two 64-row sets, one
-  // tile each; up to 64 rows -> 32-row sets (1 M tile), one tile each.
+  // Row sets (at most 128 rows here): 65..128 rows -> two 64-row sets (2 M tiles per
+  // wave); up to 64 rows -> 32-row sets (1 M tile).  Two waves per set; the waves of
+  // tile phase p (waves 2p, 2p + 1) take tile p of every step.
   const int32_t R = it.O * a.G;
   const int32_t r0 = it.rg * kRowsPerGroup;
   const int32_t rows_here = min(kRowsPerGroup, R - r0);
   const int rw = rows_here > 64 ? 64 : 32;                              // rows per wave
   const int wpr = (rows_here + rw - 1) / rw;                            // waves per row set
-  const int nph = wpr > 2 ? 1 : 2;                                      // tile phases
-  const int phase = wave / (nph == 1 ? 4 : 2);
-  const int wrow = nph == 1 ? wave : (wave & 1);
+  const int phase = wave / 2;
+  const int wrow = wave & 1;
   const bool active = wrow < wpr;
   const int32_t wr0 = r0 + wrow * rw;
   const bool on0 = active && wr0 < R;
@@ -529,11 +733,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
     for (int k = 0; k < 16; ++k) nl[t][k] = __shfl(my_nl, 32 * t + 8 * (k >> 2) + 4 * half + (k & 3));
   __syncthreads();
 
-  if (nph == 1)
-    score_steps_pipe(a, it, ring, part, bt_lds, page0, wave, lane, wpr, wrow, active, qa, nl);
-  else
-    score_steps<2>(a, it, ring, (float (*)[kStepTiles][kWaves][kTileKeys])part, bt_lds, page0, wave, lane,
-                   wpr, phase, wrow, active, on0, on1, qa, nl);
+  score_steps<2>(a, it, ring, part, bt_lds, page0, wave, lane, wpr, phase, wrow, active, on0, on1, qa, nl);
 }
 
 // VALU path: each wave owns whole 64-key quads (4 pages) of the chunk -- quad q goes
@@ -554,7 +754,7 @@ __device__ __forceinline__ void issue_quad(const ScoreArgs &a, const Item &it, i
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * r + (lane >> 4);
         const uint16_t *src = page + row * kHeadDim + (((lane & 15) ^ row) << 3);
-        lds_dma16(src, dst0 + r * 1024);
+        lds_dma16(src, dst0 + r * 1024, it.nrg == 1);
       }
     }
   }
@@ -565,7 +765,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_valu_kernel(ScoreArgs a) {
 
   Item it;
   if (!decode_item(a, it)) return;
-  const int wave = threadIdx.x >> 6;
+  make_uniform(it);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
   const int lane = threadIdx.x & 63;
   const int32_t R = it.O * a.G;
   const int32_t r0 = it.rg * kRowsPerGroup;
@@ -639,65 +840,79 @@ __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ out, int6
   if (idx < n) out[idx] = 0.f;
 }
 
-// Per-sequence work-item prefix for both paths: item_off_mfma, item_off_valu [S+1].
+// Per-sequence work-item prefix of every path: item_off[path][S+1].
 __global__ __launch_bounds__(256) void score_items_kernel(const int32_t *__restrict__ start,
                                                           const int32_t *__restrict__ len,
                                                           const int64_t *__restrict__ obs_off,
                                                           int32_t S, int32_t G, int32_t chunk_steps,
-                                                          int32_t *__restrict__ off_mfma,
-                                                          int32_t *__restrict__ off_valu) {
-  __shared__ int32_t carry[2];
-  __shared__ int32_t wsum[2][4];
+                                                          int32_t *__restrict__ item_off) {
+  __shared__ int32_t carry[kPaths];
+  __shared__ int32_t wsum[kPaths][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; }
+  if (threadIdx.x < kPaths) carry[threadIdx.x] = 0;
   __syncthreads();
   for (int32_t base = 0; base < S; base += 256) {
     const int32_t i = base + threadIdx.x;
-    int32_t cm = 0, cv = 0;
+    int32_t c[kPaths] = {0, 0, 0, 0};
     if (i < S) {
       const int32_t npages = (start[i] + len[i] + kPage - 1) / kPage;
       const int32_t nsteps = (npages + kStepPages - 1) / kStepPages;
       const int32_t nch = (nsteps + chunk_steps - 1) / chunk_steps;
       const int32_t O = (int32_t)(obs_off[i + 1] - obs_off[i]);
       const int32_t R = O * G;
-      const int32_t nrg = (R + kRowsPerGroup - 1) / kRowsPerGroup;
-      const int32_t items = (len[i] > 0 && O > 0) ? nch * nrg : 0;
-      if (O >= kMfmaMinObservers) cm = items; else cv = items;
+      const int path = path_of(O, R);
+      const int32_t rpg = rows_per_group(path);
+      const int32_t nrg = (R + rpg - 1) / rpg;
+      c[path] = (len[i] > 0 && O > 0) ? nch * nrg : 0;
     }
     // inclusive wave scans
-    int32_t xm = cm, xv = cv;
+    int32_t x[kPaths];
+#pragma unroll
+    for (int q = 0; q < kPaths; ++q) x[q] = c[q];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int32_t ym = __shfl_up(xm, d), yv = __shfl_up(xv, d);
-      if (lane >= d) { xm += ym; xv += yv; }
+#pragma unroll
+      for (int q = 0; q < kPaths; ++q) {
+        const int32_t y = __shfl_up(x[q], d);
+        if (lane >= d) x[q] += y;
+      }
     }
-    if (lane == 63) { wsum[0][wave] = xm; wsum[1][wave] = xv; }
+    if (lane == 63)
+#pragma unroll
+      for (int q = 0; q < kPaths; ++q) wsum[q][wave] = x[q];
     __syncthreads();
-    int32_t pm = carry[0], pv = carry[1];
-    for (int w = 0; w < wave; ++w) { pm += wsum[0][w]; pv += wsum[1][w]; }
-    if (i < S) { off_mfma[i] = pm + xm - cm; off_valu[i] = pv + xv - cv; }
+#pragma unroll
+    for (int q = 0; q < kPaths; ++q) {
+      int32_t pre = carry[q];
+      for (int w = 0; w < wave; ++w) pre += wsum[q][w];
+      if (i < S) item_off[q * (S + 1) + i] = pre + x[q] - c[q];
+      x[q] += pre;
+    }
     __syncthreads();
-    if (threadIdx.x == 255) { carry[0] = pm + xm; carry[1] = pv + xv; }
+    if (threadIdx.x == 255)
+#pragma unroll
+      for (int q = 0; q < kPaths; ++q) carry[q] = x[q];
     __syncthreads();
   }
-  if (threadIdx.x == 0) { off_mfma[S] = carry[0]; off_valu[S] = carry[1]; }
+  if (threadIdx.x < kPaths) item_off[threadIdx.x * (S + 1) + S] = carry[threadIdx.x];
 }
 
 struct Plan {
   int32_t chunk_steps;
-  int64_t items_mfma, items_valu;   // per (layer, head)
+  int64_t items[kPaths];   // per (layer, head)
   int32_t max_rg;
   bool any_partial;
   bool need_zero;
 };
 
-// Work items of sequence i on one path: (row groups) x (chunks of chunk_steps steps).
+// Work items of sequence i on its path: (chunks of chunk_steps steps) x (row groups).
 inline int64_t seq_items(int32_t start, int32_t len, int64_t O, int32_t G, int32_t chunk_steps) {
   if (len <= 0 || O <= 0) return 0;
   const int32_t npages = (start + len + kPage - 1) / kPage;
   const int32_t nsteps = (npages + kStepPages - 1) / kStepPages;
   const int32_t nch = (nsteps + chunk_steps - 1) / chunk_steps;
-  const int32_t nrg = (int32_t)((O * G + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int32_t rpg = rows_per_group(path_of(O, O * G));
+  const int32_t nrg = (int32_t)((O * G + rpg - 1) / rpg);
   return (int64_t)nch * nrg;
 }
 
@@ -711,31 +926,40 @@ Plan make_plan(const Batch &b, int32_t G, const int64_t *obs_off_h, const int32_
     if (len_h[i] <= 0 || O <= 0) continue;
     const int32_t npages = (start_h[i] + len_h[i] + kPage - 1) / kPage;
     const int32_t nsteps = (npages + kStepPages - 1) / kStepPages;
-    const int32_t nrg = (int32_t)((O * G + kRowsPerGroup - 1) / kRowsPerGroup);
-    total_steps += (int64_t)nsteps * nrg;
+    const int32_t rpg = rows_per_group(path_of(O, O * G));
+    const int32_t nrg = (int32_t)((O * G + rpg - 1) / rpg);
+    // a 512-row item holds a workgroup of 8 waves, twice the 4-wave items
+    total_steps += (int64_t)nsteps * nrg * (rpg == kWideRows ? 2 : 1);
     p.max_rg = nrg > p.max_rg ? nrg : p.max_rg;
   }
   p.need_zero = false;
   for (int i = 0; i < b.S; ++i) {
     const int64_t O = obs_off_h[i + 1] - obs_off_h[i];
     if (len_h[i] <= 0) continue;
-    const int32_t nrg = (int32_t)((O * G + kRowsPerGroup - 1) / kRowsPerGroup);
+    int32_t nrg = 0;
+    if (O > 0) {
+      const int32_t rpg = rows_per_group(path_of(O, O * G));
+      nrg = (int32_t)((O * G + rpg - 1) / rpg);
+    }
     if (O <= 0 || nrg < p.max_rg) p.need_zero = true;
   }
   total_steps *= (int64_t)b.L * b.Hkv;
-  // aim for ~4 work items per resident workgroup slot (256 CUs x 2)
+  // aim for ~4 work items per resident 4-wave workgroup slot (256 CUs x 2)
   int64_t cs = total_steps / (256 * 2 * 4);
   if (cs < 4) cs = 4;
   if (cs > kMaxChunkSteps) cs = kMaxChunkSteps;
   p.chunk_steps = (int32_t)cs;
-  p.items_mfma = p.items_valu = 0;
+  for (int q = 0; q < kPaths; ++q) p.items[q] = 0;
   for (int i = 0; i < b.S; ++i) {
     const int64_t O = obs_off_h[i + 1] - obs_off_h[i];
-    const int64_t it = seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
-    if (O >= kMfmaMinObservers) p.items_mfma += it; else p.items_valu += it;
+    p.items[path_of(O, O * G)] += seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
   }
   p.any_partial = p.max_rg > 1;
   return p;
+}
+
+inline size_t table_bytes(int32_t S) {
+  return ((kPaths * ((size_t)S + 1) * sizeof(int32_t)) + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -745,7 +969,7 @@ size_t score_workspace_bytes(const Batch &b, int32_t Hq, const int64_t *obs_off_
   const int32_t G = Hq / b.Hkv;
   const Plan p = make_plan(b, G, obs_off_h, len_h, start_h);
   size_t bytes = 0;
-  if (b.S > kSmallSeqs) bytes = ((2 * ((size_t)b.S + 1) * sizeof(int32_t)) + 255) & ~(size_t)255;
+  if (b.S > kSmallSeqs) bytes = table_bytes(b.S);
   if (p.any_partial) bytes += (size_t)p.max_rg * b.L * b.Hkv * b.E * sizeof(float);
   return bytes;
 }
@@ -758,12 +982,11 @@ hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers 
   const Plan p = make_plan(b, G, obs_off_h, len_h, start_h);
   const int64_t LHE = (int64_t)b.L * b.Hkv * b.E;
   const bool small = b.S <= kSmallSeqs;
-  int32_t *off_m = nullptr, *off_v = nullptr;
+  int32_t *table = nullptr;
   size_t head = 0;
   if (!small) {
-    off_m = (int32_t *)ws;
-    off_v = off_m + (b.S + 1);
-    head = ((2 * ((size_t)b.S + 1) * sizeof(int32_t)) + 255) & ~(size_t)255;
+    table = (int32_t *)ws;
+    head = table_bytes(b.S);
   }
   float *partial = p.any_partial ? (float *)((uint8_t *)ws + head) : nullptr;
 
@@ -775,9 +998,10 @@ hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers 
     const int64_t nz = p.any_partial ? LHE * p.max_rg : LHE;
     zero_kernel<<<(unsigned)((nz + 255) / 256), 256, 0, st>>>(z, nz);
   }
-  if (p.items_mfma + p.items_valu == 0) return hipGetLastError();
-  if (!small)
-    score_items_kernel<<<1, 256, 0, st>>>(b.start, b.len, o.obs_off, b.S, G, p.chunk_steps, off_m, off_v);
+  int64_t all_items = 0;
+  for (int q = 0; q < kPaths; ++q) all_items += p.items[q];
+  if (all_items == 0) return hipGetLastError();
+  if (!small) score_items_kernel<<<1, 256, 0, st>>>(b.start, b.len, o.obs_off, b.S, G, p.chunk_steps, table);
 
   ScoreArgs a{};
   a.k = (const uint16_t *)c.k;
@@ -794,28 +1018,34 @@ hipError_t launch_score(const kvs_cache &c, const Batch &b, const kvs_observers 
   a.alpha = scale * kLog2e;
   a.use_small = small ? 1 : 0;
   const int64_t LH = (int64_t)b.L * b.Hkv;
-  for (int path = 0; path < 2; ++path) {
-    const int64_t items = path == 0 ? p.items_mfma : p.items_valu;
+  // the widest items first, so that the long workgroups start early
+  const int order[kPaths] = {kPathPipe8, kPathPipe4, kPathMfma, kPathValu};
+  for (int oi = 0; oi < kPaths; ++oi) {
+    const int path = order[oi];
+    const int64_t items = p.items[path];
     if (items == 0) continue;
     if (small) {
       int32_t acc = 0;
       for (int i = 0; i < b.S; ++i) {
         a.small_off[i] = acc;
         const int64_t O = obs_off_h[i + 1] - obs_off_h[i];
-        const bool mine = (O >= kMfmaMinObservers) == (path == 0);
-        if (mine) acc += (int32_t)seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
+        if (path_of(O, O * G) == path) acc += (int32_t)seq_items(start_h[i], len_h[i], O, G, p.chunk_steps);
       }
       a.small_off[b.S] = acc;
     } else {
-      a.item_off = path == 0 ? off_m : off_v;
+      a.item_off = table + (size_t)path * (b.S + 1);
     }
+    a.rows_per_group = rows_per_group(path);
     a.items_per_lg = (int32_t)items;
     a.total_items = items * LH;
     a.padded_items = (a.total_items + 7) & ~(int64_t)7;
-    if (path == 0)
-      score_mfma_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
-    else
-      score_valu_kernel<<<(unsigned)a.padded_items, kThreads, 0, st>>>(a);
+    const unsigned grid = (unsigned)a.padded_items;
+    switch (path) {
+      case kPathPipe8: score_pipe_kernel<8><<<grid, PipeShape<8>::kThreads, 0, st>>>(a); break;
+      case kPathPipe4: score_pipe_kernel<4><<<grid, PipeShape<4>::kThreads, 0, st>>>(a); break;
+      case kPathMfma: score_mfma_kernel<<<grid, kThreads, 0, st>>>(a); break;
+      default: score_valu_kernel<<<grid, kThreads, 0, st>>>(a); break;
+    }
   }
   if (p.any_partial) {
     score_combine_kernel<<<(unsigned)((LHE + 255) / 256), 256, 0, st>>>(partial, scores, LHE, p.max_rg);

@@ -89,6 +89,17 @@ def _counter(directory: str, counter: str) -> dict[str, list[float]]:
     return per
 
 
+def _calibration_copies(directory: str, counter: str, n: int = 3) -> list[float]:
+    """The counter values of the last n copy-kernel dispatches of the run: bench.py's
+    --calibration-copy runs its copies after everything else."""
+    rows = []
+    for r in _rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") == counter and "copy" in r["Kernel_Name"].lower():
+            rows.append((int(r.get("Dispatch_Id", 0) or 0), float(r["Counter_Value"])))
+    rows.sort()
+    return [v for _, v in rows[-n:]]
+
+
 def traffic(args) -> None:
     kernel = args.kernel
     copy_bytes = args.copy_mib * 2**20
@@ -97,16 +108,20 @@ def traffic(args) -> None:
     factors = {}
     for counter, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
         per = _counter(d, counter)
-        # the calibration copy: the copy dispatches with the largest counter value
-        copies = [v for k, vs in per.items() if "copy" in k.lower() for v in vs]
+        # the calibration copy: the last copy dispatches of the run (other copies, such as
+        # the per-step pool copies, come before it and have other sizes)
+        copies = _calibration_copies(d, counter)
         if not copies:
             sys.exit(f"no copy kernel in the {counter} run")
         c_kib = max(copies)
         factor = copy_bytes / (c_kib * 1024.0)
-        sc = [v for k, vs in per.items() if kernel in k for v in vs]
-        if not sc:
+        # every kernel whose name holds one of the comma-separated substrings: the
+        # per-dispatch average of each, summed (one launch of each per call)
+        names = [k for k in per if any(x in k for x in kernel.split(","))]
+        if not names:
             sys.exit(f"no {kernel} dispatch in the {counter} run")
-        s_kib = sum(sc) / len(sc)
+        s_kib = sum(sum(per[k]) / len(per[k]) for k in names)
+        sc = [v for k in names for v in per[k]]
         key = counter.lower()
         out[f"{key}_kib_per_dispatch"] = s_kib
         out[f"copy_{key}_kib"] = c_kib

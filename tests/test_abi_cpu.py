@@ -80,9 +80,9 @@ def test_score_validation():
     assert call(cache=_cache(k=0)) == "KVS_ERR_NULL"
     assert call(scores=None) == "KVS_ERR_NULL"
     assert call(scale=float("nan")) == "KVS_ERR_SHAPE"
-    # 65 observers x GQA 4 = 260 rows > 256: partial sums need workspace
-    obs65, _ = _obs(1, Hq=4, O_=65)
-    assert call(o=obs65, wsb=8) == "KVS_ERR_WORKSPACE"
+    # 129 observers x GQA 4 = 516 rows > 512: two row groups, whose partial sums need workspace
+    obs129, _ = _obs(1, Hq=4, O_=129)
+    assert call(o=obs129, wsb=8) == "KVS_ERR_WORKSPACE"
     obs_bad, _ = _obs(1, Hq=6)   # not a multiple of Hkv = 4? (Hkv = 1 here, use Hkv=4 cache)
     assert call(cache=_cache(Hkv=4), o=obs_bad) == "KVS_ERR_SHAPE"
     bad = HostSeqs([[0, 1, 9]], [0], [40])          # page 9 outside an 8-page pool

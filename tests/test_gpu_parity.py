@@ -74,6 +74,16 @@ EDGE_CASES = [
     ("valu_row_groups", 1, 1, 32, [300], [0], [15], [40]),
     # streams longer than the register-resident per-stream kernels hold (32768 entries)
     ("long_stream", 1, 1, 4, [40000, 2000], [5, 0], [16, 16], [3000, 700]),
+    # the pipelined scorer: 128 < R <= 256 rows on 4 waves (3 or 4 of them with rows),
+    # R > 256 on 8 waves in row groups of 512 (one or two groups, the second nearly empty)
+    ("pipe4_rows", 1, 2, 8, [1000, 333, 70], [3, 0, 15], [33, 48, 64], [100, 50, 70]),
+    ("pipe8_rows", 1, 1, 8, [900, 401], [5, 9], [40, 64], [200, 100]),
+    ("pipe8_two_groups", 1, 1, 8, [600], [7], [128], [128]),
+    ("pipe8_ragged_groups", 1, 1, 4, [500], [0], [129], [64]),
+    ("all_paths", 2, 2, 8, [300, 300, 300, 300], [0, 5, 10, 15], [8, 20, 50, 100], [50, 50, 50, 50]),
+    # chunks long enough that the LDS rings wrap (9 and 19 steps per chunk)
+    ("pipe4_long_chunks", 2, 8, 32, [40000], [3], [50], [5000]),
+    ("pipe8_long_chunks", 2, 8, 64, [40000], [3], [50], [5000]),
     # more than 255 sequences: item tables built on the device
     ("many_seqs", 1, 1, 4, [(37 * i) % 90 + 1 for i in range(300)], [(5 * i) % 16 for i in range(300)],
      [16 + (i % 3) * 7 if i % 4 else 6 for i in range(300)], [(11 * i) % 50 for i in range(300)]),
@@ -93,7 +103,7 @@ def test_edge_stages(case):
 
 
 FUSED_CASES = ["page_edges_mfma", "mixed_paths", "empty_and_no_obs", "budget_all", "long_multi_chunk",
-               "long_stream", "many_seqs"]
+               "long_stream", "many_seqs", "all_paths", "pipe8_two_groups"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
