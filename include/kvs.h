@@ -465,6 +465,23 @@ kvs_status kvs_token_confidence(const void *logits, int32_t dtype, int64_t rows,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * kvs_token_confidence_static -- kvs_token_confidence for callers that cannot
+ * allocate device memory (code under graph capture, serving loops that forbid
+ * allocation): the same computation and results, with the partial results in a
+ * buffer the library holds instead of a caller workspace.  Same arguments as
+ * kvs_token_confidence without workspace/workspace_bytes.  The buffer is a static
+ * device array of 16 MiB, one per GPU the library runs on, held until the process
+ * ends; its address is looked up once per device on the first call with that device
+ * current.  Calls whose partial results need more (kvs_token_confidence_workspace_size
+ * above 16 MiB, e.g. 4 096 rows at a vocabulary above 2^17 with k = 20) return
+ * KVS_ERR_UNSUPPORTED.  This call allocates nothing, and nothing in the buffer must
+ * start at zero.  Every call on one GPU shares that GPU's buffer: calls that overlap
+ * on one GPU (concurrent streams, or threads) race and give undefined results.
+ */
+kvs_status kvs_token_confidence_static(const void *logits, int32_t dtype, int64_t rows, int64_t vocab,
+                                       int64_t row_stride, int32_t k, float *conf, void *stream);
+
+/*
  * kvs_confidence_trend (host) -- ActKV, Component 2 (token-level confidence
  * min-pooled over sliding windows into a trajectory-level series; a fitted line
  * with negative slope means the budget is too small).  From n token confidences

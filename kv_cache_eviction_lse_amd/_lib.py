@@ -26,7 +26,8 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_plan", "kvs_plan_host", "kvs_compact", "kvs_plan_compact", "kvs_budget_ratchet",
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
            "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
-           "kvs_step_select", "kvs_beacon_kmeans", "kvs_beacon_seed", "kvs_eviction_round")
+           "kvs_step_select", "kvs_beacon_kmeans", "kvs_beacon_seed", "kvs_eviction_round",
+           "kvs_token_confidence_static")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -122,6 +123,8 @@ def lib() -> C.CDLL:
         L.kvs_token_confidence.restype = C.c_int
         L.kvs_token_confidence.argtypes = [P, C.c_int32, C.c_int64, C.c_int64, C.c_int64, C.c_int32, P, P,
                                            C.c_size_t, P]
+        L.kvs_token_confidence_static.restype = C.c_int
+        L.kvs_token_confidence_static.argtypes = [P, C.c_int32, C.c_int64, C.c_int64, C.c_int64, C.c_int32, P, P]
         L.kvs_confidence_trend.restype = C.c_int
         L.kvs_confidence_trend.argtypes = [P, C.c_int64, C.c_int32, C.c_int32, C.c_int64, P, P, P, P]
         _lib = L
@@ -450,6 +453,20 @@ def kvs_token_confidence(logits, conf, k: int = 20, vocab: int | None = None, wo
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kvs_token_confidence(C.c_void_p(logits.data_ptr()), dtype, rows, V, stride, k, _ptr(conf),
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvs_token_confidence_static(logits, conf, k: int = 20, vocab: int | None = None, stream=None) -> None:
+    """kvs_token_confidence with the library's static partial-result buffer (no
+    workspace; calls that overlap on one GPU race)."""
+    import torch
+    dtype = {torch.float32: KVS_DTYPE_F32, torch.bfloat16: KVS_DTYPE_BF16}.get(logits.dtype)
+    if dtype is None:
+        raise KvsError(3, f"logits dtype {logits.dtype} (float32 or bfloat16)")
+    rows, stride = int(logits.shape[0]), int(logits.stride(0))
+    assert logits.stride(1) == 1
+    V = int(logits.shape[1]) if vocab is None else int(vocab)
+    _check(lib().kvs_token_confidence_static(C.c_void_p(logits.data_ptr()), dtype, rows, V, stride, k,
+                                             _ptr(conf), _stream(stream)))
 
 
 class Trend:

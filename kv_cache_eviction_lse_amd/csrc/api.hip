@@ -603,6 +603,25 @@ kvs_status kvs_token_confidence(const void *logits, int32_t dtype, int64_t rows,
                                            workspace, (hipStream_t)stream));
 }
 
+kvs_status kvs_token_confidence_static(const void *logits, int32_t dtype, int64_t rows, int64_t vocab,
+                                       int64_t row_stride, int32_t k, float *conf, void *stream) {
+  kvs_status st;
+  if ((st = check_confidence(dtype, rows, vocab, row_stride, k)) != KVS_OK) return st;
+  if (rows == 0) return ok();
+  if (!logits || !conf) return fail(KVS_ERR_NULL, "logits/conf is NULL");
+  const size_t need = kvs::conf_workspace_bytes(rows, vocab, k);
+  if (need > kvs::kConfScratchBytes)
+    return fail(KVS_ERR_UNSUPPORTED, "partial results need %zu bytes > the %zu-byte static buffer", need,
+                kvs::kConfScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = kvs::conf_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(kvs::launch_confidence(logits, dtype == KVS_DTYPE_BF16, rows, vocab, row_stride, k, conf,
+                                           ws, (hipStream_t)stream));
+}
+
 kvs_status kvs_confidence_trend(const float *conf_h, int64_t n, int32_t window, int32_t stride, int64_t fit_last,
                                 double *pooled_h, int64_t *pooled_count_h, double *slope_h, int32_t *flag_h) {
   if (n < 0 || window < 1 || stride < 1 || fit_last < 0)

@@ -27,6 +27,9 @@
 // so results are deterministic.
 #include "kvs_device.h"
 
+#include <mutex>
+#include <vector>
+
 namespace kvs {
 namespace {
 
@@ -536,6 +539,34 @@ size_t conf_workspace_bytes(int64_t rows, int64_t vocab, int32_t k) {
   const int32_t C = conf_chunks(vocab, false, k);
   if (C <= 1) return 0;
   return (size_t)rows * C * (2 + k) * sizeof(float);
+}
+
+// The library's own partial-result buffer, for callers that cannot allocate
+// (kvs_token_confidence_static): one copy per GPU, held until the process ends.
+static __device__ __align__(256) uint8_t scratch[kConfScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;     // per device: the address of that device's copy
+}  // namespace
+
+hipError_t conf_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    // the array's name is a host-side stand-in: its device address comes from the runtime,
+    // once per device, with that device current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_t vocab, int64_t stride,

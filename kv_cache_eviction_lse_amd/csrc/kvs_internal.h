@@ -96,6 +96,10 @@ int64_t conf_max_vocab();
 int32_t conf_max_k();
 int32_t conf_chunks(int64_t vocab, bool bf16, int32_t k);
 size_t conf_workspace_bytes(int64_t rows, int64_t vocab, int32_t k);
+// kvs_token_confidence_static: the size of the library's per-device partial-result
+// buffer, and its device address on the current device.
+constexpr size_t kConfScratchBytes = (size_t)16 << 20;
+hipError_t conf_scratch(void **out);
 hipError_t launch_confidence(const void *logits, bool bf16, int64_t rows, int64_t vocab, int64_t stride,
                              int32_t k, float *conf, void *ws, hipStream_t st);
 

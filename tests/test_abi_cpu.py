@@ -359,3 +359,18 @@ def test_beacon_seed_validation():
     assert run(N=16385) == 3 and run(k=0) == 3 and run(k=17) == 3
     assert run(pts=None) == 1 and run(u=None) == 1 and run(cent=None) == 1
     assert run(P=0, pts=None, u=None, cent=None) == 0
+
+
+def test_token_confidence_static_validation():
+    """The static-buffer confidence call validates before touching a device: bad shapes,
+    null pointers and partial results beyond its 16 MiB buffer are rejected."""
+    L = K.lib()
+
+    def run(rows=8, V=1000, stride=1000, k=20, x=FAKE, conf=FAKE, dtype=0):
+        return status(L.kvs_token_confidence_static(x, dtype, rows, V, stride, k, conf, None))
+
+    assert run(k=0) == "KVS_ERR_SHAPE" or run(k=0) == "KVS_ERR_UNSUPPORTED"
+    assert run(x=None) == "KVS_ERR_NULL" and run(conf=None) == "KVS_ERR_NULL"
+    assert run(rows=0, x=None, conf=None) == "KVS_OK"
+    assert run(rows=4096, V=1 << 20, stride=1 << 20) == "KVS_ERR_UNSUPPORTED"
+    assert b"static buffer" in L.kvs_last_error()
