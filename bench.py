@@ -473,6 +473,113 @@ def bench_stepkv(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+RATCHET_METRIC = ("KV entries scored+compacted/sec, amortised over the ratchet loop (one 8B-shape sequence "
+                  "growing 8192 -> 33000 tokens, a round every 64 tokens); achieved HBM GB/s vs peak")
+
+
+def bench_ratchet(args) -> None:
+    """The ratchet loop: 387 rounds of (append 64 tokens, 32 observers, flag, eviction
+    round).  Each round's eviction round is timed with HIP events on its stream; the
+    appends, observers and their LSE (inputs the decode kernel would hand over) are
+    prepared between rounds, untimed.  With --flags confidence the flag comes from the
+    confidence monitor (ActKV Dissected, Component 2), whose call is timed apart.  One
+    JSON line."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    from tests.ratchet_loop import APPEND, OBS, RatchetLoop, checked_round
+
+    dev = torch.device("cuda", 0)
+    lp = RatchetLoop(dev, flags=args.flags)
+    R = lp.R
+    L, Hkv, Hq = lp.L, lp.Hkv, lp.Hq
+    check = set() if args.no_cpu_baseline else {1, R // 4, R // 2, 3 * R // 4, R}
+    conf = torch.empty(APPEND, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    t_round, t_score, t_conf = [], [], []
+    entries, score_bytes, req_bytes, timed_entries = 0, 0, 0, 0
+    worst, pinned, t_ora, n_ora, expansions = 0.0, 0, 0.0, 0, 0
+    budgets = []
+    t_wall = time.perf_counter()
+    for r in range(1, R + 1):
+        q, lse = lp.prepare(r)
+        if args.flags == "confidence":
+            x = lp.step_logits(r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            f = lp.flag(r, x, conf)           # confidence kernel, then the host trend
+            e1.record(st)
+            torch.cuda.synchronize()
+            t_conf.append(e0.elapsed_time(e1))
+        else:
+            f = lp.flag(r)
+        old = lp.budget
+        expansions += int(lp.ratchet(f) != old)
+        budgets.append(lp.budget)
+        seqs, budget_h = lp.batch()
+        obs = K.ObserverSet(q.view(torch.int16), lse, np.array([0, OBS], np.int64), device=dev)
+        bufs = K.RoundBuffers(lp.cache, seqs, obs, budget_h, keep_hits=r in check)
+        n, n_prev = lp.n, lp.n_prev
+        if r in check:
+            plan, w_, pn, to, no = checked_round(lp, r, q, lse, seqs, bufs)
+            worst, pinned, t_ora, n_ora = max(worst, w_), pinned + pn, t_ora + to, n_ora + no
+        else:
+            n_prev_t = torch.tensor([n_prev], dtype=torch.int32, device=dev)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            torch.cuda.synchronize()
+            ev[0].record(st)
+            K.kvs_score(lp.cache, seqs, obs, lp.w.scale, bufs.scores, bufs.workspace)
+            ev[1].record(st)
+            K.kvs_lrfu_select(lp.cache, seqs, bufs.scores, 9, 10, lp.decay, n_prev_t, bufs.budget, bufs.budget_h,
+                              bufs.keep)
+            plan = K.kvs_plan_compact(lp.cache, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs,
+                                      bufs.pair_count)
+            ev[2].record(st)
+            torch.cuda.synchronize()
+            t_round.append(ev[0].elapsed_time(ev[2]))
+            t_score.append(ev[0].elapsed_time(ev[1]))
+            e = n * L * Hkv
+            pairs = int(bufs.pair_count.sum().item())
+            timed_entries += e
+            score_bytes += e * (2 * D + 4) + Hq * OBS * L * (2 * D + 4)
+            req_bytes += e * (2 * D + 8) + Hq * OBS * L * (2 * D + 4) + pairs * (4 * 2 * D + 8)
+        lp.finish(plan)
+    t_wall = time.perf_counter() - t_wall
+    ms_round = float(np.sum(t_round))
+    ms_score = float(np.sum(t_score))
+    gbps = score_bytes / (ms_score / 1000.0) / 1e9
+    res = {
+        "metric": RATCHET_METRIC, "value": timed_entries / (ms_round / 1000.0), "unit": "entries/s",
+        "n_gpus": 1, "steps": len(t_round), "warmup": 0, "ms_per_step": ms_round / len(t_round),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ratchet", "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": D,
+                   "prefill": 8192, "append_per_round": APPEND, "observers": OBS, "rounds": R,
+                   "timed_rounds": len(t_round), "flags": args.flags, "budget_start": 512,
+                   "budget_final": lp.budget, "budget_expansions": expansions,
+                   "timing": "HIP events around each round's kvs_score -> kvs_lrfu_select -> kvs_plan_compact; "
+                             "appends, observers and their LSE are prepared between rounds, untimed; "
+                             "value = sum of entries / sum of round times"},
+        "hbm_gbps": req_bytes / (ms_round / 1000.0) / 1e9,
+        "hbm_frac": req_bytes / (ms_round / 1000.0) / 1e9 / HBM_PEAK_GBPS,
+        "round_ms": {"median": float(np.median(t_round)), "min": float(np.min(t_round)),
+                     "max": float(np.max(t_round)), "first_timed": t_round[0], "last_timed": t_round[-1]},
+        "roofline": {"kernel": "kvs_score kernels over the loop", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "ms": ms_score / len(t_score), "bytes_per_launch": score_bytes / len(t_score)},
+        "wall_s": round(t_wall, 1),
+    }
+    if t_conf:
+        res["confidence_ms"] = {"median": float(np.median(t_conf)), "max": float(np.max(t_conf)),
+                                "includes": "kvs_token_confidence over the round's 64 steps, the copy of 64 "
+                                            "floats to the host and kvs_confidence_trend"}
+    if check:
+        res["cpu_baseline"] = {"value": n_ora / t_ora, "unit": "entries/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{len(check)} rounds x 2 streams (layer, KV head) run by the fp64 oracle "
+                                         f"from the GPU's pre-round state: {n_ora} entries in {t_ora:.1f} s"}
+        res["parity"] = {"rounds_checked": sorted(check), "max_rel_score_err": worst, "keep_pinned": pinned,
+                         "keep_pinned_mismatch": 0}
+    print(json.dumps(res), flush=True)
+
+
 KM_METRIC = ("history-query passes of beacon maintenance (k-means++ seeding, then Lloyd k-means: assignment + "
              "exact update)/sec; achieved HBM GB/s vs peak (70B shape: 80 layers x 64 query heads, 4096 "
              "queries, k = 16, 25 iterations)")
@@ -610,6 +717,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flags", choices=("bernoulli", "confidence"), default="bernoulli",
+                    help="ratchet workload: the configuration's Bernoulli(0.05) flag, or the confidence "
+                         "monitor's trend")
     ap.add_argument("--cpu-streams", type=int, default=48, help="streams in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle CPU time")
     ap.add_argument("--separate", action="store_true",
@@ -644,6 +754,9 @@ def main():
         return
     if args.workload == "beacon_kmeans_llama3_70b":
         bench_kmeans(args)
+        return
+    if args.workload == "ratchet":
+        bench_ratchet(args)
         return
     from workloads import ALL
     from workloads.host import make_layout, observers
