@@ -62,6 +62,23 @@ def step_utility(s: np.ndarray, bounds) -> np.ndarray:
     return out
 
 
+def step_utility_mean(s: np.ndarray, bounds) -> np.ndarray:
+    """The plain step mean, for comparison with reading S3: U_k = (sum of s over the
+    step) / len, taken exactly from the fp32 scores and rounded once to fp32.  S3's grid
+    mean differs from it by at most 2^-31 plus one fp32 spacing of U: each
+    floor(s 2^32) loses less than one grid unit, so the grid sum is within len units
+    of sum(s) 2^32, and the floored quotient within 2 units of the exact mean; the two
+    roundings to fp32 add half a spacing each."""
+    s = np.asarray(s, np.float32)
+    b = check_bounds(bounds, s.shape[0])
+    out = np.zeros(b.shape[0] - 1, np.float32)
+    for k in range(b.shape[0] - 1):
+        lo, hi = int(b[k]), int(b[k + 1])
+        if hi > lo:
+            out[k] = round_fraction_to_f32(sum(Fraction(float(x)) for x in s[lo:hi]) / (hi - lo))
+    return out
+
+
 def step_keys(s: np.ndarray, bounds, beta: float) -> tuple[np.ndarray, np.ndarray]:
     """(c [n] fp32, U [steps] fp32): c_j = beta U_step(j) + (1 - beta) s_j (reading S4)."""
     s = np.asarray(s, np.float32)

@@ -129,3 +129,35 @@ def test_bad_inputs():
         SO.step_keys(s, [0, 5], 1.5)
     with pytest.raises(ValueError):
         SO.step_keys(-s, [0, 5], 0.5)
+
+
+def test_grid_mean_against_the_plain_mean():
+    # reading S3 takes the step mean on the mass cut's 2^-32 grid; against the exact mean
+    # of the fp32 scores rounded once it differs by at most 2^-31 plus one fp32 spacing,
+    # and the keys by beta times that plus one spacing of the key: so a keep decision
+    # can differ only for entries whose plain-mean key lies within that of the K-th key
+    from workloads import steps as WS
+    r2 = np.random.default_rng(5)
+    n_keep_checked = 0
+    for trial in range(6):
+        n = int(r2.integers(200, 3000))
+        _, _, bounds = WS.batch_steps(r2, np.array([n]))
+        s = WS.step_scores(r2, bounds[0])
+        if trial % 2:
+            s = (s * np.float32(1e-3)).astype(np.float32)      # many values below the grid's reach
+        u_grid = SO.step_utility(s, bounds[0])
+        u_mean = SO.step_utility_mean(s, bounds[0])
+        bound = 2.0 ** -31 + np.spacing(np.abs(u_mean)).astype(np.float64)
+        assert np.all(np.abs(u_grid.astype(np.float64) - u_mean) <= bound)
+        beta, B = 0.5, n // 5
+        keep, c, _ = SO.step_select(s, bounds[0], beta, B)
+        step_of = np.repeat(np.arange(len(bounds[0]) - 1), np.diff(bounds[0]))
+        w = np.float32(np.float32(1.0) - np.float32(beta))
+        c_mean = O.fma_f32(np.full(n, np.float32(beta)), u_mean[step_of], (w * s).astype(np.float32))
+        keep_mean = O.select_top_b(c_mean, s, B)
+        kth = np.sort(c_mean.astype(np.float64))[::-1][B - 1]
+        margin = beta * (2.0 ** -31 + float(np.spacing(np.float32(abs(kth))))) + float(np.spacing(np.float32(kth)))
+        far = np.abs(c_mean.astype(np.float64) - kth) > 2 * margin
+        np.testing.assert_array_equal(keep[far], keep_mean[far])
+        n_keep_checked += int(far.sum())
+    assert n_keep_checked > 1000
