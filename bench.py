@@ -856,6 +856,9 @@ def main():
                           keep=ent(bufs.keep, s).astype(bool), crf1=crf_of(s))
         K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
         torch.cuda.synchronize()
+    # The hit bytes are an optional inspection output (the CRF carries the hits into the
+    # next round); the parity round above asked for them, the timed rounds do not.
+    bufs.hit = None
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle:
         for _ in range(20):

@@ -16,6 +16,21 @@ constexpr int kStreamWaves = kStreamThreads / 64;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
+// Workgroup barrier that orders LDS only.  The fences are scoped to the local address
+// space, so a wave waits for its own LDS operations (lgkmcnt) but not for its global
+// loads and stores: those stay in flight across the barrier.  Every block helper below
+// exchanges data through LDS only; a kernel that passes data between its threads
+// through global memory needs __syncthreads() for that.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Mask of the lanes where b holds.  (The bool goes to the builtin as the compare
+// result it is; through an int it would be materialised in a VGPR and compared again.)
+__device__ __forceinline__ uint64_t ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -95,10 +110,10 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *scratch)
   v = wave_sum_u64(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) scratch[wave] = v;
-  __syncthreads();
+  lds_barrier();
   uint64_t t = 0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += scratch[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -107,10 +122,10 @@ __device__ __forceinline__ void block_and_or(uint32_t &a, uint32_t &o, uint32_t 
   o = wave_or(o);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { scratch[2 * wave] = a; scratch[2 * wave + 1] = o; }
-  __syncthreads();
+  lds_barrier();
   uint32_t ra = ~0u, ro = 0u;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { ra &= scratch[2 * w]; ro |= scratch[2 * w + 1]; }
-  __syncthreads();
+  lds_barrier();
   a = ra;
   o = ro;
 }
@@ -126,10 +141,10 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t *scratch)
   x = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) scratch[wave] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t r = 0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r = max(r, scratch[w]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -139,14 +154,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t &t
   const uint32_t incl = wave_scan_u32(x);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) scratch[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
     const uint32_t c = scratch[w];
     before += (w < wave) ? c : 0u;
     tot += c;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return before + incl - x;
 }
@@ -158,14 +173,14 @@ __device__ __forceinline__ uint32_t block_flag_rank(bool flag, uint32_t &total, 
   const int wave = threadIdx.x >> 6;
   const uint32_t in_wave = __popcll(m & lanemask_lt());
   if ((threadIdx.x & 63) == 0) scratch[wave] = __popcll(m);
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
     const uint32_t c = scratch[w];
     before += (w < wave) ? c : 0u;
     tot += c;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return before + in_wave;
 }
@@ -209,15 +224,17 @@ __device__ __forceinline__ float *crf_slot(float *crf, const int32_t *bt_row, in
 // summed in registers first and added with one atomic; every other lane adds
 // directly.  Must be called by all lanes of the wave.
 __device__ __forceinline__ void hist_add_u64(uint64_t *hist, bool valid, uint32_t bin, uint64_t v) {
-  const uint64_t mask = __ballot(valid);
+  const uint64_t mask = ballot(valid);
   if (mask == 0) return;
   const int leader = __ffsll((long long)mask) - 1;
   const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
   const bool same = valid && bin == lb;
-  const uint64_t smask = __ballot(same);
+  const uint64_t smask = ballot(same);
   if (__popcll(smask) >= 8) {
     const uint64_t agg = wave_sum_u64(same ? v : 0ull);
-    if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[lb], (unsigned long long)agg);
+    // (the leader's own bin, lb: an address the compiler takes as per-lane, so it adds
+    // no wave-reduction code of its own around this single-lane atomic)
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)agg);
     if (valid && !same) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)v);
   } else if (valid) {
     atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)v);
@@ -227,13 +244,13 @@ __device__ __forceinline__ void hist_add_u64(uint64_t *hist, bool valid, uint32_
 // Count version: add 1 per valid lane; the lanes sharing the first valid lane's bin
 // are counted with a popcount and added once.
 __device__ __forceinline__ void hist_add_count(uint64_t *hist, bool valid, uint32_t bin) {
-  const uint64_t mask = __ballot(valid);
+  const uint64_t mask = ballot(valid);
   if (mask == 0) return;
   const int leader = __ffsll((long long)mask) - 1;
   const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
   const bool same = valid && bin == lb;
-  const uint64_t smask = __ballot(same);
-  if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[lb], (unsigned long long)__popcll(smask));
+  const uint64_t smask = ballot(same);
+  if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)__popcll(smask));
   if (valid && !same) atomicAdd((unsigned long long *)&hist[bin], 1ull);
 }
 

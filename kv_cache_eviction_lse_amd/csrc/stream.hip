@@ -17,6 +17,8 @@
 // Selection: radix search on the key bits below the candidates' common prefix (from
 // the AND and OR of their keys), 12 bits per pass, with a 4096-bin LDS histogram of
 // counts or of integer masses; the crossing bin is found with one block-wide scan.
+#include <mutex>
+
 #include "kvs_device.h"
 
 namespace kvs {
@@ -24,13 +26,12 @@ namespace kvs {
 constexpr int kRegU = 32;                                        // slots per thread
 constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 32768 entries per stream
 constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
-constexpr int kDigitBits = 12;
-constexpr int kTieList = 512;   // CRF ties at the threshold ranked directly up to this many
-#ifndef KVS_CRF_CHUNK
-#define KVS_CRF_CHUNK 8
-#endif
-static_assert(kRegU % 8 == 0, "the 8-row load and CRF chunks tile the rows exactly");
+constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
+constexpr int kTieMax = 2 * kBins - 512;   // keys searched in an LDS list (plus 256 u64 bins) up to this many
+static_assert(kRegU % 8 == 0, "the 8-row load groups tile the rows exactly");
+// LDS: the stream's scores (u32, slot-major) in dynamic shared memory, the rest static
+constexpr size_t kScoreLds = (size_t)kRegMaxLen * sizeof(uint32_t);
 
 namespace {
 
@@ -51,7 +52,13 @@ struct RegShared {
   uint64_t hist[kBins];
   uint64_t scratch[kStreamWaves];
   uint64_t found[3];
+  uint32_t list_n;
+  // entry counts of the mass cut's first pass, two 16-bit bins per word (a bin holds at
+  // most kRegMaxLen = 2^15 entries, so a count never carries into its neighbour)
+  uint32_t cnt16[kBins / 2];
 };
+static_assert(kTieMax + 512 <= 2 * kBins && kTieMax % 2 == 0, "a key list and its bins fit in the histogram's space");
+static_assert(kBins <= 4 * kStreamThreads, "the crossing-bin scan takes 4 bins per thread");
 
 struct Sel {
   uint32_t key;     // v*
@@ -66,11 +73,11 @@ __device__ __forceinline__ uint64_t block_excl_u64(uint64_t x, uint64_t *scratch
   const uint64_t incl = wave_scan_u64(x);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) scratch[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   // lane w < waves holds wave w's total; one wave scan gives every wave its offset
   const int lane = threadIdx.x & 63;
   const uint64_t wsc = wave_scan_u64(lane < kStreamWaves ? scratch[lane] : 0ull);
-  __syncthreads();
+  lds_barrier();
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto lane_u64 = [&](int l) -> uint64_t {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wsc, l);
@@ -105,13 +112,13 @@ __device__ __forceinline__ void rank_flags(uint32_t fmask, int rounds, uint32_t 
     const uint64_t b = __ballot(u < rounds && ((fmask >> u) & 1u));
     if (lane == 0) cnt[u * kStreamWaves + wave] = (uint32_t)__popcll(b);
   }
-  __syncthreads();
+  lds_barrier();
   static_assert(kRegU * kStreamWaves <= kStreamThreads, "one (row, wave) count per thread");
   const uint32_t v = threadIdx.x < kRegU * kStreamWaves ? cnt[threadIdx.x] : 0u;
   uint32_t tot;
   const uint32_t ex = block_exclusive_scan(v, tot, scratch);
   if (threadIdx.x < kRegU * kStreamWaves) cnt[threadIdx.x] = ex;
-  __syncthreads();
+  lds_barrier();
   const uint32_t *mine = cnt + opaque(wave);
 #pragma unroll
   for (int u = 0; u < kRegU; ++u) {
@@ -121,18 +128,201 @@ __device__ __forceinline__ void rank_flags(uint32_t fmask, int rounds, uint32_t 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();     // cnt is free again
+  lds_barrier();     // cnt is free again
+}
+
+// v* with weight(keys > v*) < need <= weight(keys >= v*) over the nt keys of an LDS
+// list (1 <= need <= the list's total weight), the weight of a key being 1 (COUNT)
+// or its integer mass: a radix search from the first bit where the keys differ, 8
+// bits per pass, with a 256-bin u64 histogram (LDS atomics) scanned by one wave.
+// bins: 256 u64 of LDS; found: 3 u64.  Every thread of the block must call it.
+template <bool COUNT>
+__device__ __forceinline__ Sel list_select(const uint32_t *key, int nt, uint64_t need, uint64_t *bins,
+                                           uint32_t *scratch, uint64_t *found) {
+  uint32_t a = ~0u, o = 0u;
+  for (int x = threadIdx.x; x < nt; x += kStreamThreads) {
+    a &= key[x];
+    o |= key[x];
+  }
+  block_and_or(a, o, scratch);
+  Sel r;
+  r.target = need;
+  const uint32_t diff = a ^ o;
+  if (diff == 0) {
+    r.key = a;
+    r.above = 0;
+    r.at = COUNT ? (uint64_t)nt : (uint64_t)nt * fixed_mass(a);
+    return r;
+  }
+  int top = 31 - __clz(diff);
+  uint32_t prefix = a & ~((2u << top) - 1u);      // (top = 31: the shift wraps to 0, mask all bits)
+  uint64_t rem = need, above = 0, at = 0;
+  while (top >= 0) {
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int lo = top - width + 1;
+    const uint32_t nb = 1u << width;
+    if (threadIdx.x < 256) bins[threadIdx.x] = 0ull;
+    lds_barrier();
+    const int hs = top + 1;
+    for (int x = threadIdx.x; x < nt; x += kStreamThreads) {
+      const uint32_t k = key[x];
+      if (hs >= 32 || (k >> hs) == (prefix >> hs))
+        atomicAdd((unsigned long long *)&bins[(k >> lo) & (nb - 1u)],
+                  COUNT ? 1ull : (unsigned long long)fixed_mass(k));
+    }
+    lds_barrier();
+    if (threadIdx.x < 64) {
+      // lane L takes bins nb-1-4L .. nb-4-4L (descending); the exclusive scan is the
+      // weight of all higher bins
+      const int lane = threadIdx.x;
+      uint64_t h[4], ls = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = (int)nb - 1 - (4 * lane + q);
+        h[q] = b >= 0 ? bins[b] : 0ull;
+        ls += h[q];
+      }
+      uint64_t acc = wave_scan_u64(ls) - ls;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = (int)nb - 1 - (4 * lane + q);
+        if (b >= 0 && acc < rem && rem <= acc + h[q]) {
+          found[0] = (uint64_t)b;
+          found[1] = acc;
+          found[2] = h[q];
+        }
+        acc += h[q];
+      }
+    }
+    lds_barrier();
+    const uint32_t b = (uint32_t)found[0];
+    const uint64_t ab = found[1];
+    at = found[2];
+    prefix |= b << lo;
+    rem -= ab;
+    above += ab;
+    top = lo - 1;
+  }
+  r.key = prefix;
+  r.above = above;
+  r.at = at;
+  return r;
+}
+
+// Appends key(u) of this thread's valid rows (u < cnt) where take(u, key(u)) holds to
+// an LDS list of at most cap keys, in no particular order: per row, each wave
+// reserves its range with one LDS atomic (lane 0, the wave's count of the row) and
+// its lanes write at the ballot offsets.  Returns the number of keys that hold; all of
+// them are in the list when it is at most cap (else some are missing).  Keys are read
+// 8 rows at a time and take is evaluated without branches, so the reads and the
+// atomics of a group overlap; groups of rows that every thread holds (u < full) skip
+// the row test.  Every thread of the block must call it.
+template <typename KeyF, typename P>
+__device__ __forceinline__ uint32_t gather_keys(KeyF key, P take, int cnt, int full, uint32_t *list, uint32_t cap,
+                                                uint32_t *count) {
+  if (threadIdx.x == 0) *count = 0;
+  lds_barrier();
+  const int lane = threadIdx.x & 63;
+  // (an address the compiler takes as per-lane: it then adds no wave-reduction code of
+  // its own around lane 0's atomics, code that would wait for each one in turn)
+  uint32_t *cnt_lane = count + opaque(0);
+#pragma unroll
+  for (int u0 = 0; u0 < kRegU; u0 += 8) {
+    uint32_t k[8], base[8];
+    uint64_t m[8];
+    const bool rows_full = u0 + 8 <= full;     // uniform
+    const int cnt_p = opaque(cnt);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) k[v] = key(u0 + v);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      m[v] = ballot((rows_full || u0 + v < cnt_p) && take(u0 + v, k[v]));
+      base[v] = 0;
+      if (lane == 0) base[v] = atomicAdd(cnt_lane, (uint32_t)__popcll(m[v]));
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)base[v]) +
+                           (uint32_t)__popcll(m[v] & lanemask_lt());
+      if (((m[v] >> lane) & 1ull) && pos < cap) list[pos] = k[v];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lds_barrier();
+  return *count;
+}
+
+// Adds w (1 with COUNT) to bin in the lanes where ok holds.  Lanes that share the
+// first adding lane's bin are summed first and added once when they are many (8 for
+// counts, whose sum is a popcount; every adding lane for masses, whose sum takes a wave
+// reduction: the case of equal scores); otherwise every lane adds its own and the LDS
+// serialises lanes that share an address.  Zero masses add nothing.  Must be called
+// by all lanes of the wave.
+template <bool COUNT>
+__device__ __forceinline__ void hist_add(uint64_t *hist, bool ok, uint32_t bin, uint64_t w) {
+  if (!COUNT) ok = ok && w != 0;
+  const uint64_t mask = ballot(ok);
+  if (mask == 0) return;
+  const int leader = (int)__builtin_ctzll(mask);
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+  const bool same = ok && bin == lb;
+  const uint64_t smask = ballot(same);
+  if (COUNT ? __popcll(smask) >= 8 : smask == mask) {
+    const uint64_t agg = COUNT ? (uint64_t)__popcll(smask) : wave_sum_u64(same ? w : 0ull);
+    // (the leader's own bin: an address the compiler takes as per-lane)
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)agg);
+    if (ok && !same) atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)(COUNT ? 1ull : w));
+  } else if (ok) {
+    atomicAdd((unsigned long long *)&hist[bin], (unsigned long long)(COUNT ? 1ull : w));
+  }
+}
+
+// One histogram pass: every candidate whose key matches prefix above bit hs (hs = 32:
+// no test, every candidate matches) adds its weight to bin (key >> lo) & (nb - 1).
+// Keys are read 8 rows at a time; groups of rows that every thread holds (u < full)
+// skip the per-lane row test.
+template <bool COUNT, bool FIRST, typename KeyF, typename CandF, typename WF>
+__device__ __forceinline__ void hist_pass(KeyF key, int cnt, int full, CandF cand, WF weight_of, int hs,
+                                          uint32_t prefix, int lo, uint32_t nb, uint64_t *hist, uint32_t *cnt16) {
+  const uint32_t ph = hs >= 32 ? 0u : prefix >> hs;
+  const int hsc = hs & 31;
+  // FIRST: every candidate matches the prefix (no test), and a mass pass also counts
+  // its entries per bin into cnt16
+  auto add = [&](bool ok, uint32_t k) {
+    const uint32_t bin = (k >> lo) & (nb - 1u);
+    hist_add<COUNT>(hist, ok, bin, COUNT ? 1ull : weight_of(k));
+    if (FIRST && !COUNT && ok) atomicAdd(&cnt16[bin >> 1], 1u << ((bin & 1u) << 4));
+  };
+#pragma unroll
+  for (int u0 = 0; u0 < kRegU; u0 += 8) {
+    uint32_t k[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) k[v] = key(u0 + v);
+    if (u0 + 8 <= full) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) add(cand(u0 + v) && (FIRST || (k[v] >> hsc) == ph), k[v]);
+    } else {
+      const int cnt_p = opaque(cnt);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) add(u0 + v < cnt_p && cand(u0 + v) && (FIRST || (k[v] >> hsc) == ph), k[v]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // v* with weight(keys > v*) < target <= weight(keys >= v*) over the candidates
-// (slot valid and cand(u)); key[u] holds the key of this thread's row u.  With CUT the
-// target is ceil(num * W / den) for the candidates' total weight W, which the first
-// pass yields (so W needs no pass of its own); otherwise it is `target`.  A target of
-// 0 returns key ~0 and at = 0.
-template <bool COUNT, bool CUT, typename CandF, typename WF>
-__device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt, CandF cand, WF weight_of,
-                                          uint64_t target, uint32_t num, uint32_t den, uint32_t and_all,
-                                          uint32_t or_all, RegShared &sh) {
+// (slot valid and cand(u)); key(u) is the key of this thread's row u (a register, or
+// the thread's own slot of an LDS array).  With CUT the target is ceil(num * W / den)
+// for the candidates' total weight W, which the first pass yields (so W needs no pass
+// of its own); otherwise it is `target`.  A target of 0 returns key ~0 and at = 0.
+// After each pass the candidates in the crossing bin are gathered into an LDS list
+// when they are few enough (at most kTieMax: known from the count, or bounded by the
+// bin's mass over the mass of its smallest key), and the search finishes there
+// instead of with further passes over every row.
+template <bool COUNT, bool CUT, typename KeyF, typename CandF, typename WF>
+__device__ __forceinline__ Sel reg_select(KeyF key, int cnt, int full, CandF cand, WF weight_of, uint64_t target,
+                                          uint32_t num, uint32_t den, uint32_t and_all, uint32_t or_all,
+                                          RegShared &sh) {
   auto target_of = [&](uint64_t W) -> uint64_t {
     if constexpr (CUT) return (W / den) * num + ((W % den) * num + den - 1) / den;
     else return target;
@@ -143,7 +333,8 @@ __device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt,
     uint64_t w = 0;
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) {
-      if (u < cnt && cand(u)) w += COUNT ? 1ull : weight_of(key[u]);
+      const uint32_t k = key(u);
+      if ((u < opaque(cnt)) & cand(u)) w += COUNT ? 1ull : weight_of(k);
       __builtin_amdgcn_sched_barrier(0);
     }
     const uint64_t tot = block_sum_u64(w, sh.scratch);
@@ -158,26 +349,24 @@ __device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt,
   uint64_t need = CUT ? 0 : target, above = 0, at = 0;
   r.target = need;
   bool first = CUT;
+  uint32_t *list = (uint32_t *)sh.hist;
+  uint64_t *list_bins = sh.hist + kTieMax / 2;
+  int pass = 0;
   while (top >= 0) {
     const int width = top + 1 < kDigitBits ? top + 1 : kDigitBits;
     const int lo = top - width + 1;
     const uint32_t nb = 1u << width;
     for (uint32_t b = threadIdx.x; b < nb; b += kStreamThreads) sh.hist[b] = 0;
-    __syncthreads();
-    const int hs = top + 1;
-    const int cnt_p = opaque(cnt);
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      // (the weight of a key is pass-invariant; computing it from an opaque copy keeps
-      // the compiler from hoisting all kRegU weights out of the pass loop)
-      const uint32_t k = COUNT ? key[u] : (uint32_t)opaque((int)key[u]);
-      const bool v = u < cnt_p && cand(u) && (hs >= 32 || (k >> hs) == (prefix >> hs));
-      const uint32_t bin = (k >> lo) & (nb - 1u);
-      if (COUNT) hist_add_count(sh.hist, v, bin);
-      else hist_add_u64(sh.hist, v, bin, v ? weight_of(k) : 0ull);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
+    if (!COUNT && pass == 0)
+      for (uint32_t b = threadIdx.x; b < kBins / 2; b += kStreamThreads) sh.cnt16[b] = 0;
+    lds_barrier();
+    // (the first pass needs no prefix test: and_all and or_all cover every candidate)
+    if (pass == 0)
+      hist_pass<COUNT, true>(key, cnt, full, cand, weight_of, 32, prefix, lo, nb, sh.hist, sh.cnt16);
+    else
+      hist_pass<COUNT, false>(key, cnt, full, cand, weight_of, top + 1, prefix, lo, nb, sh.hist, sh.cnt16);
+    ++pass;
+    lds_barrier();
     // bins in descending order, 4 per thread; the exclusive scan is the weight of all
     // higher bins
     uint64_t h[4], ls = 0;
@@ -210,15 +399,39 @@ __device__ __forceinline__ Sel reg_select(const uint32_t (&key)[kRegU], int cnt,
       }
       acc += h[q];
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t b = (uint32_t)sh.found[0];
     const uint64_t a = sh.found[1];
     at = sh.found[2];
-    __syncthreads();
+    lds_barrier();
     prefix |= b << lo;
     need -= a;
     above += a;
     top = lo - 1;
+    if (top < 0) break;
+    bool try_list;
+    if (COUNT) {
+      try_list = at <= (uint64_t)kTieMax;
+    } else if (pass == 1) {
+      // the first pass counted the bin's entries
+      try_list = ((sh.cnt16[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu) <= (uint32_t)kTieMax;
+    } else {
+      const uint64_t m_low = weight_of(prefix);      // the bin's smallest key
+      try_list = m_low == 0 || at / m_low <= (uint64_t)kTieMax;
+    }
+    if (try_list) {
+      const uint32_t pl = prefix >> lo;
+      const uint32_t nl = gather_keys(
+          key, [&](int u, uint32_t k) { return cand(u) && (k >> lo) == pl; }, cnt, full, list, (uint32_t)kTieMax,
+          &sh.list_n);
+      if (nl <= (uint32_t)kTieMax) {
+        const Sel r2 = list_select<COUNT>(list, (int)nl, need, list_bins, (uint32_t *)sh.scratch, sh.found);
+        r.key = r2.key;
+        r.above = above + r2.above;
+        r.at = r2.at;
+        return r;
+      }
+    }
   }
   r.key = prefix;
   r.above = above;
@@ -240,9 +453,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   __shared__ int32_t bt_lds[kRegBtCap];
   __shared__ RegShared sh;
   __shared__ uint32_t flag_scratch[kStreamWaves];
-  __shared__ __attribute__((aligned(16))) uint32_t tie_s[kTieList];
-  __shared__ __attribute__((aligned(16))) int32_t tie_j[kTieList];
-  __shared__ uint32_t tie_count;
+  extern __shared__ uint32_t s_lds[];     // kScoreLds bytes: score bits of slot u * 1024 + t
 
   const int32_t i = blockIdx.y;
   const int32_t lg = blockIdx.x;
@@ -283,20 +494,40 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     return (uint32_t)bt_lds[pos >> 4] * page_stride + (uint32_t)(pos & 15);
   };
 
-  uint32_t s[kRegU];
+  // The scores live in LDS (each thread reads and writes only its own slots, so they
+  // need no barrier); the CRF or caller keys live in registers c.
   uint32_t c[kRegU];
+  // (two opaque base addresses, with the row in the instruction's offset, and an opaque
+  // copy of cnt at each use: otherwise the compiler keeps 32 slot addresses and 32 row
+  // masks live through the whole kernel, and spills them)
+  const uint32_t *sb0 = s_lds + opaque(tid);                        // rows 0..15
+  const uint32_t *sb1 = s_lds + 16 * kStreamThreads + opaque(tid);   // rows 16..31
+  auto sv = [&](int u) -> uint32_t { return u < 16 ? sb0[u * kStreamThreads] : sb1[(u - 16) * kStreamThreads]; };
+  auto valid = [&](int u) -> bool { return u < opaque(cnt); };
   bool have_s = false;
-  auto load_s = [&]() {
-    // 8 loads in flight per thread and chunk; a chunk's offsets die at issue
+  // AND and OR of the valid scores (block-wide once reduced): the common prefix of
+  // every score, so of every subset of them
+  uint32_t s_and = ~0u, s_or = 0u;
+  // scores of every row in flight at once through the registers tmp (8 or kRegU of
+  // them), then into LDS (0 for slots past the end); this thread's AND and OR of them
+  auto load_s = [&](uint32_t *tmp, int group) {
+    for (int u0 = 0; u0 < kRegU; u0 += group) {
 #pragma unroll
-    for (int u0 = 0; u0 < kRegU; u0 += 8) {
-      const int t = opaque(tid);
+      for (int g0 = 0; g0 < group; g0 += 8) {
+        const int t = opaque(tid);
 #pragma unroll
-      for (int u = u0; u < u0 + 8; ++u) s[u] = sp[slot(u, t)];
-      __builtin_amdgcn_sched_barrier(0);
+        for (int v = 0; v < 8; ++v) tmp[g0 + v] = sp[slot(u0 + g0 + v, t)];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int v = 0; v < group; ++v) {
+        const int u = u0 + v;
+        const bool ok = valid(u);
+        s_lds[u * kStreamThreads + tid] = ok ? tmp[v] : 0u;
+        s_and &= ok ? tmp[v] : ~0u;
+        s_or |= ok ? tmp[v] : 0u;
+      }
     }
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) s[u] = u < cnt ? s[u] : 0u;
   };
   // every row's CRF in flight at once, issued in 8-row groups so that only a group's
   // offsets are live at a time (nothing waits between the groups)
@@ -311,20 +542,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   };
   auto all = [](int) { return true; };
   auto one = [](uint32_t) -> uint64_t { return 1; };
-  __syncthreads();   // block-table slice visible
+  lds_barrier();   // block-table slice visible
 
+  uint32_t cmx = 0, ncm = 0;   // this thread's largest CRF (or key) and its count
   if (LRFU) {
-    load_s();
+    // (c carries the scores on their way to LDS)
+    load_s(c, kRegU);
     have_s = true;
-    uint32_t band = ~0u, bor = 0u;
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      band &= u < cnt ? s[u] : ~0u;
-      bor |= s[u];
-    }
-    block_and_or(band, bor, (uint32_t *)sh.scratch);
+    // The prior CRF is gathered now into c and waited for only where the update reads
+    // it: the barriers of the cut order LDS only, so these loads stay in flight
+    // through the whole mass cut.
+    gather_crf();
+    block_and_or(s_and, s_or, (uint32_t *)sh.scratch);
     // T = ceil(num * M / den), M = the stream's total integer mass (from the first pass)
-    const Sel r = reg_select<false, true>(s, cnt, all, fixed_mass, 0, a.num, a.den, band, bor, sh);
+    const Sel r = reg_select<false, true>(sv, cnt, full, all, fixed_mass, 0, a.num, a.den, s_and, s_or, sh);
     const uint64_t T = r.target;
     const bool none = T == 0;
     uint32_t vstar = 0xFFFFFFFFu;
@@ -341,52 +572,39 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       // ties at the threshold exceed the hits still needed: lowest slots first
       uint32_t tmask = 0;
 #pragma unroll
-      for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(u < cnt && s[u] == vstar) << u;
+      for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(valid(u) & (sv(u) == vstar)) << u;
       rank_flags(tmask, rounds, (uint32_t *)sh.hist, flag_scratch, [&](int u, uint32_t rk) {
-        const bool valid = u < cnt;
         const bool tie = (tmask >> u) & 1u;
-        const bool h = valid && (s[u] > vstar || (tie && rk < k_needed));
+        const bool h = valid(u) & ((sv(u) > vstar) | (tie & (rk < k_needed)));
         hbits |= (uint64_t)h << u;
       });
     } else if (!none) {
 #pragma unroll
-      for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(u < cnt && s[u] >= vstar) << u;
+      for (int u = 0; u < kRegU; ++u) hbits |= (uint64_t)(valid(u) & (sv(u) >= vstar)) << u;
     }
-    // LRFU update of the paged CRF, KVS_CRF_CHUNK rows per round trip
+    // LRFU update of the paged CRF in place (the priors are in c), the hit bytes, and
+    // this thread's largest new CRF with its count, in one pass
     const float d = a.decay[i];
     const int np_rel = a.n_prev[i] - tid;       // row u has a prior iff u * 1024 < np_rel
-    constexpr int kChunk = KVS_CRF_CHUNK;
-#pragma unroll
-    for (int u0 = 0; u0 < kRegU; u0 += kChunk) {
-      const int t = opaque(tid);
-      uint32_t off[kChunk];
-      float prior[kChunk];
-#pragma unroll
-      for (int v = 0; v < kChunk; ++v) {
-        off[v] = crf_off(u0 + v, t);
-        prior[v] = crf_base[off[v]];
-      }
-#pragma unroll
-      for (int v = 0; v < kChunk; ++v) {
-        const int u = u0 + v;
-        const bool h = (hbits >> u) & 1;
-        const float p = u * kStreamThreads < np_rel ? prior[v] : 0.f;
-        const float nv = __builtin_fmaf(d, p, h ? 1.f : 0.f);
-        c[u] = u < cnt ? __float_as_uint(nv) : 0u;
-        KVS_FOR_VALID(u, crf_base[off[v]] = nv;)
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (a.hit) {
-      uint8_t *hp = a.hit + (int64_t)lg * a.b.E + e0;
+    uint8_t *hp = a.hit ? a.hit + (int64_t)lg * a.b.E + e0 : nullptr;
+    {
       const int t = opaque(tid);
 #pragma unroll
       for (int u = 0; u < kRegU; ++u) {
-        KVS_FOR_VALID(u, hp[u * kStreamThreads + t] = (uint8_t)((hbits >> u) & 1);)
+        const bool h = (hbits >> u) & 1;
+        const float p = u * kStreamThreads < np_rel ? __uint_as_float(c[u]) : 0.f;
+        const float nv = __builtin_fmaf(d, p, h ? 1.f : 0.f);
+        const uint32_t cb = __float_as_uint(nv);
+        const bool ok = valid(u);
+        c[u] = ok ? cb : 0u;
+        const bool gt = ok && cb > cmx, eq = ok && cb == cmx;
+        cmx = gt ? cb : cmx;
+        ncm = gt ? 1u : ncm + (eq ? 1u : 0u);
+        KVS_FOR_VALID(u, crf_base[crf_off(u, t)] = nv; if (hp) hp[u * kStreamThreads + t] = (uint8_t)h;)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (!SELECT) return;
-    have_s = false;     // the selection reloads the scores only for ties at the threshold
     if (K == 0 || K == n) {
       const int t = opaque(tid);
 #pragma unroll
@@ -409,7 +627,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       gather_crf();
     }
 #pragma unroll
-    for (int u = 0; u < kRegU; ++u) c[u] = u < cnt ? c[u] : 0u;
+    for (int u = 0; u < kRegU; ++u) c[u] = valid(u) ? c[u] : 0u;
   }
 
   // ---- top-K keep set ----
@@ -421,114 +639,120 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   // every key >= 1 kept).  The radix search then runs on one side only, whose keys
   // share a longer prefix, so it needs fewer passes.
   constexpr uint32_t kOne = 0x3F800000u;           // 1.0f; keys are fp32 bits of values >= 0
-  uint32_t band_hi = ~0u, bor_hi = 0u, band_lo = ~0u, bor_lo = 0u, cmax = 0u, ge = 0u;
+  auto cv = [&](int u) -> uint32_t { return c[u]; };
+  if (!LRFU) {
 #pragma unroll
-  for (int u = 0; u < kRegU; ++u) {
-    const bool v = u < cnt, hi = c[u] >= kOne;
-    band_hi &= v && hi ? c[u] : ~0u;
-    bor_hi |= v && hi ? c[u] : 0u;
-    band_lo &= v && !hi ? c[u] : ~0u;
-    bor_lo |= v && !hi ? c[u] : 0u;
-    ge += v && hi ? 1u : 0u;
-    cmax = c[u] > cmax ? c[u] : cmax;
+    for (int u = 0; u < kRegU; ++u) {
+      const bool ok = valid(u);
+      const bool gt = ok && c[u] > cmx, eq = ok && c[u] == cmx;
+      cmx = gt ? c[u] : cmx;
+      ncm = gt ? 1u : ncm + (eq ? 1u : 0u);
+    }
   }
-  cmax = block_max_u32(cmax, (uint32_t *)sh.scratch);
-  uint32_t at_max = 0;
-#pragma unroll
-  for (int u = 0; u < kRegU; ++u) at_max += (u < cnt && c[u] == cmax) ? 1u : 0u;
-  const uint64_t n_max = block_sum_u64(at_max, sh.scratch);
+  const uint32_t cmax = block_max_u32(cmx, (uint32_t *)sh.scratch);
+  const uint64_t n_max = block_sum_u64(cmx == cmax ? ncm : 0u, sh.scratch);
   Sel r1;
   if (n_max >= (uint64_t)K) {
     r1.key = cmax;
     r1.above = 0;
     r1.at = n_max;
-  } else if (!LRFU && a.keys) {
-    // caller keys (step-aware ranking) have no reason to straddle 1.0: no split
-    uint32_t band = band_hi & band_lo, bor = bor_hi | bor_lo;
-    block_and_or(band, bor, (uint32_t *)sh.scratch);
-    r1 = reg_select<true, false>(c, cnt, all, one, (uint64_t)K, 0, 1, band, bor, sh);
   } else {
-    const uint64_t n_ge = block_sum_u64(ge, sh.scratch);
-    const bool upper = n_ge >= (uint64_t)K;
-    uint32_t band = upper ? band_hi : band_lo, bor = upper ? bor_hi : bor_lo;
-    block_and_or(band, bor, (uint32_t *)sh.scratch);
-    auto side = [&](int u) { return (c[u] >= kOne) == upper; };
-    r1 = reg_select<true, false>(c, cnt, side, one, upper ? (uint64_t)K : (uint64_t)K - n_ge, 0, 1, band, bor, sh);
-    if (!upper) r1.above += n_ge;
+    uint32_t band_hi = ~0u, bor_hi = 0u, band_lo = ~0u, bor_lo = 0u, ge = 0u;
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      const bool v = valid(u), hi = c[u] >= kOne;
+      band_hi &= v && hi ? c[u] : ~0u;
+      bor_hi |= v && hi ? c[u] : 0u;
+      band_lo &= v && !hi ? c[u] : ~0u;
+      bor_lo |= v && !hi ? c[u] : 0u;
+      ge += v && hi ? 1u : 0u;
+    }
+    if (!LRFU && a.keys) {
+      // caller keys (step-aware ranking) have no reason to straddle 1.0: no split
+      uint32_t band = band_hi & band_lo, bor = bor_hi | bor_lo;
+      block_and_or(band, bor, (uint32_t *)sh.scratch);
+      r1 = reg_select<true, false>(cv, cnt, full, all, one, (uint64_t)K, 0, 1, band, bor, sh);
+    } else {
+      const uint64_t n_ge = block_sum_u64(ge, sh.scratch);
+      const bool upper = n_ge >= (uint64_t)K;
+      uint32_t band = upper ? band_hi : band_lo, bor = upper ? bor_hi : bor_lo;
+      block_and_or(band, bor, (uint32_t *)sh.scratch);
+      auto side = [&](int u) { return (c[u] >= kOne) == upper; };
+      r1 = reg_select<true, false>(cv, cnt, full, side, one, upper ? (uint64_t)K : (uint64_t)K - n_ge, 0, 1, band,
+                                   bor, sh);
+      if (!upper) r1.above += n_ge;
+    }
   }
   const uint32_t cstar = r1.key;
   const uint64_t need = K - r1.above;          // entries to keep among CRF == c*
   const bool lvl2 = need < r1.at;
-  if (lvl2 && r1.at <= (uint64_t)kTieList) {
-    // Few entries tie at c*: gather them (s, slot) into LDS and rank each one among
-    // the ties by (s desc, slot asc) directly; the first `need` are kept.
-    if (!have_s) load_s();
-    if (tid == 0) tie_count = 0;
-    __syncthreads();
-    const int lane = tid & 63;
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      const bool t = u < cnt && c[u] == cstar;
-      const uint64_t m = __ballot(t);
-      if (m) {
-        const int leader = __ffsll((long long)m) - 1;
-        uint32_t base = 0;
-        if (lane == leader) base = atomicAdd(&tie_count, (uint32_t)__popcll(m));
-        base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-        const uint32_t idx = base + (uint32_t)__popcll(m & lanemask_lt());
-        if (t && idx < (uint32_t)kTieList) {
-          tie_s[idx] = s[u];
-          tie_j[idx] = u * kStreamThreads + tid;
-        }
-      }
-    }
-    __syncthreads();
-    const int nt = (int)r1.at;     // == tie_count (the entries equal to c*)
-    for (int x = tid; x < nt; x += kStreamThreads) {
-      const uint32_t sx = tie_s[x];
-      const int32_t jx = tie_j[x];
-      // ties ahead of x in (s desc, slot asc), four at a time (16-byte LDS reads, the
-      // same address in every lane); the slots past nt are never compared
-      uint32_t rank = 0;
-      int y = 0;
-#pragma unroll 4
-      for (; y + 4 <= nt; y += 4) {
-        const uint4 sy = *(const uint4 *)&tie_s[y];
-        const int4 jy = *(const int4 *)&tie_j[y];
-        rank += (sy.x > sx || (sy.x == sx && jy.x < jx)) ? 1u : 0u;
-        rank += (sy.y > sx || (sy.y == sx && jy.y < jx)) ? 1u : 0u;
-        rank += (sy.z > sx || (sy.z == sx && jy.z < jx)) ? 1u : 0u;
-        rank += (sy.w > sx || (sy.w == sx && jy.w < jx)) ? 1u : 0u;
-      }
-      for (; y < nt; ++y) {
-        const uint32_t sy = tie_s[y];
-        rank += (sy > sx || (sy == sx && tie_j[y] < jx)) ? 1u : 0u;
-      }
-      kp[jx] = rank < need ? 1 : 0;
-    }
-    const int t = opaque(tid);
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      if (c[u] != cstar) {
-        KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = c[u] > cstar ? 1 : 0;)
-      }
-    }
-    return;
-  }
   uint32_t sstar = 0;
   uint64_t need2 = 0, at2 = 0;
   if (lvl2) {
-    if (!have_s) load_s();
-    uint32_t sa = ~0u, so = 0u;
-#pragma unroll
-    for (int u = 0; u < kRegU; ++u) {
-      const bool t = u < cnt && c[u] == cstar;
-      sa &= t ? s[u] : ~0u;
-      so |= t ? s[u] : 0u;
+    // The entries tied at c* are ranked by this round's s: v* of s over them.
+    if (!have_s) {
+      uint32_t tmp[8];
+      load_s(tmp, 8);
+      block_and_or(s_and, s_or, (uint32_t *)sh.scratch);
     }
-    block_and_or(sa, so, (uint32_t *)sh.scratch);
-    auto in_tie = [&](int u) { return c[u] == cstar; };
-    const Sel r2 = reg_select<true, false>(s, cnt, in_tie, one, need, 0, 1, sa, so, sh);
+    Sel r2;
+    if (r1.at <= (uint64_t)kTieMax) {
+      // Few enough ties: their scores are gathered into an LDS list (sh.hist is free
+      // here) and searched there, which touches at most kTieMax keys per pass instead
+      // of every row of the stream.
+      uint32_t *tl = (uint32_t *)sh.hist;
+      const uint32_t nl = gather_keys(sv, [&](int u, uint32_t) { return c[u] == cstar; }, cnt, full, tl,
+                                      (uint32_t)kTieMax, &sh.list_n);
+      r2 = list_select<true>(tl, (int)nl, need, sh.hist + kTieMax / 2, (uint32_t *)sh.scratch, sh.found);
+    } else {
+      bool done = false;
+      if (LRFU && s_and != s_or) {
+        // The mass cut's first pass counted every entry per bin of the first score digit
+        // (the same digit as here: both come from the AND and OR of every score).  Take
+        // the lowest bin b0 whose entries, with those of the bins above, number at most
+        // kTieMax: the tied entries scored from b0's lower edge up then fit the list,
+        // and when there are at least `need` of them they hold the answer.
+        const int top0 = 31 - __clz(s_and ^ s_or);
+        const int width0 = top0 + 1 < kDigitBits ? top0 + 1 : kDigitBits;
+        const int lo0 = top0 - width0 + 1;
+        const int nb0 = 1 << width0;
+        const uint32_t prefix0 = top0 == 31 ? 0u : (s_and & ~((2u << top0) - 1u));
+        uint32_t best = 0xFFFFFFFFu;      // lowest qualifying bin of this lane's bins
+        if (tid < 64) {
+          constexpr int kPer = kBins / 64;  // bins per lane, in descending order
+          uint32_t cb[kPer], ls = 0;
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) {
+            const int b = nb0 - 1 - (kPer * tid + q);
+            cb[q] = b >= 0 ? (sh.cnt16[b >> 1] >> ((b & 1) << 4)) & 0xFFFFu : 0u;
+            ls += cb[q];
+          }
+          uint32_t acc = wave_scan_u32(ls) - ls;   // entries in the bins above this lane's
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) {
+            const int b = nb0 - 1 - (kPer * tid + q);
+            acc += cb[q];
+            if (b >= 0 && acc <= (uint32_t)kTieMax) best = (uint32_t)b;
+          }
+        }
+        const uint32_t b0 = ~block_max_u32(~best, flag_scratch);    // the lowest over lanes
+        if (b0 != 0xFFFFFFFFu) {
+          const uint32_t t0 = prefix0 | (b0 << lo0);
+          uint32_t *tl = (uint32_t *)sh.hist;
+          const uint32_t nl = gather_keys(sv, [&](int u, uint32_t k) { return c[u] == cstar && k >= t0; }, cnt,
+                                          full, tl, (uint32_t)kTieMax, &sh.list_n);
+          if ((uint64_t)nl >= need && nl <= (uint32_t)kTieMax) {
+            r2 = list_select<true>(tl, (int)nl, need, sh.hist + kTieMax / 2, (uint32_t *)sh.scratch, sh.found);
+            done = true;
+          }
+        }
+      }
+      if (!done) {
+        // the prefix common to every score is common to the tied ones
+        auto in_tie = [&](int u) { return c[u] == cstar; };
+        r2 = reg_select<true, false>(sv, cnt, full, in_tie, one, need, 0, 1, s_and, s_or, sh);
+      }
+    }
     sstar = r2.key;
     need2 = need - r2.above;
     at2 = r2.at;
@@ -537,17 +761,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     const int t = opaque(tid);
 #pragma unroll
     for (int u = 0; u < kRegU; ++u) {
-      const bool k = lvl2 ? (c[u] > cstar || (c[u] == cstar && s[u] >= sstar)) : c[u] >= cstar;
+      const uint32_t x = sv(u);
+      const bool k = lvl2 ? ((c[u] > cstar) | ((c[u] == cstar) & (x >= sstar))) : c[u] >= cstar;
       KVS_FOR_VALID(u, kp[u * kStreamThreads + t] = k ? 1 : 0;)
     }
   } else {
     uint32_t tmask = 0;
 #pragma unroll
-    for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(u < cnt && c[u] == cstar && s[u] == sstar) << u;
+    for (int u = 0; u < kRegU; ++u) tmask |= (uint32_t)(valid(u) & (c[u] == cstar) & (sv(u) == sstar)) << u;
     rank_flags(tmask, rounds, (uint32_t *)sh.hist, flag_scratch, [&](int u, uint32_t rk) {
       const bool tie = (tmask >> u) & 1u;
-      const bool k = c[u] > cstar || (c[u] == cstar && (s[u] > sstar || (tie && rk < need2)));
-      if (u < cnt) kp[u * kStreamThreads + tid] = k ? 1 : 0;
+      const bool k = (c[u] > cstar) | ((c[u] == cstar) & ((sv(u) > sstar) | (tie & (rk < need2))));
+      if (valid(u)) kp[u * kStreamThreads + tid] = k ? 1 : 0;
     });
   }
 }
@@ -576,10 +801,29 @@ hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *sc
   a.b = b;
   a.num = num;
   a.den = den;
+  // the scores' LDS exceeds the default dynamic limit: raise it once per device
+  static std::mutex mu;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!attr_set[dev]) {
+      const void *fns[3] = {(const void *)stream_reg_kernel<true, true>, (const void *)stream_reg_kernel<true, false>,
+                            (const void *)stream_reg_kernel<false, true>};
+      for (const void *f : fns) {
+        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds);
+        if (e != hipSuccess) return e;
+      }
+      attr_set[dev] = true;
+    }
+  }
   dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
-  if (lrfu && select) stream_reg_kernel<true, true><<<grid, kStreamThreads, 0, st>>>(a);
-  else if (lrfu) stream_reg_kernel<true, false><<<grid, kStreamThreads, 0, st>>>(a);
-  else stream_reg_kernel<false, true><<<grid, kStreamThreads, 0, st>>>(a);
+  if (lrfu && select) stream_reg_kernel<true, true><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  else if (lrfu) stream_reg_kernel<true, false><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  else stream_reg_kernel<false, true><<<grid, kStreamThreads, kScoreLds, st>>>(a);
   return hipGetLastError();
 }
 
