@@ -710,6 +710,40 @@ def bench_kmeans(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+# Measured by the default invocation too (one child process each, before this process
+# touches the GPU), so that their figures come from the same run as the headline.
+OTHER_WORKLOADS = (("ragged64", 5), ("llama3_70b_128k", 5), ("ratchet", 1), ("decode_llama3_8b_32k", 20),
+                   ("token_confidence", 20), ("stepkv_llama3_8b_32k", 20), ("beacon_kmeans_llama3_70b", 5))
+
+
+def run_other_workloads() -> dict:
+    """One JSON summary per other workload, each from `bench.py --workload W` in a child
+    process (its own GPU memory, freed when it exits)."""
+    import subprocess
+    res = {}
+    for wname, steps in OTHER_WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", wname, "--no-cpu-baseline", "--no-others",
+               "--steps", str(steps), "--warmup", "1"]
+        t0 = time.perf_counter()
+        try:
+            p = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+            lines = [ln for ln in p.stdout.splitlines() if ln.startswith("{")]
+            if p.returncode == 0 and lines:
+                d = json.loads(lines[-1])
+                r = {k: d[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "dtype") if k in d}
+                if isinstance(d.get("roofline"), dict):
+                    r["roofline"] = {k: d["roofline"].get(k) for k in ("kernel", "bound", "achieved", "peak",
+                                                                          "unit", "frac")}
+                res[wname] = r
+            else:
+                res[wname] = {"error": f"exit status {p.returncode}", "stderr_tail": p.stderr[-400:]}
+        except subprocess.TimeoutExpired:
+            res[wname] = {"error": "timed out after 300 s"}
+        res[wname]["wall_s"] = round(time.perf_counter() - t0, 1)
+        print(f"[bench] {wname}: {json.dumps(res[wname])}", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -736,6 +770,10 @@ def main():
     ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
                     help="after timing, keep running full rounds for SECONDS (sustained rate, "
                          "e.g. for a power/clock sampler); reported under \"hold\"")
+    ap.add_argument("--no-others", action="store_true",
+                    help="the default run also measures the other workloads (ragged64, 70B, ratchet, "
+                         "decode, confidence, step-aware, k-means) in child processes and reports them "
+                         "under \"other_workloads\"; this skips that")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the eviction path "
@@ -758,6 +796,10 @@ def main():
     if args.workload == "ratchet":
         bench_ratchet(args)
         return
+    others = None
+    if (args.workload == "llama3_8b_32k" and not args.no_others and not args.no_cpu_baseline
+            and not args.separate and args.layer_chunks == 0 and not args.hold and not args.calibration_copy):
+        others = run_other_workloads()
     from workloads import ALL
     from workloads.host import make_layout, observers
     w = ALL[args.workload]
@@ -955,7 +997,7 @@ def main():
                     "bytes_per_launch": score_bytes, "mfma_tflops": score_tflops}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "llama3_8b_32k" else METRIC.replace("(8B shape, 32K ctx)", f"({w.name})"),
         "value": entries / (ms_per_step / 1000.0),
         "unit": "entries/s",
         "n_gpus": 1,
@@ -1053,6 +1095,8 @@ def main():
         del src, dst
     out["setup_s"] = {"oracle_leg": round(t_host, 2), "oracle_prep": round(ora["prep_s"], 2) if ora else None,
                       "device_fill_and_history": round(t_fill, 2), "settle_s": round(t_settle, 2)}
+    if others is not None:
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 
