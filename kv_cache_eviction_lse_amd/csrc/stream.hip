@@ -28,7 +28,8 @@ constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 32768 entrie
 constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kTieMax = 2 * kBins - 512;   // keys searched in an LDS list (plus 256 u64 bins) up to this many
+constexpr int kTieMax = 2 * kBins - 512;
+constexpr int kSmallTies = 256;   // tie classes at c* ranked pairwise up to this many   // keys searched in an LDS list (plus 256 u64 bins) up to this many
 static_assert(kRegU % 8 == 0, "the 8-row load groups tile the rows exactly");
 // LDS: the stream's scores (u32, slot-major) in dynamic shared memory, the rest static
 constexpr size_t kScoreLds = (size_t)kRegMaxLen * sizeof(uint32_t);
@@ -216,10 +217,11 @@ __device__ __forceinline__ Sel list_select(const uint32_t *key, int nt, uint64_t
 // them are in the list when it is at most cap (else some are missing).  Keys are read
 // 8 rows at a time and take is evaluated without branches, so the reads and the
 // atomics of a group overlap; groups of rows that every thread holds (u < full) skip
-// the row test.  Every thread of the block must call it.
+// the row test.  slots (optional) receives each key's slot u * 1024 + t at the same
+// position.  Every thread of the block must call it.
 template <typename KeyF, typename P>
 __device__ __forceinline__ uint32_t gather_keys(KeyF key, P take, int cnt, int full, uint32_t *list, uint32_t cap,
-                                                uint32_t *count) {
+                                                uint32_t *count, uint32_t *slots = nullptr) {
   if (threadIdx.x == 0) *count = 0;
   lds_barrier();
   const int lane = threadIdx.x & 63;
@@ -244,7 +246,10 @@ __device__ __forceinline__ uint32_t gather_keys(KeyF key, P take, int cnt, int f
     for (int v = 0; v < 8; ++v) {
       const uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)base[v]) +
                            (uint32_t)__popcll(m[v] & lanemask_lt());
-      if (((m[v] >> lane) & 1ull) && pos < cap) list[pos] = k[v];
+      if (((m[v] >> lane) & 1ull) && pos < cap) {
+        list[pos] = k[v];
+        if (slots) slots[pos] = (uint32_t)((u0 + v) * kStreamThreads) + threadIdx.x;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -686,6 +691,34 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   const uint32_t cstar = r1.key;
   const uint64_t need = K - r1.above;          // entries to keep among CRF == c*
   const bool lvl2 = need < r1.at;
+  if (lvl2 && r1.at <= (uint64_t)kSmallTies) {
+    // A small tie class at c*: its entries' scores and slots are gathered, and each one's
+    // rank in (s desc, slot asc) among them is counted directly, which settles the tied
+    // entries' keep bits without a radix search or a block-wide slot ranking.
+    if (!have_s) {
+      uint32_t tmp[8];
+      load_s(tmp, 8);
+    }
+    uint32_t *ls = (uint32_t *)sh.hist;
+    uint32_t *lslot = ls + kSmallTies;
+    const int nt = (int)gather_keys(sv, [&](int u, uint32_t) { return c[u] == cstar; }, cnt, full, ls,
+                                    (uint32_t)kSmallTies, &sh.list_n, lslot);
+    for (int x = tid; x < nt; x += kStreamThreads) {
+      const uint32_t sx = ls[x], qx = lslot[x];
+      uint32_t rank = 0;
+      for (int y = 0; y < nt; ++y) {
+        const uint32_t sy = ls[y];
+        rank += (sy > sx || (sy == sx && lslot[y] < qx)) ? 1u : 0u;
+      }
+      kp[qx] = rank < need ? 1 : 0;
+    }
+    const int t = opaque(tid);
+#pragma unroll
+    for (int u = 0; u < kRegU; ++u) {
+      KVS_FOR_VALID(u, if (c[u] != cstar) kp[u * kStreamThreads + t] = c[u] > cstar ? 1 : 0;)
+    }
+    return;
+  }
   uint32_t sstar = 0;
   uint64_t need2 = 0, at2 = 0;
   if (lvl2) {
