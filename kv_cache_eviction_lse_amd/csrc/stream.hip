@@ -695,22 +695,33 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
     // A small tie class at c*: its entries' scores and slots are gathered, and each one's
     // rank in (s desc, slot asc) among them is counted directly, which settles the tied
     // entries' keep bits without a radix search or a block-wide slot ranking.
-    if (!have_s) {
-      uint32_t tmp[8];
-      load_s(tmp, 8);
-    }
     uint32_t *ls = (uint32_t *)sh.hist;
     uint32_t *lslot = ls + kSmallTies;
-    const int nt = (int)gather_keys(sv, [&](int u, uint32_t) { return c[u] == cstar; }, cnt, full, ls,
+    const int nt = (int)gather_keys(cv, [&](int u, uint32_t) { return c[u] == cstar; }, cnt, full, ls,
                                     (uint32_t)kSmallTies, &sh.list_n, lslot);
-    for (int x = tid; x < nt; x += kStreamThreads) {
-      const uint32_t sx = ls[x], qx = lslot[x];
+    // their scores: from LDS when the cut loaded them, else straight from memory (only
+    // these few, not the whole stream)
+    for (int x = tid; x < nt; x += kStreamThreads) ls[x] = have_s ? s_lds[lslot[x]] : sp[lslot[x]];
+    lds_barrier();
+    {
+      // four threads per tied entry x, each counting a quarter of the list; lanes 4x..4x+3
+      // of a wave add their counts with two shuffles
+      static_assert(kSmallTies * 4 <= kStreamThreads, "four threads per tied entry");
+      const int x = tid >> 2, part = tid & 3;
+      const bool mine = x < nt;
+      const uint32_t sx = mine ? ls[x] : 0u, qx = mine ? lslot[x] : 0u;
+      const int y0 = part * (kSmallTies / 4), y1 = min(y0 + kSmallTies / 4, nt);
       uint32_t rank = 0;
-      for (int y = 0; y < nt; ++y) {
-        const uint32_t sy = ls[y];
-        rank += (sy > sx || (sy == sx && lslot[y] < qx)) ? 1u : 0u;
+      if (mine) {
+#pragma unroll 8
+        for (int y = y0; y < y1; ++y) {
+          const uint32_t sy = ls[y];
+          rank += (sy > sx || (sy == sx && lslot[y] < qx)) ? 1u : 0u;
+        }
       }
-      kp[qx] = rank < need ? 1 : 0;
+      rank += (uint32_t)__shfl_xor((int)rank, 1);
+      rank += (uint32_t)__shfl_xor((int)rank, 2);
+      if (mine && part == 0) kp[qx] = rank < need ? 1 : 0;
     }
     const int t = opaque(tid);
 #pragma unroll
@@ -724,8 +735,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   if (lvl2) {
     // The entries tied at c* are ranked by this round's s: v* of s over them.
     if (!have_s) {
-      uint32_t tmp[8];
-      load_s(tmp, 8);
+      uint32_t tmp[kRegU];      // every row's score in flight at once
+      load_s(tmp, kRegU);
       block_and_or(s_and, s_or, (uint32_t *)sh.scratch);
     }
     Sel r2;
