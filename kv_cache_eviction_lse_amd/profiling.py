@@ -115,9 +115,10 @@ def traffic(args) -> None:
             sys.exit(f"no copy kernel in the {counter} run")
         c_kib = max(copies)
         factor = copy_bytes / (c_kib * 1024.0)
-        # every kernel whose name holds one of the comma-separated substrings: the
-        # per-dispatch average of each, summed (one launch of each per call)
-        names = [k for k in per if any(x in k for x in kernel.split(","))]
+        # every kernel whose name holds one of the '|'-separated substrings (template
+        # names hold commas): the per-dispatch average of each, summed (one launch of
+        # each per call)
+        names = [k for k in per if any(x in k for x in kernel.split("|"))]
         if not names:
             sys.exit(f"no {kernel} dispatch in the {counter} run")
         s_kib = sum(sum(per[k]) / len(per[k]) for k in names)
@@ -281,7 +282,7 @@ def main() -> None:
     t.add_argument("--json", required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
     t.add_argument("--command", action="append", default=[])
-    t.add_argument("--kernel", default=SCORER, help="kernel name substring")
+    t.add_argument("--kernel", default=SCORER, help="kernel name substrings, separated by '|'")
     t.add_argument("--source", default="score.hip", help="csrc file the counters are tied to")
     t.add_argument("--workload", default="llama3_8b_32k")
     cp = sub.add_parser("compute")
