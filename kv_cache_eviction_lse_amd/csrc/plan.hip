@@ -64,15 +64,24 @@ __global__ __launch_bounds__(kStreamThreads) void plan_kernel(PlanArgs a, MoveAr
   }
   uint32_t ts = 0, td = 0;
   if (cap > 0 && cap <= a.P) {
-    // rounds of 1024 x 16 slots: thread t owns 16 consecutive slots of the round; one
-    // block scan per list and round gives every thread its starting ranks
-    constexpr int U = 16;
+    // rounds of 1024 x 32 slots (one round up to 32 768 entries): thread t owns 32
+    // consecutive slots of the round, read as two 16-byte loads when they are aligned;
+    // one block scan per list and round gives every thread its starting ranks
+    constexpr int U = 32;
     uint32_t base_s = 0, base_d = 0;
     for (int32_t r0 = 0; r0 < n; r0 += U * (int32_t)blockDim.x) {
       const int32_t j0 = r0 + (int32_t)threadIdx.x * U;
       uint8_t kv[U];
+      const uint8_t *kpj = kp + j0;
+      if (j0 + U <= n && ((uintptr_t)kpj & 15u) == 0) {
+        const uint4 w0 = *(const uint4 *)kpj, w1 = *(const uint4 *)(kpj + 16);
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int u = 0; u < U; ++u) kv[u] = (j0 + u < n) ? kp[j0 + u] : (uint8_t)0;
+        for (int u = 0; u < U; ++u) kv[u] = (uint8_t)(w[u >> 2] >> ((u & 3) * 8));
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) kv[u] = (j0 + u < n) ? kpj[u] : (uint8_t)0;
+      }
       uint32_t cs = 0, cd = 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(kStreamThreads) void plan_kernel(PlanArgs a, MoveAr
   if (c > (uint32_t)(cap > 0 ? cap : 0)) c = (uint32_t)(cap > 0 ? cap : 0);
   if (threadIdx.x == 0) a.pair_count[(int64_t)lg * a.b.S + i] = (int32_t)c;
   if (!MOVE || c == 0) return;
-  __syncthreads();   // pair lists and block-table row complete
+  lds_barrier();   // pair lists and block-table row complete (in LDS)
 
   const int32_t l = lg / a.b.Hkv;
   const int32_t g = lg - l * a.b.Hkv;
@@ -126,23 +135,22 @@ __global__ __launch_bounds__(kStreamThreads) void plan_kernel(PlanArgs a, MoveAr
   uint16_t *pool = kvsel ? m.v : m.k;
   const int ch = threadIdx.x & 15;
   const int32_t chunks = (int32_t)c * 32;
-  constexpr int kInFlight = 8;
+  // 16 chunks per thread in flight (every chunk of up to 512 pairs in one round trip);
+  // destinations are recomputed from the LDS lists at the stores, so only the data is
+  // held in registers meanwhile
+  constexpr int kInFlight = 16;
   for (int32_t x0 = 0; x0 < chunks; x0 += kInFlight * kStreamThreads) {
     uint4 buf[kInFlight];
-    int64_t dst_off[kInFlight];
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       const int32_t x = x0 + u * kStreamThreads + (int32_t)threadIdx.x;
-      dst_off[u] = -1;
-      if (x < chunks) {
-        const int32_t t = x >> 5;
-        buf[u] = *(const uint4 *)(pool + slot_elem(ls_src[t]) * kHeadDim + ch * 8);
-        dst_off[u] = slot_elem(ls_dst[t]) * kHeadDim + ch * 8;
-      }
+      if (x < chunks) buf[u] = *(const uint4 *)(pool + slot_elem(ls_src[x >> 5]) * kHeadDim + ch * 8);
     }
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u)
-      if (dst_off[u] >= 0) *(uint4 *)(pool + dst_off[u]) = buf[u];
+    for (int u = 0; u < kInFlight; ++u) {
+      const int32_t x = x0 + u * kStreamThreads + (int32_t)threadIdx.x;
+      if (x < chunks) *(uint4 *)(pool + slot_elem(ls_dst[x >> 5]) * kHeadDim + ch * 8) = buf[u];
+    }
   }
   for (int32_t t = threadIdx.x; t < (int32_t)c; t += kStreamThreads)
     m.crf[slot_elem(ls_dst[t])] = m.crf[slot_elem(ls_src[t])];
