@@ -926,6 +926,8 @@ def main():
             K.eviction_round(c, seqs, obs, bufs, decay, n_prev, scale, layer_chunks=chunks)
             evs[k][2].record(st)
             continue
+        # (a round ends where the next one's first event is recorded: each event record
+        # leaves the GPU idle for a few microseconds, so a round carries two, not three)
         evs[k][0].record(st)
         K.kvs_score(c, seqs, obs, scale, bufs.scores, bufs.workspace)
         evs[k][1].record(st)
@@ -937,11 +939,16 @@ def main():
         else:
             K.kvs_lrfu_select(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h, bufs.keep)
             K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
-        evs[k][2].record(st)
+        if k == args.steps - 1:
+            evs[k][2].record(st)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    round_ev = [a.elapsed_time(c_) for a, _, c_ in evs]
+    if chunks > 0:
+        round_ev = [a.elapsed_time(c_) for a, _, c_ in evs]
+    else:
+        round_ev = [evs[k][0].elapsed_time(evs[k + 1][0] if k + 1 < args.steps else evs[k][2])
+                    for k in range(args.steps)]
     if chunks > 0:
         # the dominant kernel's launch time, live with HIP events on its stream: the scorer
         # alone on the same inputs, as many launches as timed steps
