@@ -937,8 +937,8 @@ def main():
             K.kvs_plan(seqs, L, Hkv, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
             K.kvs_compact(c, seqs, bufs.budget_h, bufs.pairs, bufs.pair_count)
         else:
-            K.kvs_lrfu_select(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h, bufs.keep)
-            K.kvs_plan_compact(c, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs, bufs.pair_count)
+            K.kvs_lrfu_select_compact(c, seqs, bufs.scores, 9, 10, decay, n_prev, bufs.budget, bufs.budget_h,
+                                      bufs.keep, bufs.pairs, bufs.pair_count)
         if k == args.steps - 1:
             evs[k][2].record(st)
     torch.cuda.synchronize()

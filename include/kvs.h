@@ -351,11 +351,27 @@ kvs_status kvs_compact(const kvs_cache *cache, const kvs_seqs *seqs, const int32
                        const int32_t *pairs, const int32_t *pair_count, void *stream);
 
 /*
+ * kvs_lrfu_select_compact -- kvs_lrfu_select followed by kvs_plan_compact in one call, with
+ * the union of their arguments and validation, and the same results: hit (optional),
+ * keep, the updated CRF, pairs, pair_count, the host outputs, and the moved K/V rows and
+ * CRF values.  ActKV Dissected, Component 1 (the 90 % attention-mass cut, LRFU) and
+ * Summary (top-B per head), then Component 3 (the slot plan and the one-pass in-place
+ * move).  While every stream has at most 32 768 entries, one kernel workgroup per stream
+ * selects and plans it (the plan as soon as its keep set is written) and one further
+ * kernel moves all pairs; otherwise the two calls run in turn.  Errors as for the two
+ * calls; on error nothing is enqueued.
+ */
+kvs_status kvs_lrfu_select_compact(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
+                                   uint32_t mass_num, uint32_t mass_den, const float *decay, const int32_t *n_prev,
+                                   uint8_t *hit, const int32_t *budget, const int32_t *budget_h, uint8_t *keep,
+                                   int32_t *pairs, int32_t *pair_count, int32_t *shift_h, int32_t *new_start_h,
+                                   int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                                   int64_t *freed_count_h, void *stream);
+
+/*
  * kvs_plan_compact -- kvs_plan followed by kvs_compact in one call, with the union of
  * their arguments and validation, and the same results (pairs, pair_count, the host
- * outputs and the moved K/V rows and CRF values).  While every stream has at most
- * 8192 pairs and 8192 pages, one kernel plans and moves each stream, keeping the
- * stream's pairs and block-table row on chip; otherwise the two kernels run in turn.
+ * outputs and the moved K/V rows and CRF values).
  */
 kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const uint8_t *keep,
                             const int32_t *budget, const int32_t *budget_h, int32_t *pairs,

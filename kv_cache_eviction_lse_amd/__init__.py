@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     kvs_token_confidence_workspace_size, kvs_confidence_trend, KVS_DTYPE_F32, KVS_DTYPE_BF16,
     DecodeQueries, kvs_decode_workspace_size, kvs_decode_attention, StepSet, kvs_step_select_workspace_size,
     kvs_step_select, CacheShape, kvs_beacon_kmeans, kvs_beacon_seed, kvs_eviction_round,
-    kvs_token_confidence_static,
+    kvs_token_confidence_static, kvs_lrfu_select_compact,
 )
 from .round import RoundBuffers, eviction_round  # noqa: F401

@@ -27,7 +27,7 @@ EXPORTS = ("kvs_status_string", "kvs_last_error", "kvs_version", "kvs_score_work
            "kvs_token_confidence_workspace_size", "kvs_token_confidence", "kvs_confidence_trend",
            "kvs_decode_workspace_size", "kvs_decode_attention", "kvs_step_select_workspace_size",
            "kvs_step_select", "kvs_beacon_kmeans", "kvs_beacon_seed", "kvs_eviction_round",
-           "kvs_token_confidence_static")
+           "kvs_token_confidence_static", "kvs_lrfu_select_compact")
 
 KVS_DTYPE_F32, KVS_DTYPE_BF16 = 0, 1
 
@@ -101,6 +101,9 @@ def lib() -> C.CDLL:
         L.kvs_compact.argtypes = [P, P, P, P, P, P]
         L.kvs_plan_compact.restype = C.c_int
         L.kvs_plan_compact.argtypes = [P, P, P, P, P, P, P, P, P, P, P, C.c_int64, P, P]
+        L.kvs_lrfu_select_compact.restype = C.c_int
+        L.kvs_lrfu_select_compact.argtypes = [P, P, P, C.c_uint32, C.c_uint32, P, P, P, P, P, P, P, P, P, P, P, P,
+                                              C.c_int64, P, P]
         L.kvs_budget_ratchet.restype = C.c_int
         L.kvs_budget_ratchet.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
         L.kvs_decode_workspace_size.restype = C.c_size_t
@@ -326,6 +329,24 @@ def kvs_plan_compact(cache: PagedCache, seqs: SeqBatch, keep, budget, budget_h: 
     _check(lib().kvs_plan_compact(cache.ref, seqs.ref, _ptr(keep), _ptr(budget), _ptr(budget_h), _ptr(pairs),
                                   _ptr(pair_count), _ptr(shift), _ptr(new_start), _ptr(new_len), _ptr(freed),
                                   cap, _ptr(nfreed), _stream(stream)))
+    return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
+
+
+def kvs_lrfu_select_compact(cache: PagedCache, seqs: SeqBatch, scores, mass_num: int, mass_den: int, decay,
+                            n_prev, budget, budget_h: np.ndarray, keep, pairs, pair_count, hit=None,
+                            stream=None) -> PlanHost:
+    budget_h = np.ascontiguousarray(budget_h, np.int32)
+    S = seqs.num_seqs
+    shift = np.zeros(S, np.int32)
+    new_start = np.zeros(S, np.int32)
+    new_len = np.zeros(S, np.int32)
+    cap = int(seqs.block_table_h.size)
+    freed = np.zeros(max(cap, 1), np.int32)
+    nfreed = np.zeros(1, np.int64)
+    _check(lib().kvs_lrfu_select_compact(cache.ref, seqs.ref, _ptr(scores), mass_num, mass_den, _ptr(decay),
+                                         _ptr(n_prev), _ptr(hit), _ptr(budget), _ptr(budget_h), _ptr(keep),
+                                         _ptr(pairs), _ptr(pair_count), _ptr(shift), _ptr(new_start),
+                                         _ptr(new_len), _ptr(freed), cap, _ptr(nfreed), _stream(stream)))
     return PlanHost(shift, new_start, new_len, freed[:int(nfreed[0])].copy())
 
 

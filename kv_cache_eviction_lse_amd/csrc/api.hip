@@ -463,19 +463,48 @@ kvs_status kvs_plan_compact(const kvs_cache *cache, const kvs_seqs *seqs, const 
     return st;
   if (seqs->num_seqs == 0) return ok();
   const kvs::Batch b = make_batch(cache, seqs);
-  int32_t max_npages = 0;
-  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
-    const int32_t n = seqs->len_h[i];
-    const int32_t np = n == 0 ? 0 : (seqs->start_h[i] + n + kvs::kPage - 1) / kvs::kPage;
-    max_npages = np > max_npages ? np : max_npages;
-  }
-  if (kvs::plan_move_fits(P, max_npages))
-    return hip_status(kvs::launch_plan_move(*cache, b, keep, budget, pairs, pair_count, P, max_npages,
-                                            (hipStream_t)stream));
   hipError_t e = kvs::launch_plan(b, keep, budget, pairs, pair_count, P, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e);
   if (P == 0) return ok();
   return hip_status(kvs::launch_compact(*cache, b, pairs, pair_count, P, (hipStream_t)stream));
+}
+
+kvs_status kvs_lrfu_select_compact(const kvs_cache *cache, const kvs_seqs *seqs, const float *scores,
+                                   uint32_t mass_num, uint32_t mass_den, const float *decay, const int32_t *n_prev,
+                                   uint8_t *hit, const int32_t *budget, const int32_t *budget_h, uint8_t *keep,
+                                   int32_t *pairs, int32_t *pair_count, int32_t *shift_h, int32_t *new_start_h,
+                                   int32_t *new_len_h, int32_t *freed_h, int64_t freed_capacity,
+                                   int64_t *freed_count_h, void *stream) {
+  kvs_status st;
+  if ((st = check_cache(cache, true, true)) != KVS_OK) return st;
+  if ((st = check_seqs(seqs, cache->num_pages, true)) != KVS_OK) return st;
+  if (mass_den == 0 || mass_num > mass_den)
+    return fail(KVS_ERR_SHAPE, "mass fraction %u/%u must satisfy 0 <= num <= den, den > 0", mass_num, mass_den);
+  if (seqs->num_seqs > 0 && (!budget || !budget_h)) return fail(KVS_ERR_NULL, "budget is NULL");
+  for (int32_t i = 0; i < seqs->num_seqs; ++i)
+    if (budget_h[i] < 0) return fail(KVS_ERR_SHAPE, "budget[%d] = %d < 0", i, budget_h[i]);
+  const int64_t P = seqs->num_seqs ? pair_cap_of(seqs, budget_h) : 0;
+  if (seqs->num_seqs > 0 && (!keep || !pair_count || (P > 0 && !pairs)))
+    return fail(KVS_ERR_NULL, "keep/pairs/pair_count is NULL");
+  if ((st = kvs_plan_host(seqs, budget_h, shift_h, new_start_h, new_len_h, freed_h, freed_capacity,
+                          freed_count_h)) != KVS_OK)
+    return st;
+  if (seqs->num_seqs == 0) return ok();
+  const kvs::Batch b = make_batch(cache, seqs);
+  if (b.E > 0 && (!scores || !decay || !n_prev)) return fail(KVS_ERR_NULL, "scores/decay/n_prev is NULL");
+  if (b.E > 0 && kvs::stream_reg_fits(max_len_of(seqs), cache->num_pages, cache->num_kv_heads)) {
+    // selection and slot plan in one kernel, then the moves
+    hipError_t e = kvs::launch_stream_reg_plan(*cache, b, scores, mass_num, mass_den, decay, n_prev, hit, budget,
+                                               keep, pairs, pair_count, P, (hipStream_t)stream);
+    if (e != hipSuccess || P == 0) return hip_status(e);
+    return hip_status(kvs::launch_compact(*cache, b, pairs, pair_count, P, (hipStream_t)stream));
+  }
+  // otherwise the two calls in turn (the host outputs are already written)
+  if ((st = kvs_lrfu_select(cache, seqs, scores, mass_num, mass_den, decay, n_prev, hit, budget, budget_h, keep,
+                            stream)) != KVS_OK)
+    return st;
+  return kvs_plan_compact(cache, seqs, keep, budget, budget_h, pairs, pair_count, nullptr, nullptr, nullptr,
+                          nullptr, 0, nullptr, stream);
 }
 
 kvs_status kvs_budget_ratchet(int32_t *budget_h, const uint8_t *flag_h, int32_t num_seqs, int32_t num, int32_t den,
@@ -709,7 +738,7 @@ struct RoundArgs {
   uint8_t *hit, *keep;
   int32_t *pairs, *pair_count;
   int64_t pair_cap;
-  int32_t max_npages, max_len;
+  int32_t max_len;
   void *ws;
   size_t ws_bytes;
 };
@@ -743,16 +772,13 @@ hipError_t round_select_move(const RoundArgs &r, const kvs_seqs *seqs, hipStream
   const kvs::Batch b = make_batch(&r.cache, seqs);
   hipError_t e;
   if (kvs::stream_reg_fits(r.max_len, r.cache.num_pages, r.cache.num_kv_heads)) {
-    e = kvs::launch_stream_reg(r.cache, b, r.scores, true, true, r.mass_num, r.mass_den, r.decay, r.n_prev, r.hit,
-                               r.budget, r.keep, st);
+    e = kvs::launch_stream_reg_plan(r.cache, b, r.scores, r.mass_num, r.mass_den, r.decay, r.n_prev, r.hit,
+                                    r.budget, r.keep, r.pairs, r.pair_count, r.pair_cap, st);
   } else {
     e = kvs::launch_lrfu(r.cache, b, r.scores, r.mass_num, r.mass_den, r.decay, r.n_prev, r.hit, r.max_len, st);
     if (e == hipSuccess) e = kvs::launch_select(r.cache, b, r.scores, r.budget, r.keep, r.max_len, st);
+    if (e == hipSuccess) e = kvs::launch_plan(b, r.keep, r.budget, r.pairs, r.pair_count, r.pair_cap, st);
   }
-  if (e != hipSuccess) return e;
-  if (kvs::plan_move_fits(r.pair_cap, r.max_npages))
-    return kvs::launch_plan_move(r.cache, b, r.keep, r.budget, r.pairs, r.pair_count, r.pair_cap, r.max_npages, st);
-  e = kvs::launch_plan(b, r.keep, r.budget, r.pairs, r.pair_count, r.pair_cap, st);
   if (e != hipSuccess || r.pair_cap == 0) return e;
   return kvs::launch_compact(r.cache, b, r.pairs, r.pair_count, r.pair_cap, st);
 }
@@ -807,11 +833,6 @@ kvs_status kvs_eviction_round(const kvs_cache *cache, const kvs_seqs *seqs, cons
   r.pair_count = pair_count;
   r.pair_cap = P;
   r.max_len = max_len_of(seqs);
-  for (int32_t i = 0; i < seqs->num_seqs; ++i) {
-    const int32_t n = seqs->len_h[i];
-    const int32_t np = n == 0 ? 0 : (seqs->start_h[i] + n + kvs::kPage - 1) / kvs::kPage;
-    r.max_npages = np > r.max_npages ? np : r.max_npages;
-  }
   r.ws = workspace;
   r.ws_bytes = workspace_bytes;
   const hipStream_t main = (hipStream_t)stream;

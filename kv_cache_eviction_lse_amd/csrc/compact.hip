@@ -2,15 +2,17 @@
 //
 // ActKV Dissected, Component 3: all planned pairs are copied in one parallel pass,
 // with no extra KV buffer.  Sources and destinations are disjoint, so there is no
-// ordering between pairs.  A workgroup moves 64 pairs of one stream: 64 pairs x
-// (K row + V row) = 2048 chunks of 16 bytes, 8 per thread, all loads issued before
-// the stores; the first 64 threads also move the pairs' CRF values.
+// ordering between pairs.  A workgroup moves 8 pairs of one stream: 8 pairs x (K row +
+// V row) = 256 chunks of 16 bytes, one per thread; the thread at the start of each
+// pair's 32 also moves the pair's CRF value.  One chunk per thread over many small
+// workgroups keeps reads and writes interleaved across the chip: the same rows moved
+// with 8 or 16 chunks per thread (all loads before the stores) take 1.4-1.6x longer.
 #include "kvs_device.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kPairsPerBlock = 64;
+constexpr int kPairsPerBlock = 8;
 constexpr int kMoveThreads = 256;
 
 struct CompactArgs {
@@ -31,54 +33,33 @@ __device__ __forceinline__ int64_t row_elem(const CompactArgs &a, const int32_t 
 }
 
 __global__ __launch_bounds__(kMoveThreads) void compact_kernel(CompactArgs a) {
+  static_assert(kPairsPerBlock * 32 == kMoveThreads, "one 16-byte chunk per thread");
   const int32_t i = blockIdx.z;
   const int32_t lg = blockIdx.y;
   const int32_t cnt = a.pair_count[(int64_t)lg * a.b.S + i];
-  const int32_t p0 = blockIdx.x * kPairsPerBlock;
-  if (p0 >= cnt || cnt > a.P) return;
+  const int32_t t = (int32_t)blockIdx.x * kPairsPerBlock + (int32_t)(threadIdx.x >> 5);
+  if (t >= cnt || cnt > a.P) return;
   const int32_t l = lg / a.b.Hkv;
   const int32_t g = lg - l * a.b.Hkv;
   const int32_t start = a.b.start[i];
   const int32_t n = a.b.len[i];
   const int32_t *bt_row = a.b.bt + (int64_t)i * a.b.max_pages;
   const int32_t *pp = a.pairs + (((int64_t)lg * a.b.S + i) * a.P) * 2;
-
-  // chunk c = threadIdx.x + 256u: pair c / 32, row half (K or V) (c / 16) % 2, 16-byte
-  // piece c % 16; the K/V choice is the same for every u of a thread
-  const int kv = (threadIdx.x >> 4) & 1;
-  uint16_t *pool = kv ? a.v : a.k;
+  const int32_t src = pp[2 * t];
+  const int32_t dst = pp[2 * t + 1];
+  if (src < 0 || src >= n || dst < 0 || dst >= n) return;
+  const int64_t se = row_elem(a, bt_row, start, src, l, g);
+  const int64_t de = row_elem(a, bt_row, start, dst, l, g);
+  // chunk = pair (threadIdx / 32), row half (K or V) (threadIdx / 16) % 2, 16-byte piece
+  // threadIdx % 16
+  uint16_t *pool = ((threadIdx.x >> 4) & 1) ? a.v : a.k;
   const int ch = threadIdx.x & 15;
-  uint4 buf[8];
-  int64_t dst_off[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int32_t t = p0 + ((threadIdx.x + u * kMoveThreads) >> 5);
-    dst_off[u] = -1;
-    if (t < cnt) {
-      const int32_t src = pp[2 * t];
-      const int32_t dst = pp[2 * t + 1];
-      if (src < 0 || src >= n || dst < 0 || dst >= n) continue;
-      buf[u] = *(const uint4 *)(pool + row_elem(a, bt_row, start, src, l, g) * kHeadDim + ch * 8);
-      dst_off[u] = row_elem(a, bt_row, start, dst, l, g) * kHeadDim + ch * 8;
-    }
-  }
+  const uint4 x = *(const uint4 *)(pool + se * kHeadDim + ch * 8);
+  const bool lead = (threadIdx.x & 31) == 0;
   float cval = 0.f;
-  int64_t cdst = -1;
-  if (threadIdx.x < kPairsPerBlock) {
-    const int32_t t = p0 + threadIdx.x;
-    if (t < cnt) {
-      const int32_t src = pp[2 * t];
-      const int32_t dst = pp[2 * t + 1];
-      if (src >= 0 && src < n && dst >= 0 && dst < n) {
-        cval = a.crf[row_elem(a, bt_row, start, src, l, g)];
-        cdst = row_elem(a, bt_row, start, dst, l, g);
-      }
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (dst_off[u] >= 0) *(uint4 *)(pool + dst_off[u]) = buf[u];
-  if (cdst >= 0) a.crf[cdst] = cval;
+  if (lead) cval = a.crf[se];
+  *(uint4 *)(pool + de * kHeadDim + ch * 8) = x;
+  if (lead) a.crf[de] = cval;
 }
 
 }  // namespace

@@ -166,6 +166,65 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t &t
   return before + incl - x;
 }
 
+// The slot plan of one stream from its keep bytes kp[0..n) with K kept (ActKV
+// Dissected, Component 3: survivors skew toward the tail, so the tail is the target
+// region).  With D = n - K the sources are the kept slots below D and the destinations
+// the evicted slots from D on, both ascending; pair t = (source t, destination t) goes
+// to pp[2t], pp[2t + 1] for t < min(D, K), so a keep mask with the wrong count cannot
+// overrun.  Returns the pair count, min(#sources, #destinations, D, K), in every
+// thread.  Slots go in rounds of blockDim x 32: thread t owns 32 consecutive slots of a
+// round, read as two 16-byte loads when aligned, and one block scan per list and round
+// gives its starting ranks.  sc1, sc2: kStreamWaves words of LDS each.  Every thread of
+// the block must call it.
+__device__ __forceinline__ uint32_t plan_slots(const uint8_t *kp, int32_t n, int32_t K, int32_t *pp, uint32_t *sc1,
+                                               uint32_t *sc2) {
+  const int32_t D = n - K;
+  const int32_t cap = D < K ? D : K;
+  if (cap <= 0) return 0u;
+  constexpr int U = 32;
+  uint32_t base_s = 0, base_d = 0;
+  for (int32_t r0 = 0; r0 < n; r0 += U * (int32_t)blockDim.x) {
+    const int32_t j0 = r0 + (int32_t)threadIdx.x * U;
+    uint8_t kv[U];
+    const uint8_t *kpj = kp + j0;
+    if (j0 + U <= n && ((uintptr_t)kpj & 15u) == 0) {
+      const uint4 w0 = *(const uint4 *)kpj, w1 = *(const uint4 *)(kpj + 16);
+      const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int u = 0; u < U; ++u) kv[u] = (uint8_t)(w[u >> 2] >> ((u & 3) * 8));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) kv[u] = (j0 + u < n) ? kpj[u] : (uint8_t)0;
+    }
+    uint32_t cs = 0, cd = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t j = j0 + u;
+      cs += (j < n && j < D && kv[u]) ? 1u : 0u;
+      cd += (j < n && j >= D && !kv[u]) ? 1u : 0u;
+    }
+    uint32_t rts, rtd;
+    uint32_t rs = base_s + block_exclusive_scan(cs, rts, sc1);
+    uint32_t rd = base_d + block_exclusive_scan(cd, rtd, sc2);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t j = j0 + u;
+      if (j >= n) continue;
+      if (j < D && kv[u]) {
+        if (rs < (uint32_t)cap) pp[(int64_t)rs * 2] = j;
+        ++rs;
+      } else if (j >= D && !kv[u]) {
+        if (rd < (uint32_t)cap) pp[(int64_t)rd * 2 + 1] = j;
+        ++rd;
+      }
+    }
+    base_s += rts;
+    base_d += rtd;
+  }
+  uint32_t c = base_s < base_d ? base_s : base_d;
+  return c < (uint32_t)cap ? c : (uint32_t)cap;
+}
+
 // Exclusive rank of this thread's flag among all flags of the block in thread order,
 // plus the block total.  One barrier pair.
 __device__ __forceinline__ uint32_t block_flag_rank(bool flag, uint32_t &total, uint32_t *scratch) {

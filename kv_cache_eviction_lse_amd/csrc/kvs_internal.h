@@ -51,6 +51,12 @@ hipError_t launch_select(const kvs_cache &c, const Batch &b, const float *scores
                          const float *keys = nullptr);
 
 // Register-resident cut + LRFU and/or top-B for streams of at most 32768 entries.
+// launch_stream_reg_plan: the fused cut, LRFU update and keep set, then the slot plan
+// (pairs, pair counts) in the same workgroup.
+hipError_t launch_stream_reg_plan(const kvs_cache &c, const Batch &b, const float *scores, uint32_t num,
+                                  uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
+                                  const int32_t *budget, uint8_t *keep, int32_t *pairs, int32_t *pair_count,
+                                  int64_t pair_cap, hipStream_t st);
 bool stream_reg_fits(int32_t max_len, int64_t num_pages, int32_t Hkv);
 hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *scores, bool lrfu, bool select,
                              uint32_t num, uint32_t den, const float *decay, const int32_t *n_prev,
@@ -60,11 +66,6 @@ hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *sc
 hipError_t launch_plan(const Batch &b, const uint8_t *keep, const int32_t *budget, int32_t *pairs,
                        int32_t *pair_count, int64_t pair_cap, hipStream_t st);
 
-// Plan and move in one kernel for streams of at most 8192 pairs and 8192 pages.
-bool plan_move_fits(int64_t pair_cap, int32_t max_npages);
-hipError_t launch_plan_move(const kvs_cache &c, const Batch &b, const uint8_t *keep, const int32_t *budget,
-                            int32_t *pairs, int32_t *pair_count, int64_t pair_cap, int32_t max_npages,
-                            hipStream_t st);
 
 hipError_t launch_compact(const kvs_cache &c, const Batch &b, const int32_t *pairs,
                           const int32_t *pair_count, int64_t pair_cap, hipStream_t st);

@@ -28,8 +28,8 @@ constexpr int32_t kRegMaxLen = kRegU * kStreamThreads;           // 32768 entrie
 constexpr int kRegBtCap = (kRegMaxLen + 2 * kPage - 2) / kPage;  // pages of a stream (start < 16)
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kTieMax = 2 * kBins - 512;
-constexpr int kSmallTies = 256;   // tie classes at c* ranked pairwise up to this many   // keys searched in an LDS list (plus 256 u64 bins) up to this many
+constexpr int kTieMax = 2 * kBins - 512;   // keys searched in an LDS list (plus 256 u64 bins) up to this many
+constexpr int kSmallTies = 256;            // tie classes at c* ranked pairwise up to this many
 static_assert(kRegU % 8 == 0, "the 8-row load groups tile the rows exactly");
 // LDS: the stream's scores (u32, slot-major) in dynamic shared memory, the rest static
 constexpr size_t kScoreLds = (size_t)kRegMaxLen * sizeof(uint32_t);
@@ -47,6 +47,10 @@ struct StreamArgs {
   const float *keys;     // nullable: top-B keys per entry [L*Hkv][E] in place of the CRF
   Batch b;
   uint32_t num, den;
+  // PLAN: the slot plan of kvs_plan, in the same workgroup
+  int32_t *pairs;        // [L*Hkv][S][P][2]
+  int32_t *pair_count;   // [L*Hkv][S]
+  int64_t P;
 };
 
 struct RegShared {
@@ -444,6 +448,23 @@ __device__ __forceinline__ Sel reg_select(KeyF key, int cnt, int full, CandF can
   return r;
 }
 
+// The slot plan of one stream once its keep set is written (kvs_plan, in the
+// selection's workgroup): plan_slots over the keep bytes, re-read after a full barrier
+// so that this workgroup's stores are visible to all of it.  The moves are a kernel of
+// their own, which spreads each stream's pairs over many small workgroups.
+__device__ __forceinline__ void plan_pairs(const StreamArgs &a, int32_t K, RegShared &sh, uint32_t *flag_scratch,
+                                           int32_t i, int32_t lg, int32_t n) {
+  const int64_t pc = (int64_t)lg * a.b.S + i;
+  const int32_t D = n - K;
+  uint32_t c = 0;
+  if ((D < K ? D : K) > 0) {
+    __syncthreads();
+    c = plan_slots(a.keep + (int64_t)lg * a.b.E + a.b.entry_off[i], n, K, a.pairs + pc * a.P * 2, flag_scratch,
+                   (uint32_t *)sh.scratch);
+  }
+  if (threadIdx.x == 0) a.pair_count[pc] = (int32_t)c;
+}
+
 // Stores for slot rows: rows u < full exist in every thread (uniform branch); the
 // partial row after them is predicated per lane.
 #define KVS_FOR_VALID(u, ...)   \
@@ -453,8 +474,9 @@ __device__ __forceinline__ Sel reg_select(KeyF key, int cnt, int full, CandF can
     __VA_ARGS__                 \
   }
 
-template <bool LRFU, bool SELECT>
+template <bool LRFU, bool SELECT, bool PLAN>
 __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a) {
+  static_assert(!PLAN || (LRFU && SELECT), "the plan follows the fused cut, update and keep set");
   __shared__ int32_t bt_lds[kRegBtCap];
   __shared__ RegShared sh;
   __shared__ uint32_t flag_scratch[kStreamWaves];
@@ -463,7 +485,10 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   const int32_t i = blockIdx.y;
   const int32_t lg = blockIdx.x;
   const int32_t n = a.b.len[i];
-  if (n <= 0) return;
+  if (n <= 0) {
+    if (PLAN && threadIdx.x == 0) a.pair_count[(int64_t)lg * a.b.S + i] = 0;
+    return;
+  }
   const int32_t l = lg / a.b.Hkv;
   const int32_t g = lg - l * a.b.Hkv;
   const int64_t e0 = a.b.entry_off[i];
@@ -550,6 +575,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
   lds_barrier();   // block-table slice visible
 
   uint32_t cmx = 0, ncm = 0;   // this thread's largest CRF (or key) and its count
+  // (the cut, the LRFU update and the keep set; each exit of the selection returns from
+  // this lambda, after which PLAN writes the stream's slot plan)
+  auto select_body = [&]() __attribute__((always_inline)) {
   if (LRFU) {
     // (c carries the scores on their way to LDS)
     load_s(c, kRegU);
@@ -819,6 +847,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
       if (valid(u)) kp[u * kStreamThreads + tid] = k ? 1 : 0;
     });
   }
+  };
+  select_body();
+  if constexpr (PLAN) plan_pairs(a, K, sh, flag_scratch, i, lg, n);
 }
 
 #undef KVS_FOR_VALID
@@ -827,6 +858,58 @@ __global__ __launch_bounds__(kStreamThreads) void stream_reg_kernel(StreamArgs a
 
 bool stream_reg_fits(int32_t max_len, int64_t num_pages, int32_t Hkv) {
   return max_len <= kRegMaxLen && num_pages * Hkv * kPage < (int64_t(1) << 31);
+}
+
+namespace {
+
+// the scores' LDS exceeds the default dynamic limit: raise it once per device
+hipError_t stream_reg_attrs() {
+  static std::mutex mu;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!attr_set[dev]) {
+    const void *fns[4] = {(const void *)stream_reg_kernel<true, true, false>,
+                          (const void *)stream_reg_kernel<true, false, false>,
+                          (const void *)stream_reg_kernel<false, true, false>,
+                          (const void *)stream_reg_kernel<true, true, true>};
+    for (const void *f : fns) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds);
+      if (e != hipSuccess) return e;
+    }
+    attr_set[dev] = true;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_stream_reg_plan(const kvs_cache &c, const Batch &b, const float *scores, uint32_t num,
+                                  uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
+                                  const int32_t *budget, uint8_t *keep, int32_t *pairs, int32_t *pair_count,
+                                  int64_t pair_cap, hipStream_t st) {
+  StreamArgs a{};
+  a.scores = scores;
+  a.crf = c.crf;
+  a.hit = hit;
+  a.decay = decay;
+  a.n_prev = n_prev;
+  a.budget = budget;
+  a.keep = keep;
+  a.b = b;
+  a.num = num;
+  a.den = den;
+  a.pairs = pairs;
+  a.pair_count = pair_count;
+  a.P = pair_cap;
+  hipError_t e = stream_reg_attrs();
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
+  stream_reg_kernel<true, true, true><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *scores, bool lrfu, bool select,
@@ -845,29 +928,12 @@ hipError_t launch_stream_reg(const kvs_cache &c, const Batch &b, const float *sc
   a.b = b;
   a.num = num;
   a.den = den;
-  // the scores' LDS exceeds the default dynamic limit: raise it once per device
-  static std::mutex mu;
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = stream_reg_attrs();
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (!attr_set[dev]) {
-      const void *fns[3] = {(const void *)stream_reg_kernel<true, true>, (const void *)stream_reg_kernel<true, false>,
-                            (const void *)stream_reg_kernel<false, true>};
-      for (const void *f : fns) {
-        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds);
-        if (e != hipSuccess) return e;
-      }
-      attr_set[dev] = true;
-    }
-  }
   dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
-  if (lrfu && select) stream_reg_kernel<true, true><<<grid, kStreamThreads, kScoreLds, st>>>(a);
-  else if (lrfu) stream_reg_kernel<true, false><<<grid, kStreamThreads, kScoreLds, st>>>(a);
-  else stream_reg_kernel<false, true><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  if (lrfu && select) stream_reg_kernel<true, true, false><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  else if (lrfu) stream_reg_kernel<true, false, false><<<grid, kStreamThreads, kScoreLds, st>>>(a);
+  else stream_reg_kernel<false, true, false><<<grid, kStreamThreads, kScoreLds, st>>>(a);
   return hipGetLastError();
 }
 

@@ -116,6 +116,30 @@ def test_lrfu_select_validation():
     assert status(L.kvs_select(C.byref(c), C.byref(seqs.s), FAKE, FAKE, bud.ctypes.data, FAKE, None)) == "KVS_ERR_SHAPE"
 
 
+def test_lrfu_select_compact_validation():
+    L = K.lib()
+    seqs = HostSeqs([[0, 1]], [3], [20])
+    c = _cache()
+    bud = np.array([8], np.int32)
+    z = np.zeros(4, np.int32)
+    n64 = np.zeros(1, np.int64)
+    # hit, budget, budget_h (host), keep, pairs, pair_count, then the host plan outputs
+    args = (FAKE, FAKE, bud.ctypes.data, FAKE, FAKE, FAKE, z.ctypes.data, z.ctypes.data, z.ctypes.data,
+            z.ctypes.data, 4, n64.ctypes.data, None)
+    assert status(L.kvs_lrfu_select_compact(C.byref(c), C.byref(seqs.s), FAKE, 11, 10, FAKE, FAKE, *args)) \
+        == "KVS_ERR_SHAPE"
+    assert status(L.kvs_lrfu_select_compact(C.byref(c), C.byref(seqs.s), FAKE, 9, 0, FAKE, FAKE, *args)) \
+        == "KVS_ERR_SHAPE"
+    assert status(L.kvs_lrfu_select_compact(None, C.byref(seqs.s), FAKE, 9, 10, FAKE, FAKE, *args)) \
+        == "KVS_ERR_NULL"
+    assert status(L.kvs_lrfu_select_compact(C.byref(_cache(crf=0)), C.byref(seqs.s), FAKE, 9, 10, FAKE, FAKE,
+                                            *args)) == "KVS_ERR_NULL"
+    neg = np.array([-1], np.int32)
+    args_neg = (FAKE, FAKE, neg.ctypes.data) + args[3:]
+    assert status(L.kvs_lrfu_select_compact(C.byref(c), C.byref(seqs.s), FAKE, 9, 10, FAKE, FAKE, *args_neg)) \
+        == "KVS_ERR_SHAPE"
+
+
 def test_lrfu_decay_matches_oracle():
     for lam in (0.5, 0.0, 0.25, 1.0):
         for dt in range(0, 130):
