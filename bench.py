@@ -5,7 +5,7 @@ A step is one full round over the Llama-3-8B-shaped cache (32 layers x 8 KV head
 32 query heads, 32,768 live entries per stream in 16-token pages scattered over a
 4,096-page pool, 64 observers per sequence, budget 512):
 
-    kvs_score -> kvs_lrfu_select -> kvs_plan_compact
+    kvs_score -> kvs_lrfu_select_compact
     (with --separate: kvs_score -> kvs_lrfu_update -> kvs_select -> kvs_plan -> kvs_compact)
 
 all enqueued on one stream with inputs resident in HBM.  Every step re-runs the
@@ -529,10 +529,8 @@ def bench_ratchet(args) -> None:
             ev[0].record(st)
             K.kvs_score(lp.cache, seqs, obs, lp.w.scale, bufs.scores, bufs.workspace)
             ev[1].record(st)
-            K.kvs_lrfu_select(lp.cache, seqs, bufs.scores, 9, 10, lp.decay, n_prev_t, bufs.budget, bufs.budget_h,
-                              bufs.keep)
-            plan = K.kvs_plan_compact(lp.cache, seqs, bufs.keep, bufs.budget, bufs.budget_h, bufs.pairs,
-                                      bufs.pair_count)
+            plan = K.kvs_lrfu_select_compact(lp.cache, seqs, bufs.scores, 9, 10, lp.decay, n_prev_t, bufs.budget,
+                                             bufs.budget_h, bufs.keep, bufs.pairs, bufs.pair_count)
             ev[2].record(st)
             torch.cuda.synchronize()
             t_round.append(ev[0].elapsed_time(ev[2]))
@@ -555,7 +553,7 @@ def bench_ratchet(args) -> None:
                    "prefill": 8192, "append_per_round": APPEND, "observers": OBS, "rounds": R,
                    "timed_rounds": len(t_round), "flags": args.flags, "budget_start": 512,
                    "budget_final": lp.budget, "budget_expansions": expansions,
-                   "timing": "HIP events around each round's kvs_score -> kvs_lrfu_select -> kvs_plan_compact; "
+                   "timing": "HIP events around each round's kvs_score -> kvs_lrfu_select_compact; "
                              "appends, observers and their LSE are prepared between rounds, untimed; "
                              "value = sum of entries / sum of round times"},
         "hbm_gbps": req_bytes / (ms_round / 1000.0) / 1e9,
