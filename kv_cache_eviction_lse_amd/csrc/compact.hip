@@ -36,17 +36,21 @@ __global__ __launch_bounds__(kMoveThreads) void compact_kernel(CompactArgs a) {
   static_assert(kPairsPerBlock * 32 == kMoveThreads, "one 16-byte chunk per thread");
   const int32_t i = blockIdx.z;
   const int32_t lg = blockIdx.y;
-  const int32_t cnt = a.pair_count[(int64_t)lg * a.b.S + i];
   const int32_t t = (int32_t)blockIdx.x * kPairsPerBlock + (int32_t)(threadIdx.x >> 5);
+  if (t >= a.P) return;   // (the grid rounds P up to whole workgroups)
+  const int64_t pc = (int64_t)lg * a.b.S + i;
+  // the pair is read together with the count (slot t < P is in the buffer whatever the
+  // count), so the row addresses wait on one round trip instead of two
+  const int2 pr = *(const int2 *)(a.pairs + (pc * a.P + t) * 2);
+  const int32_t cnt = a.pair_count[pc];
   if (t >= cnt || cnt > a.P) return;
   const int32_t l = lg / a.b.Hkv;
   const int32_t g = lg - l * a.b.Hkv;
   const int32_t start = a.b.start[i];
   const int32_t n = a.b.len[i];
   const int32_t *bt_row = a.b.bt + (int64_t)i * a.b.max_pages;
-  const int32_t *pp = a.pairs + (((int64_t)lg * a.b.S + i) * a.P) * 2;
-  const int32_t src = pp[2 * t];
-  const int32_t dst = pp[2 * t + 1];
+  const int32_t src = pr.x;
+  const int32_t dst = pr.y;
   if (src < 0 || src >= n || dst < 0 || dst >= n) return;
   const int64_t se = row_elem(a, bt_row, start, src, l, g);
   const int64_t de = row_elem(a, bt_row, start, dst, l, g);

@@ -5,9 +5,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kvs.h"
 
 namespace kvs {
+
+// Raises the dynamic-LDS limit of the n kernels in fns to `bytes`.  The attribute belongs
+// to a device, so it is set once per device (the current one), under a lock; `done`
+// holds one flag per device for this group of kernels.
+inline hipError_t raise_lds_limit(const void *const *fns, int n, int bytes, bool (&done)[64]) {
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return hipSuccess;
+  for (int k = 0; k < n; ++k) {
+    e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  done[dev] = true;
+  return hipSuccess;
+}
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;

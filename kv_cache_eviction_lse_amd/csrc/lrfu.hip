@@ -160,15 +160,12 @@ __global__ __launch_bounds__(kStreamThreads) void lrfu_kernel(LrfuArgs a) {
 hipError_t launch_lrfu(const kvs_cache &c, const Batch &b, const float *scores, uint32_t num,
                        uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
                        int32_t max_len, hipStream_t st) {
-  static bool attr_set = false;
   const int32_t cache = max_len <= kCacheCap ? max_len : 0;
   const size_t dyn = ((size_t)cache + kBtCap) * sizeof(uint32_t);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)lrfu_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (kCacheCap + kBtCap) * 4);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool done[64] = {};
+  const void *fn = (const void *)lrfu_kernel;
+  const hipError_t e = raise_lds_limit(&fn, 1, (kCacheCap + kBtCap) * 4, done);
+  if (e != hipSuccess) return e;
   LrfuArgs a{};
   a.scores = scores;
   a.crf = c.crf;

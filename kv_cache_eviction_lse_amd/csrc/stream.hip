@@ -17,7 +17,6 @@
 // Selection: radix search on the key bits below the candidates' common prefix (from
 // the AND and OR of their keys), 12 bits per pass, with a 4096-bin LDS histogram of
 // counts or of integer masses; the crossing bin is found with one block-wide scan.
-#include <mutex>
 
 #include "kvs_device.h"
 
@@ -864,25 +863,12 @@ namespace {
 
 // the scores' LDS exceeds the default dynamic limit: raise it once per device
 hipError_t stream_reg_attrs() {
-  static std::mutex mu;
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!attr_set[dev]) {
-    const void *fns[4] = {(const void *)stream_reg_kernel<true, true, false>,
-                          (const void *)stream_reg_kernel<true, false, false>,
-                          (const void *)stream_reg_kernel<false, true, false>,
-                          (const void *)stream_reg_kernel<true, true, true>};
-    for (const void *f : fns) {
-      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds);
-      if (e != hipSuccess) return e;
-    }
-    attr_set[dev] = true;
-  }
-  return hipSuccess;
+  static bool done[64] = {};
+  const void *fns[4] = {(const void *)stream_reg_kernel<true, true, false>,
+                        (const void *)stream_reg_kernel<true, false, false>,
+                        (const void *)stream_reg_kernel<false, true, false>,
+                        (const void *)stream_reg_kernel<true, true, true>};
+  return raise_lds_limit(fns, 4, (int)kScoreLds, done);
 }
 
 }  // namespace
