@@ -32,7 +32,7 @@ struct LrfuArgs {
 };
 
 constexpr int kU = 16;             // loads in flight per thread in the streaming passes
-constexpr int kBtCap = 4096;
+constexpr int kBtCap = 16384;      // block-table entries per stream kept in LDS
 constexpr int kCacheCap = 35 * 1024;
 
 __global__ __launch_bounds__(kStreamThreads) void lrfu_kernel(LrfuArgs a) {
@@ -160,11 +160,17 @@ __global__ __launch_bounds__(kStreamThreads) void lrfu_kernel(LrfuArgs a) {
 hipError_t launch_lrfu(const kvs_cache &c, const Batch &b, const float *scores, uint32_t num,
                        uint32_t den, const float *decay, const int32_t *n_prev, uint8_t *hit,
                        int32_t max_len, hipStream_t st) {
+  // LDS: the scores (streams up to kCacheCap entries), then the block-table row when it
+  // fits in what is left of 156 KiB
+  constexpr int32_t kLdsWords = 156 * 1024 / 4;
   const int32_t cache = max_len <= kCacheCap ? max_len : 0;
-  const size_t dyn = ((size_t)cache + kBtCap) * sizeof(uint32_t);
+  int32_t bt = max_len / kPage + 2;       // pages of a stream of max_len entries at any start
+  if (bt > kBtCap) bt = kBtCap;
+  if (cache + bt > kLdsWords) bt = kLdsWords - cache;
+  const size_t dyn = ((size_t)cache + (size_t)bt) * sizeof(uint32_t);
   static bool done[64] = {};
   const void *fn = (const void *)lrfu_kernel;
-  const hipError_t e = raise_lds_limit(&fn, 1, (kCacheCap + kBtCap) * 4, done);
+  const hipError_t e = raise_lds_limit(&fn, 1, kLdsWords * 4, done);
   if (e != hipSuccess) return e;
   LrfuArgs a{};
   a.scores = scores;
@@ -176,7 +182,7 @@ hipError_t launch_lrfu(const kvs_cache &c, const Batch &b, const float *scores, 
   a.num = num;
   a.den = den;
   a.cache_cap = cache;
-  a.bt_cap = kBtCap;
+  a.bt_cap = bt;
   dim3 grid((unsigned)(b.L * b.Hkv), (unsigned)b.S);
   lrfu_kernel<<<grid, kStreamThreads, dyn, st>>>(a);
   return hipGetLastError();
