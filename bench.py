@@ -137,7 +137,7 @@ def score_kernels(w, lay) -> str:
     names = set()
     for O in lay.obs.tolist():
         R = O * G
-        if O < 16:
+        if R < 16:
             names.add("score_valu_kernel")
         elif R <= 128:
             names.add("score_mfma_kernel")

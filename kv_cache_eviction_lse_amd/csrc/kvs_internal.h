@@ -34,7 +34,7 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 constexpr int kPageElems = kPage * kHeadDim;          // bf16 elements in one (layer, page, head) block
 constexpr int64_t kMaxLen = int64_t(1) << 24;         // live entries per sequence
-constexpr int kMfmaMinObservers = 16;                 // MFMA scorer when observers >= 16
+constexpr int kMfmaMinRows = 16;                      // MFMA scorer when observer rows R = O G >= 16
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;

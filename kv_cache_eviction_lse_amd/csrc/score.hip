@@ -8,10 +8,10 @@
 //
 // Work items are chunks of consecutive 4-page steps of one stream and one group of its
 // observer rows.  A sequence's rows R = O G decide its path:
-//   score_valu_kernel  (O < 16): one key per lane, 64 keys per wave; the key row is
+//   score_valu_kernel  (R < 16): one key per lane, 64 keys per wave; the key row is
 //       pulled from LDS into registers and every observer row (uniform across the wave,
 //       so it lives in SGPRs) is dotted with v_dot2c_f32_bf16.  Row groups of 256.
-//   score_mfma_kernel  (O >= 16, R <= 128): QK^T on v_mfma_f32_32x32x16_bf16 with the
+//   score_mfma_kernel  (16 <= R <= 128): QK^T on v_mfma_f32_32x32x16_bf16 with the
 //       observer rows on M and the keys on N, so each lane holds one key and 16 rows and
 //       the exp and the row sum stay in-lane; 32- or 64-row sets, waves split the tiles.
 //   score_pipe_kernel<4> (128 < R <= 256) and score_pipe_kernel<8> (R > 256, row groups
@@ -67,7 +67,7 @@ struct ScoreArgs {
 // The scoring path of a sequence with O observers and R = O G rows.
 enum Path : int { kPathValu = 0, kPathMfma = 1, kPathPipe4 = 2, kPathPipe8 = 3, kPaths = 4 };
 __host__ __device__ inline int path_of(int64_t O, int64_t R) {
-  if (O < kMfmaMinObservers) return kPathValu;
+  if (R < kMfmaMinRows) return kPathValu;
   if (R <= 128) return kPathMfma;
   return R <= 256 ? kPathPipe4 : kPathPipe8;
 }

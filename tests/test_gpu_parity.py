@@ -62,7 +62,10 @@ EDGE_CASES = [
     # name, L, Hkv, Hq, lengths, starts, observers, budgets
     ("one_entry", 1, 1, 4, [1], [0], [16], [1]),
     ("page_edges_mfma", 1, 2, 8, [15, 16, 17, 33], [0, 0, 15, 7], [16, 17, 20, 32], [4, 16, 3, 40]),
-    ("valu_observers", 2, 2, 8, [100, 37, 300], [3, 0, 9], [1, 8, 15], [10, 0, 64]),
+    # the VALU scorer takes R = O G < 16 rows, the MFMA scorer 16 <= R <= 128
+    ("few_observers", 2, 2, 8, [100, 37, 300], [3, 0, 9], [1, 8, 15], [10, 0, 64]),
+    ("valu_rows", 2, 2, 4, [100, 300, 65], [3, 9, 0], [1, 3, 7], [10, 64, 20]),
+    ("mfma_rows_16", 1, 2, 4, [300, 97], [5, 0], [8, 9], [40, 30]),
     ("mixed_paths", 1, 2, 8, [200, 513, 70], [5, 0, 15], [3, 16, 15], [50, 100, 80]),
     ("big_group", 1, 1, 8, [777], [11], [40], [300]),
     ("two_row_groups", 1, 1, 4, [1000], [2], [65], [256]),
@@ -71,7 +74,7 @@ EDGE_CASES = [
     ("budget_all", 2, 1, 4, [129, 64], [1, 15], [20, 16], [129, 1000]),
     ("long_multi_chunk", 1, 1, 4, [5000, 3333], [0, 13], [24, 18], [700, 1000]),
     ("gqa1", 1, 4, 4, [300, 300], [0, 8], [16, 16], [30, 30]),
-    ("valu_row_groups", 1, 1, 32, [300], [0], [15], [40]),
+    ("pipe8_g32", 1, 1, 32, [300], [0], [15], [40]),
     # streams longer than the register-resident per-stream kernels hold (32768 entries)
     ("long_stream", 1, 1, 4, [40000, 2000], [5, 0], [16, 16], [3000, 700]),
     # the pipelined scorer: 128 < R <= 256 rows on 4 waves (3 or 4 of them with rows),
@@ -80,7 +83,7 @@ EDGE_CASES = [
     ("pipe8_rows", 1, 1, 8, [900, 401], [5, 9], [40, 64], [200, 100]),
     ("pipe8_two_groups", 1, 1, 8, [600], [7], [128], [128]),
     ("pipe8_ragged_groups", 1, 1, 4, [500], [0], [129], [64]),
-    ("all_paths", 2, 2, 8, [300, 300, 300, 300], [0, 5, 10, 15], [8, 20, 50, 100], [50, 50, 50, 50]),
+    ("all_paths", 2, 2, 8, [300, 300, 300, 300], [0, 5, 10, 15], [3, 20, 50, 100], [50, 50, 50, 50]),
     # chunks long enough that the LDS rings wrap (9 and 19 steps per chunk)
     ("pipe4_long_chunks", 2, 8, 32, [40000], [3], [50], [5000]),
     ("pipe8_long_chunks", 2, 8, 64, [40000], [3], [50], [5000]),
