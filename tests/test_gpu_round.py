@@ -2,7 +2,10 @@
 1, 2, 3 or 5 chunks (scoring of one chunk overlapped with the cut, keep set and moves
 of the previous one), every output matches the staged round bit for bit -- scores,
 hits, CRF, keep set, pairs, pair counts, the moved K/V rows and the host plan -- and the
-staged round is itself checked against the oracle (tests/gpu_util.check_stages)."""
+staged round is itself checked against the oracle (tests/gpu_util.check_stages).  The
+"short" batch takes the fused selection-and-plan kernel; the "long" batch has a stream of
+40 000 entries, so the round takes the long-stream kernels (cut and update, keep set,
+plan, then moves)."""
 import numpy as np
 import pytest
 
@@ -11,17 +14,26 @@ from workloads.edge import random_batch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("chunks", [1, 2, 3, 5])
-def test_round_matches_stages(chunks):
+LAYOUTS = {
+    # name: (layers, lengths, starts, observers, budgets); Hkv = 2, Hq = 8 (G = 4)
+    "short": (5, [700, 333, 0, 1300], [0, 9, 3, 5], [20, 5, 3, 16], [96, 40, 8, 512]),
+    "long": (3, [40000, 900, 17], [3, 0, 8], [16, 3, 8], [3000, 64, 20]),
+}
+CASES = [("short", c) for c in (1, 2, 3, 5)] + [("long", c) for c in (1, 2)]
+
+
+@pytest.mark.parametrize("layout,chunks", CASES, ids=[f"{n}-{c}" for n, c in CASES])
+def test_round_matches_stages(layout, chunks):
     import torch
     import kv_cache_eviction_lse_amd as K
     import oracle as O
     from tests import gpu_util as U
-    # 5 layers, G = 4; MFMA (20 observers) and VALU (5) scorer paths, a ragged batch
-    lay, inp = random_batch(61, 5, 2, 8, [700, 333, 0, 1300], [0, 9, 3, 5], [20, 5, 3, 16])
-    budget = np.array([96, 40, 8, 512], np.int32)
+    # MFMA (R >= 16) and VALU (R < 16) scorer paths, ragged batches
+    L, lengths, starts, observers, budget = LAYOUTS[layout]
+    lay, inp = random_batch(61, L, 2, 8, lengths, starts, observers)
+    budget = np.array(budget, np.int32)
     decay = np.array([O.lrfu_decay(0.5, int(d)) for d in lay.dt], np.float32)
-    print(f"round chunks={chunks}", flush=True)
+    print(f"round {layout} chunks={chunks}", flush=True)
     ref = U.run_stages(lay, inp, 8, budget, decay, fused=True)
     if chunks == 1:
         U.check_stages(lay, inp, ref, 8, budget, decay)
