@@ -53,7 +53,7 @@ __device__ __forceinline__ void store_mask_bits(uint32_t *m, int32_t j0, bool bi
 // which the bin's keys differ.  At the 70B shape after a first update every CRF is 0 or
 // 1, and this ends the search after one histogram pass instead of four.
 template <typename KeyF>
-__device__ SelResult select_crf_jump(int32_t n, KeyF key_of, uint64_t target, uint32_t and_all, uint32_t or_all,
+__device__ __forceinline__ SelResult select_crf_jump(int32_t n, KeyF key_of, uint64_t target, uint32_t and_all, uint32_t or_all,
                                      SelShared &sh, uint32_t *m_gt, uint32_t *m_in, bool *masks_ok) {
   SelResult r;
   *masks_ok = false;
@@ -160,6 +160,133 @@ __device__ SelResult select_crf_jump(int32_t n, KeyF key_of, uint64_t target, ui
     top = 31 - __clz(ba ^ bo);
     prefix = ba & ~((2u << top) - 1u);
   }
+  r.key = prefix;
+  r.above = above;
+  r.at = at;
+  return r;
+}
+
+// Level 2 for a stream with the level-1 masks: radix_select32's count search over the
+// scores of the candidates (ok), finished in LDS.  After a pass whose crossing bin holds
+// at most cap candidates, their scores are gathered into `list` (each wave reserves its
+// range with one LDS atomic per group of kU rows) and the search continues over the
+// list, so the remaining 8-bit passes read at most cap keys from LDS instead of every
+// score from HBM.
+template <typename SF, typename OkF>
+__device__ __forceinline__ SelResult select_count_list(int32_t n, SF s_of, OkF ok, uint64_t target, uint32_t and_all,
+                                       uint32_t or_all, SelShared &sh, uint32_t *list, int32_t cap) {
+  auto one = [](uint32_t) -> uint64_t { return 1; };
+  const uint32_t diff = and_all ^ or_all;
+  if (diff == 0 || cap <= 0) return radix_select32<true>(n, s_of, ok, one, target, and_all, or_all, sh);
+  int top = 31 - __clz(diff);
+  uint32_t prefix = top == 31 ? 0u : (and_all & ~((2u << top) - 1u));
+  uint64_t need = target, above = 0, at = 0;
+  const int lane = threadIdx.x & 63;
+  while (top >= 0) {
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int lo = top - width + 1;
+    const uint32_t nb = 1u << width;
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) sh.hist[b] = 0;
+    __syncthreads();
+    const int hs = top + 1;
+    constexpr int U = 8;
+    for (int32_t base = 0; base < n; base += U * (int32_t)blockDim.x) {
+      uint32_t keys[U];
+      bool ok_[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        ok_[u] = j < n && ok(j);
+        keys[u] = ok_[u] ? s_of(j) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t key = keys[u];
+        const bool v = ok_[u] && (hs >= 32 ? true : ((key >> hs) == (prefix >> hs)));
+        hist_add_count(sh.hist, v, (key >> lo) & (nb - 1u));
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      uint64_t h[4], ls = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = (int)nb - 1 - (4 * lane + q);
+        h[q] = b >= 0 ? sh.hist[b] : 0ull;
+        ls += h[q];
+      }
+      uint64_t acc = wave_scan_u64(ls) - ls;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = (int)nb - 1 - (4 * lane + q);
+        if (b >= 0 && acc < need && need <= acc + h[q]) {
+          sh.found[0] = (uint64_t)b;
+          sh.found[1] = acc;
+          sh.found[2] = h[q];
+        }
+        acc += h[q];
+      }
+    }
+    __syncthreads();
+    const uint32_t b = (uint32_t)sh.found[0];
+    const uint64_t ab = sh.found[1];
+    at = sh.found[2];
+    __syncthreads();
+    prefix |= b << lo;
+    need -= ab;
+    above += ab;
+    top = lo - 1;
+    if (top < 0 || at > (uint64_t)cap) continue;
+    // gather the crossing bin's keys into the list
+    uint32_t *cnt = (uint32_t *)&sh.found[3];
+    if (threadIdx.x == 0) *cnt = 0u;
+    __syncthreads();
+    const uint32_t pb = prefix >> lo;
+    for (int32_t base = 0; base < n; base += kU * (int32_t)blockDim.x) {
+      uint32_t keys[kU];
+      bool take[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t j = base + u * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+        take[u] = j < n && ok(j);
+        keys[u] = take[u] ? s_of(j) : 0u;
+      }
+      uint64_t m[kU];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        take[u] = take[u] && (keys[u] >> lo) == pb;
+        m[u] = ballot(take[u]);
+        tot += (uint32_t)__popcll(m[u]);
+      }
+      uint32_t wb = 0;
+      if (lane == 0 && tot) wb = atomicAdd(cnt, tot);
+      wb = (uint32_t)__shfl((int)wb, 0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t x = wb + (uint32_t)__popcll(m[u] & lanemask_lt());
+        if (take[u] && x < (uint32_t)cap) list[x] = keys[u];
+        wb += (uint32_t)__popcll(m[u]);
+      }
+    }
+    __syncthreads();
+    const int32_t nl = (int32_t)min(*cnt, (uint32_t)cap);    // (= at)
+    uint32_t la = ~0u, lor = 0u;
+    for (int32_t x = threadIdx.x; x < nl; x += blockDim.x) {
+      la &= list[x];
+      lor |= list[x];
+    }
+    block_and_or(la, lor, (uint32_t *)sh.scratch);
+    auto l_of = [&](int32_t x) -> uint32_t { return list[x]; };
+    auto all = [](int32_t) { return true; };
+    const SelResult r2 = radix_select32<true>(nl, l_of, all, one, need, la, lor, sh);
+    SelResult r;
+    r.key = r2.key;
+    r.above = above + r2.above;
+    r.at = r2.at;
+    return r;
+  }
+  SelResult r;
   r.key = prefix;
   r.above = above;
   r.at = at;
@@ -295,7 +422,9 @@ __global__ __launch_bounds__(kStreamThreads) void select_kernel(SelectArgs a) {
     block_and_or(sa, so, (uint32_t *)sh.scratch);
     auto s_of = [&](int32_t j) -> uint32_t { return sp[j]; };
     auto in_tie = [&](int32_t j) { return at_c(j, crf_if(j)); };
-    const SelResult r2 = radix_select32<true>(n, s_of, in_tie, one, need, sa, so, sh);
+    // (with the masks, the block-table row is no longer read: its LDS holds the list)
+    const SelResult r2 = masked ? select_count_list(n, s_of, in_tie, need, sa, so, sh, (uint32_t *)bt_lds, a.bt_cap)
+                                : radix_select32<true>(n, s_of, in_tie, one, need, sa, so, sh);
     sstar = r2.key;
     need2 = need - r2.above;
     at2 = r2.at;

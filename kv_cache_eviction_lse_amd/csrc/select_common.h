@@ -28,7 +28,7 @@ struct SelShared {
 // key_of(j) -> uint32 key; ok(j) -> candidate?; weight_of(key) -> uint64.
 // COUNT: every weight is 1 (weight_of is not called in the histogram passes).
 template <bool COUNT, typename KeyF, typename OkF, typename WF>
-__device__ SelResult radix_select32(int32_t n, KeyF key_of, OkF ok, WF weight_of, uint64_t target,
+__device__ __forceinline__ SelResult radix_select32(int32_t n, KeyF key_of, OkF ok, WF weight_of, uint64_t target,
                                     uint32_t and_all, uint32_t or_all, SelShared &sh) {
   SelResult r;
   const uint32_t diff = and_all ^ or_all;
