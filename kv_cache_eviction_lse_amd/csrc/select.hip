@@ -8,7 +8,11 @@
 //   1. radix-select the K-th largest CRF value c* (CRF cached in LDS when it fits);
 //   2. among CRF == c*, radix-select s* so that the remaining count is met;
 //   3. among (c*, s*) ties, take the lowest slots (ballot scan in slot order).
-// A level is skipped when every tied entry is kept.
+// A level is skipped when every tied entry is kept.  Streams too long for the CRF cache
+// (up to kMaskCap entries) keep two LDS bitmasks from level 1 (CRF above c*, CRF equal
+// to c*), so the later passes read only the scores; level 1 skips the bits a large
+// crossing bin shares (select_crf_jump), and level 2 finishes in an LDS list
+// (select_count_list).
 #include "select_common.h"
 
 namespace kvs {
@@ -35,14 +39,15 @@ constexpr uint64_t kJumpMin = 4096;    // crossing-bin size from which its AND/O
 
 __device__ __forceinline__ bool mask_bit(const uint32_t *m, int32_t j) { return (m[j >> 5] >> (j & 31)) & 1u; }
 
-// Writes bit j of the masks m_gt and m_in for this thread's entries j = base + u * 1024 +
-// t (u < kU): the 32 entries of a half wave are one mask word, so lanes 0 and 32 store
-// the ballots and no atomics are needed.  Entries past n get 0 bits.
+// Writes one word of the bitmask m: the bits of the 32 consecutive entries of this
+// thread's half wave, starting at entry j0 (a multiple of 32; every lane of the half wave
+// passes the same j0).  Lanes 0 and 32 store the two halves of the ballot, so no atomics
+// are needed.  Callers pass bit = 0 for entries past n.
 __device__ __forceinline__ void store_mask_bits(uint32_t *m, int32_t j0, bool bit) {
   const uint64_t b = ballot(bit);
   const int lane = threadIdx.x & 63;
   if (lane == 0) m[j0 >> 5] = (uint32_t)b;
-  if (lane == 32) m[(j0 >> 5)] = (uint32_t)(b >> 32);
+  if (lane == 32) m[j0 >> 5] = (uint32_t)(b >> 32);
 }
 
 // Level 1 for a stream whose CRF values are not in LDS: radix_select32's search with a
