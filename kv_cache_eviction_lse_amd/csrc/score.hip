@@ -415,10 +415,12 @@ __device__ __forceinline__ void lds_dma16_s(const uint16_t *base, uint32_t voff,
 }
 
 // One pipeline phase: the QK^T MFMAs of the next key tile (LDS bytes tile_base + rd[s]
-// for k-step s) overlapped with the exp/sum of the previous tile's accumulators.  The
-// scheduling barriers fix the issue order: the 8 LDS reads first, then one MFMA per
-// six VALU operations, so that the matrix core runs while the exp work issues.  With
-// tile_base a compile-time constant the reads take it as their immediate offset.
+// for k-step s) overlapped with the exp/sum of the previous tile's accumulators, for the
+// T (1 or 2) 32-row M tiles of the wave.  The scheduling barriers fix the issue order:
+// the 8 LDS reads first, then one MFMA per six VALU operations, so that the matrix core
+// runs while the exp work issues.  With tile_base a compile-time constant the reads take
+// it as their immediate offset.
+template <int T>
 __device__ __forceinline__ float pipe_phase(const uint8_t *tile_base, const uint32_t rd[8],
                                             const bf16x8 (*qa)[8], floatx16 &n0, floatx16 &n1,
                                             const floatx16 &p0, const floatx16 &p1, float alpha,
@@ -430,14 +432,16 @@ __device__ __forceinline__ float pipe_phase(const uint8_t *tile_base, const uint
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], c1, 0, 0, 0);
+    if constexpr (T == 2) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], c1, 0, 0, 0);
   }
-  const float v = exp_rows2(p0, p1, alpha, nl);
+  float v;
+  if constexpr (T == 2) v = exp_rows2(p0, p1, alpha, nl);
+  else v = exp_rows(p0, alpha, nl[0]);
   n0 = c0;
-  n1 = c1;
+  if constexpr (T == 2) n1 = c1;
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8 * T; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
   }
@@ -446,17 +450,20 @@ __device__ __forceinline__ float pipe_phase(const uint8_t *tile_base, const uint
 
 // ---- The pipelined scorer for more than 128 rows ----
 //
-// W waves per workgroup, each owning 64 observer rows (two 32-row M tiles), so one
-// workgroup covers a row group of up to 64 W rows and stages each K step in LDS once
-// for all of them.  A step is 4 pages (64 keys, two 32-key tiles); waves 0..3 each DMA
+// W waves per workgroup and up to 2 W 32-row M tiles of observer rows.  One workgroup
+// covers a row group of up to 64 W rows and stages each K step in LDS once for all of
+// them.  With W = 8 (one workgroup per CU) tile k goes to wave k mod W, so wave w owns
+// rows 32 w + i and 32 (w + W) + i (i < 32) when they exist: dealing the tiles out one
+// at a time spreads a partial row group over more waves, hence more SIMDs (10 tiles, R =
+// 300, put at most 3 on a SIMD instead of 4).  With W = 4 wave w owns tiles 2w, 2w + 1.  A step is 4 pages (64 keys, two 32-key tiles); waves 0..3 each DMA
 // one page of it.  Tile u's MFMAs overlap tile u-1's exp work:
 //   phase A of step j:  MFMA(j, tile 1)    || exp(j, tile 0)
 //   phase B of step j:  ring barrier(j+1), refill, combine;
 //                       MFMA(j+1, tile 0)  || exp(j, tile 1)
 // The loop is unrolled over the ring slots, so every LDS read is a per-lane register
 // plus an immediate and every DMA a scalar page base plus a per-lane offset computed
-// once; control flow in the loop is uniform across the workgroup.  Waves without rows
-// (a row group of fewer than 64 W rows) run the same barriers, loads and combines
+// once; control flow in the loop is uniform across the workgroup.  Waves run the loop
+// with T = 2, 1 or 0 tiles; those without rows run the same barriers, loads and combines
 // without the arithmetic.  Each wave writes its per-lane partial sums (both lane
 // halves) to part[step % 2]; after barrier j+1, wave 0 sums tile 0 of step j and
 // wave 1 tile 1 of step j-1 in wave order (deterministic), and stores the 32 keys.
@@ -468,7 +475,7 @@ struct PipeShape {
   static constexpr int kWgPerCu = W == 8 ? 1 : 2;
 };
 
-template <int W, bool COMPUTE>
+template <int W, int T>
 __device__ __forceinline__ void pipe_loop(const ScoreArgs &a, const Item &it, uint8_t (*ring)[kStepBytes],
                                           float (*part)[kStepTiles][W][64], const int32_t *bt_lds, int32_t page0,
                                           int wave, int lane, int nact, const bf16x8 (*qa)[8],
@@ -531,14 +538,14 @@ __device__ __forceinline__ void pipe_loop(const ScoreArgs &a, const Item &it, ui
 
   constexpr int kTileBytes = kTileKeys * kHeadDim * 2;
   floatx16 t0a = {}, t0b = {}, t1a = {}, t1b = {};
-  if (COMPUTE) {
+  if constexpr (T > 0) {
     bf16x8 kb[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kb[s] = *(const bf16x8 *)(ring[0] + rd[s]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       t0a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb[s], t0a, 0, 0, 0);
-      t0b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], t0b, 0, 0, 0);
+      if constexpr (T == 2) t0b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb[s], t0b, 0, 0, 0);
     }
   }
   // one step with its ring slot fixed at compile time
@@ -546,7 +553,7 @@ __device__ __forceinline__ void pipe_loop(const ScoreArgs &a, const Item &it, ui
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int NEXT = (SLOT + 1) % S;
     float *mine = &part[(SLOT & 1)][0][wave][0];
-    if (COMPUTE) mine[lane] = pipe_phase(ring[SLOT] + kTileBytes, rd, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
+    if constexpr (T > 0) mine[lane] = pipe_phase<T>(ring[SLOT] + kTileBytes, rd, qa, t1a, t1b, t0a, t0b, a.alpha, nl);
     if (step + 1 < s_end) {
       int later = 0;
 #pragma unroll
@@ -557,10 +564,10 @@ __device__ __forceinline__ void pipe_loop(const ScoreArgs &a, const Item &it, ui
         if (wave == 0) combine(step, 0);
         else if (wave == 1 && step > s_begin) combine(step - 1, 1);
       }
-      if (COMPUTE)
-        mine[W * 64 + lane] = pipe_phase(ring[NEXT], rd, qa, t0a, t0b, t1a, t1b, a.alpha, nl);
-    } else if (COMPUTE) {
-      mine[W * 64 + lane] = exp_rows2(t1a, t1b, a.alpha, nl);
+      if constexpr (T > 0)
+        mine[W * 64 + lane] = pipe_phase<T>(ring[NEXT], rd, qa, t0a, t0b, t1a, t1b, a.alpha, nl);
+    } else if constexpr (T > 0) {
+      mine[W * 64 + lane] = T == 2 ? exp_rows2(t1a, t1b, a.alpha, nl) : exp_rows(t1a, a.alpha, nl[0]);
     }
   };
   for (int32_t step = s_begin; step < s_end; step += S) {
@@ -608,18 +615,26 @@ __global__ __launch_bounds__(PipeShape<W>::kThreads, PipeShape<W>::kWgPerCu) voi
   const int32_t R = it.O * a.G;
   const int32_t r0 = it.rg * a.rows_per_group;
   const int32_t rows_here = min(a.rows_per_group, R - r0);
-  const int nact = (rows_here + 63) / 64;                 // waves with rows
-  const bool active = wave < nact;
-  const int32_t wr0 = r0 + wave * 64;
+  // 32-row M tiles.  W = 8: tile k of the row group goes to wave k mod W, so this wave's
+  // tile t (t < nt) is rows r0 + 32 (wave + W t) + i.  W = 4 (two workgroups per CU):
+  // wave w takes tiles 2w and 2w + 1, and a wave with rows always runs both (a partial
+  // second tile computes zero rows), which keeps that kernel's code as tuned.
+  constexpr bool kDeal = W == 8;
+  const int32_t ntr = (rows_here + 31) / 32;
+  const int nt = kDeal ? (wave < ntr ? 1 : 0) + (wave + W < ntr ? 1 : 0) : (2 * wave < ntr ? 2 : 0);
+  const int nact = kDeal ? (ntr < W ? (int)ntr : W) : (int)((ntr + 1) / 2);   // waves with rows
+  auto row_of = [&](int t, int i) -> int32_t {
+    return kDeal ? r0 + 32 * (wave + W * t) + i : r0 + 64 * wave + 32 * t + i;
+  };
 
-  // Observer rows of this wave as MFMA A operands: lane (m, h) holds row m,
+  // Observer rows of this wave as MFMA A operands: lane (m, h) holds row m of the tile,
   // dims 16s + 8h .. +8 for k-step s.  Loads are unconditional (invalid rows read
   // row 0 of the stream and are zeroed) so that they all issue back to back.
   bf16x8 qa[2][8];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int32_t r = wr0 + 32 * t + col;
-    const bool ok = active && r < R;
+    const int32_t r = row_of(t, col);
+    const bool ok = t < nt && r < R;
     const int32_t rc = ok ? r : 0;
     const int32_t h = it.g * a.G + rc / it.O;
     const int32_t o = rc - (rc / it.O) * it.O;
@@ -631,13 +646,13 @@ __global__ __launch_bounds__(PipeShape<W>::kThreads, PipeShape<W>::kWgPerCu) voi
       qa[t][s] = ok ? v : z;
     }
   }
-  // LSE of the wave's rows, one per lane, then spread to the accumulator layout:
-  // register k of M tile t holds row 32t + 8(k/4) + 4h + k%4.  Rows past the end have
-  // zero Q and LSE +inf, so they add exactly 0.
+  // LSE of the wave's rows, one per lane (lane 32 t + i: row i of tile t), then spread
+  // to the accumulator layout: register k of M tile t holds row 8(k/4) + 4h + k%4 of the
+  // tile.  Rows past the end have zero Q and LSE +inf, so they add exactly 0.
   float my_nl;
   {
-    const int32_t r = wr0 + lane;
-    const bool ok = active && r < R && r < r0 + rows_here;
+    const int32_t r = row_of(lane >> 5, lane & 31);
+    const bool ok = (lane >> 5) < nt && r < R && r < r0 + rows_here;
     const int32_t rc = ok ? r : 0;
     const int32_t h = it.g * a.G + rc / it.O;
     const int32_t o = rc - (rc / it.O) * it.O;
@@ -655,10 +670,12 @@ __global__ __launch_bounds__(PipeShape<W>::kThreads, PipeShape<W>::kWgPerCu) voi
 #pragma unroll
     for (int k = 0; k < 16; ++k) nl[t][k] = __shfl(my_nl, 32 * t + 8 * (k >> 2) + 4 * half + (k & 3));
   __syncthreads();
-  if (active)
-    pipe_loop<W, true>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
+  if (nt == 2)
+    pipe_loop<W, 2>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
+  else if (kDeal && nt == 1)
+    pipe_loop<W, kDeal ? 1 : 2>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
   else
-    pipe_loop<W, false>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
+    pipe_loop<W, 0>(a, it, ring, part, bt_lds, page0, wave, lane, nact, qa, nl);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void score_mfma_kernel(ScoreArgs a) {
