@@ -58,3 +58,42 @@ def test_round_matches_stages(layout, chunks):
     np.testing.assert_array_equal(cache.crf.cpu().numpy().view(np.uint32), ref["crf2"].view(np.uint32))
     for f in ("shift", "new_start", "new_len", "freed"):
         np.testing.assert_array_equal(getattr(plan, f), getattr(ref["plan"], f))
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_round_repeats_bit_for_bit(layout):
+    """Three rounds from identical copies of one state give identical results, bit for
+    bit: scores, hits, CRF, keep set, pair counts, pairs and the moved K/V rows.  Every
+    reduction and ranking in the kernels runs in a fixed order and the moves' pairs are
+    disjoint, so nothing may depend on timing (a race would show up here as a difference
+    between the runs)."""
+    import torch
+    import kv_cache_eviction_lse_amd as K
+    import oracle as O
+    from tests import gpu_util as U
+    L, lengths, starts, observers, budget = LAYOUTS[layout]
+    lay, inp = random_batch(83, L, 2, 8, lengths, starts, observers)
+    budget = np.array(budget, np.int32)
+    dev = torch.device("cuda", 0)
+    dec = torch.from_numpy(np.array([O.lrfu_decay(0.5, int(d)) for d in lay.dt], np.float32)).to(dev)
+    n_prev = torch.from_numpy(np.asarray(lay.n_prev, np.int32)).to(dev)
+    runs = []
+    for rep in range(3):
+        print(f"repeat {layout} run {rep}", flush=True)
+        cache, seqs, obs = U.upload(lay, inp)
+        bufs = K.RoundBuffers(cache, seqs, obs, budget, keep_hits=True)
+        plan = K.eviction_round(cache, seqs, obs, bufs, dec, n_prev, 1.0 / np.sqrt(128.0))
+        torch.cuda.synchronize()
+        pc = bufs.pair_count.cpu().numpy()
+        pairs = bufs.pairs.cpu().numpy()
+        runs.append({
+            "s": bufs.scores.cpu().numpy().view(np.uint32), "hit": bufs.hit.cpu().numpy(),
+            "keep": bufs.keep.cpu().numpy(), "pc": pc,
+            "pairs": [pairs[idx][:int(pc[idx])] for idx in np.ndindex(pc.shape)],
+            "k": cache.k.cpu().numpy(), "v": cache.v.cpu().numpy(),
+            "crf": cache.crf.cpu().numpy().view(np.uint32), "freed": plan.freed})
+    for r in runs[1:]:
+        for key in ("s", "hit", "keep", "pc", "k", "v", "crf", "freed"):
+            np.testing.assert_array_equal(r[key], runs[0][key], err_msg=key)
+        for a, b in zip(r["pairs"], runs[0]["pairs"]):
+            np.testing.assert_array_equal(a, b)
