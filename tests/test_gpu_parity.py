@@ -87,6 +87,10 @@ EDGE_CASES = [
     # chunks long enough that the LDS rings wrap (9 and 19 steps per chunk)
     ("pipe4_long_chunks", 2, 8, 32, [40000], [3], [50], [5000]),
     ("pipe8_long_chunks", 2, 8, 64, [40000], [3], [50], [5000]),
+    # the largest GQA group (G = 64): R = 576 rows, two row groups of the 8-wave scorer
+    ("max_group", 1, 1, 64, [500], [3], [9], [100]),
+    # the register-resident per-stream kernels' limit (32 768 entries) and one past it
+    ("reg_boundary", 1, 1, 4, [32768, 32769], [0, 7], [16, 16], [1000, 32768]),
     # more than 255 sequences: item tables built on the device
     ("many_seqs", 1, 1, 4, [(37 * i) % 90 + 1 for i in range(300)], [(5 * i) % 16 for i in range(300)],
      [16 + (i % 3) * 7 if i % 4 else 6 for i in range(300)], [(11 * i) % 50 for i in range(300)]),
