@@ -519,7 +519,12 @@ def bench_ratchet(args) -> None:
     budgets = []
     t_wall = time.perf_counter()
     for r in range(1, R + 1):
-        q, lse = lp.prepare(r)
+        # the round's tokens and observers; their LSE (the decode kernel's hand-over) is
+        # computed below, right before the round, except on the checked rounds
+        q = lp.append(r)
+        lse = torch.empty((L, Hq, OBS), dtype=torch.float32, device=dev)
+        if r in check:
+            lp.observer_lse(q, lse)
         if args.flags == "confidence":
             x = lp.step_logits(r)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -544,6 +549,11 @@ def bench_ratchet(args) -> None:
             n_prev_t = torch.tensor([n_prev], dtype=torch.int32, device=dev)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             torch.cuda.synchronize()
+            # The LSE is device work on this stream (after its own host-to-device copies):
+            # the round's calls are enqueued while it runs, as they would be behind the
+            # decode kernel, so the events time the round's kernels and not the host's
+            # enqueue on an idle GPU.
+            lp.observer_lse(q, lse)
             ev[0].record(st)
             K.kvs_score(lp.cache, seqs, obs, lp.w.scale, bufs.scores, bufs.workspace)
             ev[1].record(st)
@@ -571,8 +581,9 @@ def bench_ratchet(args) -> None:
                    "prefill": 8192, "append_per_round": APPEND, "observers": OBS, "rounds": R,
                    "timed_rounds": len(t_round), "flags": args.flags, "budget_start": 512,
                    "budget_final": lp.budget, "budget_expansions": expansions,
-                   "timing": "HIP events around each round's kvs_score -> kvs_lrfu_select_compact; "
-                             "appends, observers and their LSE are prepared between rounds, untimed; "
+                   "timing": "HIP events around each round's kvs_score -> kvs_lrfu_select_compact, "
+                             "enqueued behind the device work that computes the round's observer LSE; "
+                             "appends, observers and their LSE are untimed; "
                              "value = sum of entries / sum of round times"},
         "hbm_gbps": req_bytes / (ms_round / 1000.0) / 1e9,
         "hbm_frac": req_bytes / (ms_round / 1000.0) / 1e9 / HBM_PEAK_GBPS,

@@ -89,8 +89,15 @@ class RatchetLoop:
     def prepare(self, r: int):
         """Append the round's tokens and draw its observers and their LSE; returns
         (q, lse) on the device."""
+        q = self.append(r)
+        lse = self.torch.empty((self.L, self.Hq, OBS), dtype=self.torch.float32, device=self.dev)
+        self.observer_lse(q, lse)
+        return q, lse
+
+    def append(self, r: int):
+        """Append the round's 64 tokens (K with planted keys aligned to the round's
+        observers, V) and draw the observers; returns q (bf16 [L][Hq][OBS][D], device)."""
         torch, dev, d = self.torch, self.dev, self.d
-        from workloads import device as DV
         L, Hkv, Hq, G, D = self.L, self.Hkv, self.Hq, self.G, self.D
         q = torch.randn((L, Hq, OBS, D), generator=self.gen, device=dev).to(torch.bfloat16)
         qf = q.float()
@@ -112,14 +119,22 @@ class RatchetLoop:
                 .to(torch.bfloat16).view(torch.int16)
         self.n_prev = self.n
         self.n += APPEND
+        return q
+
+    def observer_lse(self, q, lse) -> None:
+        """The observers' LSE over the live entries into lse (fp32 [L][Hq][OBS], device):
+        what the decode kernel hands over.  Its host-to-device copies come first, so
+        after they return the rest is device work enqueued on the current stream."""
+        torch, dev, d = self.torch, self.dev, self.d
+        from workloads import device as DV
+        L, Hkv, Hq, G, D = self.L, self.Hkv, self.Hq, self.G, self.D
+        qf = q.float()
         live = self.start + np.arange(self.n)
         lpg = torch.from_numpy(np.asarray(self.pages, np.int64)[live // 16]).to(dev)
         lrw = torch.from_numpy(live % 16).to(dev)
-        lse = torch.empty((L, Hq, OBS), dtype=torch.float32, device=dev)
         for l in range(L):
             keys = d.k[l][lpg, :, lrw, :].view(torch.bfloat16).float()
             lse[l] = DV.live_lse(keys, qf[l].reshape(Hkv, G * OBS, D), self.w.scale).reshape(Hq, OBS)
-        return q, lse
 
     def step_logits(self, r: int):
         """The round's 64 decode steps' logits (bf16, device)."""
