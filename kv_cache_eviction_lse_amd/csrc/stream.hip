@@ -1,8 +1,9 @@
 // Register-resident per-stream kernels: the attention-mass cut with the LRFU update,
 // the top-B keep set, or both in one pass over the data.  One 1024-thread workgroup
-// per stream; thread t holds the scores and CRF of slots u * 1024 + t (u < kRegU) in
-// registers, so each input is read from memory once and every selection pass runs
-// on registers.  Streams longer than kRegU * 1024 entries take the kernels of
+// per stream; thread t owns slots u * 1024 + t (u < kRegU): their scores sit in LDS
+// (slot-major, each thread touching only its own) and their CRF, or caller keys, in
+// registers, so each input is read from memory once and every selection pass runs on
+// LDS and registers.  Streams longer than kRegU * 1024 entries take the kernels of
 // lrfu.hip and select.hip.
 //
 // ActKV Dissected, Component 1: hits are the shortest prefix of (s desc, slot asc)
@@ -15,8 +16,9 @@
 // and ties at a threshold go to the lowest slots, so the results are exact.
 //
 // Selection: radix search on the key bits below the candidates' common prefix (from
-// the AND and OR of their keys), 12 bits per pass, with a 4096-bin LDS histogram of
-// counts or of integer masses; the crossing bin is found with one block-wide scan.
+// the AND and OR of their keys), kDigitBits = 11 bits per pass, with a 2048-bin LDS
+// histogram of counts or of integer masses; the crossing bin is found with one
+// block-wide scan.
 
 #include "kvs_device.h"
 
